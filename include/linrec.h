@@ -1,0 +1,219 @@
+/*
+ * linrec.h -- C ABI of the MI355X (gfx950) chunkwise linear-recurrence layer.
+ *
+ * The layer (per batch b and head h, one sub-sequence of T tokens):
+ *
+ *     S_0 = S_in,   S_t = a_t S_{t-1} + k_t^T v_t,   o_t = q_t S_t,   S_out = S_T
+ *
+ * with a d_k x d_v state per head.  A long sequence is processed as a chain
+ * of sub-sequences: S_out of one piece is S_in of the next, and in the
+ * backward pass dS_in of one piece is dS_out of the previous one, so any
+ * split gives the result of one pass over the whole sequence.  Sources: the
+ * d x d memory state accumulated over sub-sequences processed one after
+ * another, with the backward pass over stored states (Sequence Accumulation
+ * and Beyond, "Approach"); boundary states and gradients propagated across
+ * chunks (StateFlow, Abstract; the gptget summary's method details: a linear
+ * recurrence kernel inside each chunk, chunks joined by boundary states);
+ * the right-product form of linear attention with cached intermediate
+ * states (Linear Attention Sequence Parallelism, abstract).
+ *
+ * Inside a piece the work is done chunkwise with C = 64 tokens per chunk:
+ *   - a state-transition kernel walks the chunks in order, carrying S in
+ *     fp32 registers and storing the state entering every chunk ("states");
+ *   - an intra-chunk kernel computes, for every chunk independently,
+ *         O_n = [(Q_n K_n^T) .* D_n] V_n + (Q_n .* gamma) S_{n-1}
+ *     where gamma_i is the chunk-local cumulative decay of token i and
+ *     D_ij = gamma_i / gamma_j for j <= i (0 above the diagonal).
+ *   The backward mirrors this: a reverse scan carries dS from dS_out back to
+ *   dS_in and stores the gradient leaving every chunk; a per-chunk kernel
+ *   computes dQ, dK, dV from the stored states.
+ *
+ * ---------------------------------------------------------------- layouts
+ *   Activations q, k (d_k wide), v, o, dO, dq, dk, dv (d_v or d_k wide) are
+ *   [B, H, T, d] with element strides (sb, sh, st); the feature index is
+ *   contiguous (stride 1).  A piece of a longer tensor is passed as a
+ *   strided view (pointer advanced to the piece's first token), no copy.
+ *   decay:  LINREC_DECAY_NONE  -> a_t = 1, decay.ptr ignored;
+ *           LINREC_DECAY_HEAD  -> fp32 [H] (a_h itself, not its log), element
+ *                                 stride decay.sh (sb, st ignored);
+ *           LINREC_DECAY_TOKEN -> fp32 [B, H, T] with strides (sb, sh, st).
+ *           Values must lie in (0, 1].
+ *   S_in, S_out, dS_out, dS_in: contiguous fp32 [B, H, d_k, d_v].
+ *   states: opaque, linrec_states_bytes() bytes, 256-byte aligned.
+ *   workspace: opaque, linrec_bwd_workspace_bytes() bytes, 256-byte aligned.
+ *
+ * ---------------------------------------------------------------- dtypes
+ *   dtype (inputs q, k, v, dO):
+ *     LINREC_BF16: products run on bf16 MFMA with fp32 accumulation.  Every
+ *                  operand the kernels compute (the masked score matrix, the
+ *                  decay-scaled keys/queries, the carried state) enters the
+ *                  MFMA as a hi + lo pair of bf16 values, so its rounding
+ *                  costs ~2^-17 rather than 2^-9 of relative accuracy.
+ *     LINREC_F32:  fp32 MFMA; only d_k = d_v = 64.
+ *   out_dtype (outputs o, dq, dk, dv): LINREC_BF16 (round to nearest even
+ *     from the fp32 result) or LINREC_F32; must be LINREC_F32 when dtype is.
+ *   S_*, dS_*, decay, the per-chunk state store and the workspace are fp32.
+ *
+ * ---------------------------------------------------------------- shapes
+ *   chunk == 64; T % 64 == 0 and T >= 64; d_k, d_v in {64, 128};
+ *   B >= 1, H >= 1.  Activation pointers and their strides sb, sh, st must
+ *   keep every token row 16-byte aligned.
+ *
+ * ---------------------------------------------------------------- semantics
+ *   Ownership: the caller owns all device memory; the library keeps no
+ *   pointer after a call returns and allocates no device memory (a context
+ *   owns one auxiliary HIP stream and a few events).
+ *   Ordering: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *   stream) and the call returns at once.  Inputs must be ready on `stream`;
+ *   outputs are ready on `stream` when it reaches the call's end.
+ *   Errors: every argument is checked on the host before anything is
+ *   enqueued; on error nothing runs and no output is touched.  A failed
+ *   launch returns LINREC_E_LAUNCH (linrec_last_hip_error() gives the HIP
+ *   code).  Faults inside kernels surface at the caller's next
+ *   synchronisation.  Nothing is printed and no exception crosses the ABI.
+ *   Aliasing: S_out may equal S_in and dS_in may equal dS_out (the carry
+ *   loop's natural form).  Any other overlap between an output and any
+ *   argument is undefined.
+ *   Threads: a context is used by one host thread at a time.
+ */
+#ifndef LINREC_H
+#define LINREC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LINREC_OK = 0,
+    LINREC_E_NULL = 1,      /* a required pointer is NULL                     */
+    LINREC_E_SHAPE = 2,     /* unsupported B, H, T, d_k, d_v, chunk or pieces  */
+    LINREC_E_DTYPE = 3,     /* unknown dtype, or dtype/shape combination      */
+    LINREC_E_LAYOUT = 4,    /* unsupported strides or decay kind              */
+    LINREC_E_ALIGN = 5,     /* a pointer or stride breaks 16-byte row alignment */
+    LINREC_E_WORKSPACE = 6, /* states/workspace pointer missing or misaligned */
+    LINREC_E_DEVICE = 7,    /* HIP runtime error outside a launch             */
+    LINREC_E_LAUNCH = 8     /* a kernel launch failed                         */
+} linrec_status;
+
+typedef enum { LINREC_BF16 = 0, LINREC_F32 = 1 } linrec_dtype;
+
+typedef enum {
+    LINREC_DECAY_NONE = 0,
+    LINREC_DECAY_HEAD = 1,
+    LINREC_DECAY_TOKEN = 2
+} linrec_decay_kind;
+
+/* A device tensor: base pointer and element strides over (b, h, t). */
+typedef struct {
+    void* ptr;
+    int64_t sb, sh, st;
+} linrec_tensor;
+
+/* Problem description of one call (T = tokens of this piece or sequence). */
+typedef struct {
+    int32_t B, H, T, dk, dv;
+    int32_t chunk;            /* must be 64 */
+    int32_t dtype;            /* linrec_dtype of q, k, v, dO */
+    int32_t decay;            /* linrec_decay_kind */
+    int32_t out_dtype;        /* linrec_dtype of o, dq, dk, dv */
+} linrec_desc;
+
+typedef struct linrec_ctx linrec_ctx;
+
+/* Create a context on HIP device `device` (owns an auxiliary stream, created
+ * at default priority, and events).  *out is set only on success. */
+linrec_status linrec_ctx_create(linrec_ctx** out, int device);
+/* Destroy a context; waits for its auxiliary stream.  NULL is a no-op. */
+linrec_status linrec_ctx_destroy(linrec_ctx* ctx);
+
+/* Bytes of the per-chunk state store for `d` (0 if `d` is invalid).  It is
+ * B*H*(T/64)*d_k*d_v fp32 values: the state entering every chunk, written by
+ * linrec_fwd and read by linrec_bwd.  It depends on T only through T/64
+ * (linear in the piece length, constant in the number of pieces already
+ * processed). */
+size_t linrec_states_bytes(const linrec_desc* d);
+
+/* Bytes of backward workspace for `d` (0 if `d` is invalid): the gradient
+ * leaving every chunk, B*H*(T/64)*d_k*d_v fp32 values. */
+size_t linrec_bwd_workspace_bytes(const linrec_desc* d);
+
+/* Forward over one piece.
+ *   q, k: [B,H,T,d_k];  v, o: [B,H,T,d_v];  decay per d->decay.
+ *   S_in: fp32 [B,H,d_k,d_v] or NULL (zeros).  S_out: fp32, required.
+ *   states: required (linrec_states_bytes(d) bytes); pass it unmodified to
+ *   linrec_bwd for the same piece.
+ * Reference: the recurrence above (Sequence Accumulation and Beyond,
+ * "Approach"; StateFlow, Abstract). */
+linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d,
+                         linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                         linrec_tensor decay, const float* S_in,
+                         linrec_tensor o, float* S_out, void* states,
+                         void* stream);
+
+/* Backward over one piece, for the loss L = <dO, o> + <dS_out, S_out>.
+ *   states: as written by linrec_fwd for this piece (it holds S_in).
+ *   dO: [B,H,T,d_v].  dS_out: fp32 [B,H,d_k,d_v] or NULL (zeros).
+ *   dq, dk: [B,H,T,d_k], dv: [B,H,T,d_v], dS_in: fp32; all required.
+ *   workspace: linrec_bwd_workspace_bytes(d) bytes.
+ * The decay is not differentiated (it is an input, not a parameter).
+ * Reference: boundary gradients propagated across chunks (StateFlow,
+ * Abstract); backward pass over stored states (Sequence Accumulation and
+ * Beyond, "Approach"). */
+linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d,
+                         linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                         linrec_tensor decay, const void* states,
+                         linrec_tensor dO, const float* dS_out,
+                         linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                         float* dS_in, void* workspace, void* stream);
+
+/* Sequence accumulation over `npieces` consecutive pieces of the sequence
+ * described by `d` (d->T = total tokens; lengths[i] % 64 == 0, sum = T;
+ * lengths is host memory).  Piece i is processed as its own sub-sequence,
+ * in order, with S carried from piece to piece; the state-transition
+ * kernels run on the context's auxiliary stream so that piece i+1's state
+ * transition overlaps piece i's intra-chunk work (state transitions with
+ * limited parallelism overlapped with surrounding computation: StateFlow,
+ * Abstract).  `states` covers the whole sequence
+ * (linrec_states_bytes(d) with the total T).  Same arguments and rules as
+ * linrec_fwd otherwise. */
+linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d,
+                             int32_t npieces, const int32_t* lengths,
+                             linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                             linrec_tensor decay, const float* S_in,
+                             linrec_tensor o, float* S_out, void* states,
+                             void* stream);
+
+/* Bytes of workspace linrec_bwd_seq needs for these pieces (0 if invalid). */
+size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
+                                      const int32_t* lengths);
+
+/* Backward of linrec_fwd_seq: pieces in reverse order with dS carried back
+ * from dS_out to dS_in; the reverse state scans run on the auxiliary stream
+ * and overlap the per-chunk gradient kernels of the following piece. */
+linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
+                             int32_t npieces, const int32_t* lengths,
+                             linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                             linrec_tensor decay, const void* states,
+                             linrec_tensor dO, const float* dS_out,
+                             linrec_tensor dq, linrec_tensor dk,
+                             linrec_tensor dv, float* dS_in, void* workspace,
+                             void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* linrec_status_str(linrec_status s);
+
+/* HIP error code of the most recent LINREC_E_DEVICE / LINREC_E_LAUNCH on
+ * the calling thread (0 if none). */
+int linrec_last_hip_error(void);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int linrec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINREC_H */

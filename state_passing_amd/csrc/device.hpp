@@ -1,0 +1,334 @@
+// device.hpp -- gfx950 building blocks shared by the linear-recurrence kernels.
+//
+// Conventions (one wave = 64 lanes; lane l = 16*g + t, g = l/16, t = l%16):
+//
+//   MFMA 16x16, k = 32 per step ("k32 step").  An operand fragment holds 8
+//   values per lane.  For A (M x K) lane (g,t) holds A[t][8g + r], r = 0..7;
+//   for B (K x N) it holds B[8g + r][t].  The result tile D (16 x 16 fp32)
+//   gives lane (g,t) the values D[4g + r][t], r = 0..3.
+//     bf16: one v_mfma_f32_16x16x32_bf16 per k32 step.
+//     fp32: eight v_mfma_f32_16x16x4_f32; sub-step r contracts the four
+//           k-slots {8g + r : g = 0..3}, so both dtypes share one fragment
+//           layout and any k-slot order shared by A and B is exact.
+//
+//   LDS tiles are row-major with a pitch in elements.  frag_rows() reads an
+//   operand whose M/N index runs down LDS rows (k contiguous in a row: one
+//   16-byte read for bf16); frag_cols() reads one whose k index runs down
+//   LDS rows (gfx950 ds_read_b64_tr_b16 transposing reads for bf16, scalar
+//   reads for fp32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace linrec {
+
+constexpr int CHUNK = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
+
+// Decay description as the kernels see it (kind: 0 none, 1 per head, 2 per token).
+struct DecayArg {
+    const float* ptr;
+    int64_t sb, sh, st;
+    int kind;
+};
+
+// Strided activation view (element strides; the feature index is contiguous).
+template <typename T>
+struct Act {
+    T* ptr;
+    int64_t sb, sh, st;
+    __device__ __forceinline__ T* head(int b, int h) const { return ptr + b * sb + h * sh; }
+};
+
+template <typename T>
+struct Pad { static constexpr int value = 16 / sizeof(T); };  // 16 bytes of row padding
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <typename T>
+struct Frag;
+template <>
+struct Frag<bf16> {
+    bf16x8 v;
+};
+template <>
+struct Frag<float> {
+    float v[8];
+};
+
+__device__ __forceinline__ floatx4 mma(const Frag<bf16>& a, const Frag<bf16>& b, floatx4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Frag<float>& b, floatx4 c)
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[r], b.v[r], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- fragment reads from LDS -------------------------------------------
+
+// lane (g,t) <- tile[rbase + t][kbase + 8g + r]
+__device__ __forceinline__ Frag<bf16> frag_rows(const bf16* tile, int pitch, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(tile + (rbase + t) * pitch + kbase + 8 * g);
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_rows(const float* tile, int pitch, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const float4* p = reinterpret_cast<const float4*>(tile + (rbase + t) * pitch + kbase + 8 * g);
+    const float4 a = p[0], b = p[1];
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+
+// lane (g,t) <- tile[kbase + 8g + r][cbase + t]
+// ds_read_b64_tr_b16: within each 16-lane group, lane t addresses row
+// R + t/4, columns c0 + 4(t%4) .. +3, and receives column c0 + t of rows
+// R .. R+3.  Two reads cover the 8 k-slots.
+__device__ __forceinline__ Frag<bf16> frag_cols(const bf16* tile, int pitch, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const bf16* p = tile + (kbase + 8 * g + (t >> 2)) * pitch + cbase + 4 * (t & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * pitch));
+    Frag<bf16> f;
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_cols(const float* tile, int pitch, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        f.v[r] = tile[(kbase + 8 * g + r) * pitch + cbase + t];
+    return f;
+}
+
+// Fragment read straight from global memory, k contiguous: lane (g,t) <-
+// base[(rbase + t) * ld + kbase + 8g + r].
+__device__ __forceinline__ Frag<bf16> frag_rows_global(const bf16* base, int64_t ld, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(base + (rbase + t) * ld + kbase + 8 * g);
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_rows_global(const float* base, int64_t ld, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const float4* p = reinterpret_cast<const float4*>(base + (rbase + t) * ld + kbase + 8 * g);
+    const float4 a = p[0], b = p[1];
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+
+__device__ __forceinline__ Frag<bf16> scaled(Frag<bf16> f, float s)
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        f.v[r] = (bf16)((float)f.v[r] * s);
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> scaled(Frag<float> f, float s)
+{
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        f.v[r] *= s;
+    return f;
+}
+
+// ---- global <-> LDS staging ---------------------------------------------
+
+// Copy ROWS x D elements (row stride `ld` in global) into LDS (row pitch
+// `pitch`) with 16-byte accesses, all NT threads cooperating.
+template <typename T, int ROWS, int D, int NT>
+__device__ __forceinline__ void stage_rows(T* lds, int pitch, const T* src, int64_t ld)
+{
+    constexpr int VEC = 16 / sizeof(T);
+    constexpr int PER_ROW = D / VEC;
+    static_assert(D % VEC == 0, "row must be a whole number of 16-byte vectors");
+    for (int idx = threadIdx.x; idx < ROWS * PER_ROW; idx += NT) {
+        const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
+        *reinterpret_cast<uint4*>(lds + r * pitch + c) =
+            *reinterpret_cast<const uint4*>(src + r * ld + c);
+    }
+}
+
+// ---- decay ----------------------------------------------------------------
+
+// Inclusive cumulative log-decay of the chunk's tokens, token = lane:
+// lam_i = sum_{r <= i} ln a_r over the chunk starting at token tok0.  Must be
+// called by a full wave.  Log-space and chunk-local, so exp(lam_i - lam_j)
+// and exp(lam_i) never overflow or underflow across long sequences.
+__device__ __forceinline__ float chunk_log_cumsum(const DecayArg& d, int b, int h, int64_t tok0)
+{
+    const int lane = lane_id();
+    if (d.kind == 0)
+        return 0.f;
+    if (d.kind == 1)
+        return (float)(lane + 1) * logf(d.ptr[h * d.sh]);
+    float x = logf(d.ptr[b * d.sb + h * d.sh + (tok0 + lane) * d.st]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    return x;
+}
+
+// ---- split operands ---------------------------------------------------------
+//
+// A computed MFMA operand (P, the decay-scaled K or Q, a carried state) is
+// not a bf16 input, and rounding it to bf16 once would cost about 2^-9 of
+// relative accuracy per element.  It is therefore carried as hi + lo, two
+// bf16 values whose sum holds ~16 significant bits, and multiplied against
+// the exact bf16 activation with two MFMAs.  For fp32 activations the fp32
+// MFMA is used directly and there is no remainder.
+template <typename T>
+struct Split;
+template <>
+struct Split<bf16> {
+    Frag<bf16> hi, lo;
+};
+template <>
+struct Split<float> {
+    Frag<float> hi;
+};
+
+template <typename T>
+__device__ __forceinline__ Split<T> split8(const float (&x)[8]);
+
+template <>
+__device__ __forceinline__ Split<bf16> split8<bf16>(const float (&x)[8])
+{
+    Split<bf16> s;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const bf16 h = (bf16)x[r];
+        s.hi.v[r] = h;
+        s.lo.v[r] = (bf16)(x[r] - (float)h);
+    }
+    return s;
+}
+
+template <>
+__device__ __forceinline__ Split<float> split8<float>(const float (&x)[8])
+{
+    Split<float> s;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        s.hi.v[r] = x[r];
+    return s;
+}
+
+__device__ __forceinline__ floatx4 mma(const Frag<bf16>& a, const Split<bf16>& b, floatx4 c)
+{
+    return mma(a, b.lo, mma(a, b.hi, c));
+}
+__device__ __forceinline__ floatx4 mma(const Split<bf16>& a, const Frag<bf16>& b, floatx4 c)
+{
+    return mma(a.lo, b, mma(a.hi, b, c));
+}
+__device__ __forceinline__ floatx4 mma(const Frag<float>& a, const Split<float>& b, floatx4 c)
+{
+    return mma(a, b.hi, c);
+}
+__device__ __forceinline__ floatx4 mma(const Split<float>& a, const Frag<float>& b, floatx4 c)
+{
+    return mma(a.hi, b, c);
+}
+
+// Write x into an LDS plane pair: hi[idx] and (bf16 only) lo[idx].
+template <typename T>
+__device__ __forceinline__ void put_split(T* hi, T* lo, int idx, float x)
+{
+    const T h = (T)x;
+    hi[idx] = h;
+    if constexpr (sizeof(T) == 2)
+        lo[idx] = (T)(x - (float)h);
+}
+
+// Split fragments read from LDS plane pairs.
+template <typename T>
+__device__ __forceinline__ Split<T> frag_rows_split(const T* hi, const T* lo, int pitch, int rbase, int kbase)
+{
+    Split<T> s;
+    s.hi = frag_rows(hi, pitch, rbase, kbase);
+    if constexpr (sizeof(T) == 2)
+        s.lo = frag_rows(lo, pitch, rbase, kbase);
+    return s;
+}
+
+template <typename T>
+__device__ __forceinline__ Split<T> frag_cols_split(const T* hi, const T* lo, int pitch, int cbase, int kbase)
+{
+    Split<T> s;
+    s.hi = frag_cols(hi, pitch, cbase, kbase);
+    if constexpr (sizeof(T) == 2)
+        s.lo = frag_cols(lo, pitch, cbase, kbase);
+    return s;
+}
+
+// Split fragment of an fp32 matrix in global memory.
+//   contiguous k: lane (g,t) <- base[(rbase + t) * ld + kbase + 8g + r]
+//   strided k:    lane (g,t) <- base[(kbase + 8g + r) * ld + cbase + t]
+template <typename T>
+__device__ __forceinline__ Split<T> gfrag_rows_split(const float* base, int64_t ld, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const float4* p = reinterpret_cast<const float4*>(base + (rbase + t) * ld + kbase + 8 * g);
+    const float4 a = p[0], b = p[1];
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return split8<T>(x);
+}
+
+template <typename T>
+__device__ __forceinline__ Split<T> gfrag_cols_split(const float* base, int64_t ld, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        x[r] = base[(kbase + 8 * g + r) * ld + cbase + t];
+    return split8<T>(x);
+}
+
+// Store a 16x16 fp32 result tile (lane (g,t) holds rows 4g + r, column t)
+// to row-major global memory as OT.
+template <typename OT>
+__device__ __forceinline__ void store_tile(OT* base, int64_t ld, int rbase, int cbase, floatx4 acc)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    OT* p = base + (rbase + 4 * g) * ld + cbase + t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        p[r * ld] = (OT)acc[r];
+}
+
+}  // namespace linrec

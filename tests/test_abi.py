@@ -1,0 +1,159 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/linrec.h declares, sizes its buffers as documented, and rejects bad
+arguments with the documented status before touching any device state.
+
+The pointers below are fake addresses: a rejected call must never
+dereference them, and the valid-looking calls all stop at the NULL context
+check, which comes after every argument check."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_passing_amd import linrec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linrec.h")
+
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(linrec_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    lib = linrec._lib()
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(linrec.EXPORTS) == declared
+
+
+def test_version_and_status_strings():
+    lib = linrec._lib()
+    assert lib.linrec_version() >= 100
+    for code in range(9):
+        assert lib.linrec_status_str(code)
+    assert lib.linrec_status_str(99) == b"unknown status"
+
+
+def d(**kw):
+    base = dict(B=1, H=16, T=4096, dk=128, dv=128, dtype=linrec.BF16, decay=linrec.DECAY_HEAD)
+    base.update(kw)
+    return linrec.Desc(base["B"], base["H"], base["T"], base["dk"], base["dv"], 64,
+                       base["dtype"], base["decay"], base.get("out", base["dtype"]))
+
+
+def test_sizes():
+    # per-chunk states are fp32 whatever the activation dtype
+    assert linrec.states_bytes(d()) == 16 * 64 * 128 * 128 * 4
+    assert linrec.states_bytes(d(dtype=linrec.F32, dk=64, dv=64)) == 16 * 64 * 64 * 64 * 4
+    assert linrec.states_bytes(d(out=linrec.F32)) == linrec.states_bytes(d())
+    assert linrec.bwd_workspace_bytes(d()) == linrec.states_bytes(d())
+    # the per-piece store is linear in the piece length only
+    assert linrec.states_bytes(d(T=8192)) == 2 * linrec.states_bytes(d())
+    # two slots of the longest piece
+    assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \
+        2 * linrec.states_bytes(d(T=4096))
+    assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == linrec.states_bytes(d())
+    for bad in (d(T=100), d(T=0), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
+        assert linrec.states_bytes(bad) == 0
+    assert linrec.bwd_seq_workspace_bytes(d(T=8192), [4096, 4000]) == 0
+
+
+def act(ptr=FAKE, sb=16 * 4096 * 128, sh=4096 * 128, st=128):
+    return linrec.Tensor(ptr, sb, sh, st)
+
+
+def call_fwd(desc, q=None, k=None, v=None, decay=None, S_in=None, o=None, S_out=FAKE,
+             states=FAKE, ctx=None):
+    lib = linrec._lib()
+    return lib.linrec_fwd(ctx, ctypes.byref(desc), q or act(), k or act(), v or act(),
+                          decay or linrec.Tensor(FAKE, 0, 1, 0), S_in, o or act(), S_out,
+                          states, None)
+
+
+def call_bwd(desc, dq=None, workspace=FAKE, dS_in=FAKE, states=FAKE, ctx=None):
+    lib = linrec._lib()
+    return lib.linrec_bwd(ctx, ctypes.byref(desc), act(), act(), act(),
+                          linrec.Tensor(FAKE, 0, 1, 0), states, act(), None,
+                          dq or act(), act(), act(), dS_in, workspace, None)
+
+
+E = {v: k for k, v in linrec.STATUS.items()}
+
+
+@pytest.mark.parametrize("desc,code", [
+    (d(T=100), "LINREC_E_SHAPE"),
+    (d(T=0), "LINREC_E_SHAPE"),
+    (d(dk=96), "LINREC_E_SHAPE"),
+    (d(B=0), "LINREC_E_SHAPE"),
+    (d(H=0), "LINREC_E_SHAPE"),
+    (d(dtype=5), "LINREC_E_DTYPE"),
+    (d(dtype=linrec.F32), "LINREC_E_DTYPE"),
+    (d(dtype=linrec.F32, dk=64, dv=64, out=linrec.BF16), "LINREC_E_DTYPE"),
+    (d(out=3), "LINREC_E_DTYPE"),
+    (d(decay=3), "LINREC_E_LAYOUT"),
+])
+def test_bad_desc(desc, code):
+    assert call_fwd(desc) == E[code]
+    assert call_bwd(desc) == E[code]
+
+
+def test_bad_tensors():
+    good = d()
+    assert call_fwd(good, q=act(ptr=0)) == E["LINREC_E_NULL"]
+    assert call_fwd(good, k=act(ptr=FAKE + 2)) == E["LINREC_E_ALIGN"]
+    assert call_fwd(good, v=act(st=100)) == E["LINREC_E_LAYOUT"]    # rows overlap
+    assert call_fwd(good, o=act(st=132)) == E["LINREC_E_ALIGN"]     # 264-byte rows
+    # the output's alignment is judged in the output dtype: 132 fp32 = 528-byte rows
+    assert call_fwd(d(out=linrec.F32), o=act(st=132)) == E["LINREC_E_NULL"]
+    assert call_fwd(good, q=act(sh=-1)) == E["LINREC_E_LAYOUT"]
+    assert call_fwd(good, decay=linrec.Tensor(None, 0, 1, 0)) == E["LINREC_E_NULL"]
+    assert call_fwd(good, decay=linrec.Tensor(FAKE + 2, 0, 1, 0)) == E["LINREC_E_ALIGN"]
+    assert call_fwd(good, S_out=None) == E["LINREC_E_NULL"]
+    assert call_fwd(good, S_in=FAKE + 2) == E["LINREC_E_ALIGN"]
+    assert call_fwd(good, states=None) == E["LINREC_E_WORKSPACE"]
+    assert call_fwd(good, states=FAKE + 8) == E["LINREC_E_WORKSPACE"]
+    assert call_bwd(good, workspace=None) == E["LINREC_E_WORKSPACE"]
+    assert call_bwd(good, dS_in=None) == E["LINREC_E_NULL"]
+    assert call_bwd(good, dq=act(ptr=0)) == E["LINREC_E_NULL"]
+    # no decay tensor needed when there is no decay
+    assert call_fwd(d(decay=linrec.DECAY_NONE), decay=linrec.Tensor(None, 0, 0, 0)) == E["LINREC_E_NULL"]
+
+
+def test_valid_arguments_stop_at_missing_context():
+    # every argument check passes; the NULL context is the first thing rejected
+    assert call_fwd(d()) == E["LINREC_E_NULL"]
+    assert call_bwd(d()) == E["LINREC_E_NULL"]
+
+
+def test_bad_piece_lists():
+    lib = linrec._lib()
+    desc = d(T=8192)
+    for lengths in ([4096, 4000], [4096], [4096, 4096, 64], [0, 8192]):
+        arr = (ctypes.c_int32 * len(lengths))(*lengths)
+        rc = lib.linrec_fwd_seq(None, ctypes.byref(desc), len(lengths), arr, act(), act(), act(),
+                                linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE, None)
+        # the piece list is checked before the context
+        assert rc == E["LINREC_E_SHAPE"], lengths
+    arr = (ctypes.c_int32 * 2)(4096, 4096)
+    assert lib.linrec_fwd_seq(None, ctypes.byref(desc), 2, arr, act(), act(), act(),
+                              linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE,
+                              None) == E["LINREC_E_NULL"]
+    assert lib.linrec_fwd_seq(None, ctypes.byref(desc), 0, arr, act(), act(), act(),
+                              linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE,
+                              None) == E["LINREC_E_SHAPE"]
+
+
+def test_null_desc_and_ctx_destroy_null():
+    lib = linrec._lib()
+    assert lib.linrec_fwd(None, None, act(), act(), act(), linrec.Tensor(FAKE, 0, 1, 0), None,
+                          act(), FAKE, FAKE, None) == E["LINREC_E_NULL"]
+    assert lib.linrec_ctx_destroy(None) == 0
+    assert lib.linrec_ctx_create(None, 0) == E["LINREC_E_NULL"]

@@ -1,0 +1,150 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle,
+at sizes the oracle finishes in seconds: several chunks and tiles, every
+decay kind, d_k != d_v, fp32, a nonzero S_in / dS_out, and uniform,
+non-uniform and single-chunk splits."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from parity_util import TOL, compare, oracle_run
+from state_passing_amd import linrec
+from state_passing_amd.workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def small(name, B, H, T, dk, dv, dtype, decay, s_in=0.0):
+    return Workload(900, name, B, H, T, dk, dv, dtype, decay, s_in_std=s_in, piece=T)
+
+
+SMALL = [
+    small("bf16-head", 1, 2, 256, 128, 128, "bf16", "head"),
+    small("bf16-token", 2, 3, 384, 128, 128, "bf16", "token", s_in=0.1),
+    small("bf16-none", 1, 2, 192, 128, 128, "bf16", "none"),
+    small("bf16-64x64", 2, 2, 320, 64, 64, "bf16", "token", s_in=0.1),
+    small("bf16-64x128", 1, 3, 256, 64, 128, "bf16", "head", s_in=0.1),
+    small("bf16-128x64", 1, 3, 256, 128, 64, "bf16", "token", s_in=0.1),
+    small("f32-64", 1, 2, 1024, 64, 64, "f32", "none"),
+    small("f32-64-token", 2, 2, 256, 64, 64, "f32", "token", s_in=0.1),
+    small("bf16-one-chunk", 1, 1, 64, 128, 128, "bf16", "token", s_in=0.1),
+]
+
+
+def gpu_inputs(wl, seed=7, with_dS_out=True):
+    inp = make_inputs(wl, device="cpu", seed=seed, with_dS_out=with_dS_out)
+    for name in ("q", "k", "v", "dO", "S_in", "decay", "dS_out"):
+        x = getattr(inp, name)
+        if x is not None:
+            setattr(inp, name, x.to(DEV))
+    return inp
+
+
+def run_unsplit(inp, out_dtype=None):
+    o, S_out, st = linrec.fwd(inp.q, inp.k, inp.v, inp.decay, inp.S_in, out_dtype=out_dtype)
+    dq, dk, dv, dS_in = linrec.bwd(inp.q, inp.k, inp.v, inp.decay, st, inp.dO, inp.dS_out,
+                                   out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in)
+
+
+def run_seq(inp, lengths, out_dtype=None):
+    o, S_out, st = linrec.fwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, inp.S_in,
+                                  out_dtype=out_dtype)
+    dq, dk, dv, dS_in = linrec.bwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, st, inp.dO,
+                                       inp.dS_out, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in)
+
+
+def run_loop(inp, lengths, out_dtype=None):
+    o, S_out, dq, dk, dv, dS_in = linrec.piece_loop(inp.q, inp.k, inp.v, inp.decay, lengths,
+                                                    inp.S_in, inp.dO, inp.dS_out,
+                                                    out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in)
+
+
+def check(got, ref, heads, wl, label):
+    tol = TOL[wl.torch_dtype]
+    errs, bad = compare(got, ref, heads, tol)
+    print(f"[{label}] {wl.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, f"{label} {wl.name}: over tolerance {tol}: {bad}"
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_unsplit(wl):
+    """fp32 outputs against the plain bar, and the activation-dtype outputs
+    (bf16 beyond its half-ulp representation limit, or fp32)."""
+    print(f"case {wl}", flush=True)
+    inp = gpu_inputs(wl)
+    ref = oracle_run(inp)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    check(run_unsplit(inp, torch.float32), ref, heads, wl, "unsplit/f32-out")
+    if wl.dtype == "bf16":
+        check(run_unsplit(inp), ref, heads, wl, "unsplit/bf16-out")
+
+
+@pytest.mark.parametrize("wl", SMALL[:2] + SMALL[6:8], ids=[w.name for w in SMALL[:2] + SMALL[6:8]])
+def test_small_split_matches_oracle_and_unsplit(wl):
+    """Uniform and non-uniform splits (seq driver and per-piece loop) against
+    the oracle; the GPU split result is also compared with the GPU unsplit
+    result (chunk-aligned cuts and an fp32 carry make them bitwise equal)."""
+    inp = gpu_inputs(wl)
+    ref = oracle_run(inp)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    base = run_unsplit(inp, torch.float32)
+    N = wl.T // 64
+    splits = {"uniform": [wl.T // 2] * 2 if N % 2 == 0 else [64] * N,
+              "ragged": [64] + [wl.T - 128] + [64] if N >= 3 else [wl.T]}
+    for sname, lengths in splits.items():
+        for runner in (run_seq, run_loop):
+            got = runner(inp, lengths, torch.float32)
+            check(got, ref, heads, wl, f"{runner.__name__}/{sname}")
+            same = {k: bool(torch.equal(got[k], base[k])) for k in got}
+            print(f"  bitwise equal to unsplit: {same}", flush=True)
+            assert all(same.values()), same
+
+
+def test_deterministic_run_to_run():
+    wl = SMALL[1]
+    inp = gpu_inputs(wl)
+    a, b = run_unsplit(inp), run_unsplit(inp)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_aliasing_carry_in_place():
+    """S_out may alias S_in and dS_in may alias dS_out."""
+    wl = SMALL[1]
+    inp = gpu_inputs(wl)
+    base = run_unsplit(inp)
+    S = inp.S_in.clone()
+    o, S2, st = linrec.fwd(inp.q, inp.k, inp.v, inp.decay, S, S_out=S)
+    dS = inp.dS_out.clone()
+    _, _, _, dS2 = linrec.bwd(inp.q, inp.k, inp.v, inp.decay, st, inp.dO, dS, dS_in=dS)
+    torch.cuda.synchronize()
+    assert torch.equal(S, base["S_out"]) and torch.equal(dS, base["dS_in"])
+
+
+def test_strided_piece_views():
+    """Pieces passed as strided views of a [B,T,H,d]-major buffer."""
+    wl = SMALL[0]
+    inp = gpu_inputs(wl)
+    base = run_unsplit(inp)
+    # same values, memory laid out [B, T, H, d] and viewed as [B, H, T, d]
+    rel = lambda x: x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)  # noqa: E731
+    q, k, v, dO = (rel(x) for x in (inp.q, inp.k, inp.v, inp.dO))
+    assert q.stride(2) == wl.H * wl.dk
+    o, S_out, st = linrec.fwd(q, k, v, inp.decay, inp.S_in)
+    dq, dk, dv, dS_in = linrec.bwd(q, k, v, inp.decay, st, dO, inp.dS_out)
+    torch.cuda.synchronize()
+    for name, x in dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in).items():
+        assert torch.equal(x, base[name]), name
+
+
+if __name__ == "__main__":
+    sys.exit(pytest.main([__file__, "-v", "-s"]))

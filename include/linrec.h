@@ -202,6 +202,24 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              linrec_tensor dv, float* dS_in, void* workspace,
                              void* stream);
 
+/* Kernel kinds for linrec_ctx_kernel_times(). */
+enum {
+    LINREC_KERNEL_FWD_SCAN = 0,   /* forward state transition (S carried)      */
+    LINREC_KERNEL_FWD_INTRA = 1,  /* forward intra-chunk output                */
+    LINREC_KERNEL_BWD_SCAN = 2,   /* reverse state transition (dS carried)     */
+    LINREC_KERNEL_BWD_INTRA = 3,  /* backward per-chunk dQ, dK, dV             */
+    LINREC_KERNEL_KINDS = 4
+};
+
+/* Per-kernel timing (instrumentation, off by default).  While enabled, every
+ * kernel the context launches is bracketed by two HIP events recorded on
+ * the stream that kernel runs on.  Enabling or disabling resets the totals.
+ * linrec_ctx_kernel_times() waits for the recorded launches, adds them to
+ * the totals and returns the number of launches of `kind` and their summed
+ * duration in milliseconds. */
+linrec_status linrec_ctx_set_timing(linrec_ctx* ctx, int enable);
+linrec_status linrec_ctx_kernel_times(linrec_ctx* ctx, int kind, int64_t* count, double* ms);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* linrec_status_str(linrec_status s);
 

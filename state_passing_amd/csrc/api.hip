@@ -7,6 +7,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <new>
+#include <vector>
+
 #include "launch.hpp"
 #include "linrec.h"
 
@@ -15,12 +18,23 @@ using linrec::FwdIntraLaunch;
 using linrec::ScanLaunch;
 using linrec::TensorArg;
 
+struct TimedLaunch {
+    int kind;
+    hipEvent_t begin, end;
+};
+
 struct linrec_ctx {
     int device;
     hipStream_t aux;        // state transitions
     hipEvent_t ev_start;    // inputs ready on the caller's stream
     hipEvent_t ev_scan;     // a piece's scan finished (aux)
     hipEvent_t ev_intra[2]; // a piece's per-chunk kernel finished (caller's stream)
+    // opt-in per-kernel timing (linrec_ctx_set_timing)
+    int timing;
+    std::vector<TimedLaunch> pending;
+    std::vector<hipEvent_t> pool;
+    double ms[LINREC_KERNEL_KINDS];
+    int64_t count[LINREC_KERNEL_KINDS];
 };
 
 namespace {
@@ -283,12 +297,59 @@ BwdIntraLaunch bwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
     return s;
 }
 
+hipError_t pool_event(linrec_ctx* ctx, hipEvent_t* ev)
+{
+    if (!ctx->pool.empty()) {
+        *ev = ctx->pool.back();
+        ctx->pool.pop_back();
+        return hipSuccess;
+    }
+    return hipEventCreate(ev);
+}
+
+// Launch `fn` on `stream`; with timing on, bracket it by events on that stream.
+template <typename F>
+hipError_t timed_launch(linrec_ctx* ctx, int kind, hipStream_t stream, F fn)
+{
+    if (!ctx->timing)
+        return fn();
+    TimedLaunch t{kind, nullptr, nullptr};
+    hipError_t e = pool_event(ctx, &t.begin);
+    if (e == hipSuccess)
+        e = pool_event(ctx, &t.end);
+    if (e == hipSuccess)
+        e = hipEventRecord(t.begin, stream);
+    if (e == hipSuccess)
+        e = fn();
+    if (e == hipSuccess)
+        e = hipEventRecord(t.end, stream);
+    if (e != hipSuccess) {
+        if (t.begin)
+            ctx->pool.push_back(t.begin);
+        if (t.end)
+            ctx->pool.push_back(t.end);
+        return e;
+    }
+    ctx->pending.push_back(t);
+    return hipSuccess;
+}
+
 #define LAUNCH(call)                                              \
     do {                                                          \
         hipError_t e_ = (call);                                   \
         if (e_ != hipSuccess)                                     \
             return hip_fail(e_, LINREC_E_LAUNCH);                 \
     } while (0)
+
+#define LAUNCH_SCAN(ctx, desc, stream)                                                     \
+    LAUNCH(timed_launch((ctx), (desc).reverse ? LINREC_KERNEL_BWD_SCAN : LINREC_KERNEL_FWD_SCAN, \
+                        (stream), [&] { return linrec::launch_state_scan((desc), (stream)); }))
+#define LAUNCH_FWD_INTRA(ctx, desc, stream)                                                \
+    LAUNCH(timed_launch((ctx), LINREC_KERNEL_FWD_INTRA, (stream),                          \
+                        [&] { return linrec::launch_fwd_intra((desc), (stream)); }))
+#define LAUNCH_BWD_INTRA(ctx, desc, stream)                                                \
+    LAUNCH(timed_launch((ctx), LINREC_KERNEL_BWD_INTRA, (stream),                          \
+                        [&] { return linrec::launch_bwd_intra((desc), (stream)); }))
 
 #define HIPCHECK(call)                                            \
     do {                                                          \
@@ -308,7 +369,7 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device)
     int prev = -1;
     HIPCHECK(hipGetDevice(&prev));
     HIPCHECK(hipSetDevice(device));
-    linrec_ctx* c = (linrec_ctx*)calloc(1, sizeof(linrec_ctx));
+    linrec_ctx* c = new (std::nothrow) linrec_ctx();
     if (!c) {
         (void)hipSetDevice(prev);
         return LINREC_E_DEVICE;
@@ -345,9 +406,56 @@ linrec_status linrec_ctx_destroy(linrec_ctx* ctx)
     for (int i = 0; i < 2; ++i)
         if (ctx->ev_intra[i])
             (void)hipEventDestroy(ctx->ev_intra[i]);
+    for (const TimedLaunch& t : ctx->pending) {
+        (void)hipEventDestroy(t.begin);
+        (void)hipEventDestroy(t.end);
+    }
+    for (hipEvent_t e : ctx->pool)
+        (void)hipEventDestroy(e);
     if (ctx->aux)
         (void)hipStreamDestroy(ctx->aux);
-    free(ctx);
+    delete ctx;
+    return LINREC_OK;
+}
+
+linrec_status linrec_ctx_set_timing(linrec_ctx* ctx, int enable)
+{
+    if (!ctx)
+        return LINREC_E_NULL;
+    ctx->timing = enable ? 1 : 0;
+    for (int k = 0; k < LINREC_KERNEL_KINDS; ++k) {
+        ctx->ms[k] = 0.0;
+        ctx->count[k] = 0;
+    }
+    for (const TimedLaunch& t : ctx->pending) {
+        ctx->pool.push_back(t.begin);
+        ctx->pool.push_back(t.end);
+    }
+    ctx->pending.clear();
+    return LINREC_OK;
+}
+
+linrec_status linrec_ctx_kernel_times(linrec_ctx* ctx, int kind, int64_t* count, double* ms)
+{
+    if (!ctx || !count || !ms)
+        return LINREC_E_NULL;
+    if (kind < 0 || kind >= LINREC_KERNEL_KINDS)
+        return LINREC_E_SHAPE;
+    for (const TimedLaunch& t : ctx->pending) {
+        float el = 0.f;
+        hipError_t e = hipEventSynchronize(t.end);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&el, t.begin, t.end);
+        if (e != hipSuccess)
+            return hip_fail(e, LINREC_E_DEVICE);
+        ctx->ms[t.kind] += el;
+        ctx->count[t.kind] += 1;
+        ctx->pool.push_back(t.begin);
+        ctx->pool.push_back(t.end);
+    }
+    ctx->pending.clear();
+    *count = ctx->count[kind];
+    *ms = ctx->ms[kind];
     return LINREC_OK;
 }
 
@@ -382,8 +490,10 @@ linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
         return st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t N = d->T / kChunk;
-    LAUNCH(linrec::launch_state_scan(fwd_scan_of(d, k, v, decay, 0, d->T, S_in, S_out, states, 0, N), s));
-    LAUNCH(linrec::launch_fwd_intra(fwd_intra_of(d, q, k, v, decay, o, 0, d->T, states, 0, N), s));
+    const ScanLaunch sc = fwd_scan_of(d, k, v, decay, 0, d->T, S_in, S_out, states, 0, N);
+    const FwdIntraLaunch in = fwd_intra_of(d, q, k, v, decay, o, 0, d->T, states, 0, N);
+    LAUNCH_SCAN(ctx, sc, s);
+    LAUNCH_FWD_INTRA(ctx, in, s);
     return LINREC_OK;
 }
 
@@ -399,9 +509,11 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
         return st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t N = d->T / kChunk;
-    LAUNCH(linrec::launch_state_scan(bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace), s));
-    LAUNCH(linrec::launch_bwd_intra(
-        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, N, workspace), s));
+    const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
+    const BwdIntraLaunch in =
+        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, N, workspace);
+    LAUNCH_SCAN(ctx, sc, s);
+    LAUNCH_BWD_INTRA(ctx, in, s);
     return LINREC_OK;
 }
 
@@ -423,12 +535,14 @@ linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         const int64_t chunk0 = tok0 / kChunk;
         // piece i's state transition: S carried in S_out from piece i-1
         const float* cin = i == 0 ? S_in : S_out;
-        LAUNCH(linrec::launch_state_scan(
-            fwd_scan_of(d, k, v, decay, tok0, lengths[i], cin, S_out, states, chunk0, Ntot), ctx->aux));
+        const ScanLaunch sc =
+            fwd_scan_of(d, k, v, decay, tok0, lengths[i], cin, S_out, states, chunk0, Ntot);
+        const FwdIntraLaunch in =
+            fwd_intra_of(d, q, k, v, decay, o, tok0, lengths[i], states, chunk0, Ntot);
+        LAUNCH_SCAN(ctx, sc, ctx->aux);
         HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
         HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
-        LAUNCH(linrec::launch_fwd_intra(
-            fwd_intra_of(d, q, k, v, decay, o, tok0, lengths[i], states, chunk0, Ntot), s));
+        LAUNCH_FWD_INTRA(ctx, in, s);
         tok0 += lengths[i];
     }
     return LINREC_OK;
@@ -467,13 +581,13 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         if (slot_used[slot])
             HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_intra[slot], 0));
         const float* cin = i == npieces - 1 ? dS_out : dS_in;
-        LAUNCH(linrec::launch_state_scan(
-            bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, ghat), ctx->aux));
+        const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, ghat);
+        const BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0, lengths[i],
+                                               states, tok0 / kChunk, Ntot, ghat);
+        LAUNCH_SCAN(ctx, sc, ctx->aux);
         HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
         HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
-        LAUNCH(linrec::launch_bwd_intra(bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0,
-                                                     lengths[i], states, tok0 / kChunk, Ntot, ghat),
-                                        s));
+        LAUNCH_BWD_INTRA(ctx, in, s);
         HIPCHECK(hipEventRecord(ctx->ev_intra[slot], s));
         slot_used[slot] = true;
         tok_end = tok0;

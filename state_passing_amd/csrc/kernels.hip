@@ -32,7 +32,43 @@ namespace linrec {
 // the X tile (K or Q, rows scaled by the decay factor, split hi + lo) and the
 // Y tile (V or dO, exact) through LDS, store the carried tile (fp32), then
 // carry = gamma_C carry + X^T Y.
+//
+// The carry is the only serial dependency, so the kernel is a software
+// pipeline: the global loads of chunk it+2 are in flight while chunk it is
+// staged and multiplied (two register buffers, 16-byte loads).
 // ---------------------------------------------------------------------------
+template <typename T>
+struct ScanTile {
+    static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte vector
+    static constexpr int NV = 32 / VEC;            // vectors per lane per 64x32 tile
+    uint4 x[NV], y[NV];
+};
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<bf16> {
+    typedef bf16x8 type;
+};
+template <>
+struct Vec16<float> {
+    typedef floatx4 type;
+};
+
+template <typename T>
+__device__ __forceinline__ void scan_load(ScanTile<T>& r, const T* xh, const T* yh, int64_t xst,
+                                          int64_t yst, int64_t tok0)
+{
+    constexpr int VEC = ScanTile<T>::VEC, PR = 32 / VEC;
+    const int l = lane_id();
+#pragma unroll
+    for (int p = 0; p < ScanTile<T>::NV; ++p) {
+        const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
+        r.x[p] = *reinterpret_cast<const uint4*>(xh + (tok0 + row) * xst + col);
+        r.y[p] = *reinterpret_cast<const uint4*>(yh + (tok0 + row) * yst + col);
+    }
+}
+
 template <typename T, int DK, int DV, bool REVERSE>
 __global__ __launch_bounds__(64) void state_scan_kernel(
     Act<const T> X, Act<const T> Y, DecayArg dec, const float* __restrict__ carry_in,
@@ -42,10 +78,9 @@ __global__ __launch_bounds__(64) void state_scan_kernel(
     constexpr int PAD = Pad<T>::value;
     constexpr int XP = TF + PAD, YP = TC + PAD;
     constexpr int NTC = DV / TC;
-    constexpr int VEC = 16 / sizeof(T);
+    constexpr int VEC = ScanTile<T>::VEC, NV = ScanTile<T>::NV, PR = 32 / VEC;
     __shared__ __align__(16) T Xs[2][CHUNK * XP];
     __shared__ __align__(16) T Ys[CHUNK * YP];
-    __shared__ float lam[CHUNK];
 
     const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int f0 = (tile / NTC) * TF, c0 = (tile % NTC) * TC;
@@ -68,24 +103,53 @@ __global__ __launch_bounds__(64) void state_scan_kernel(
     const T* yh = Y.head(b, h) + c0;
     float* sh = store + bh * store_nchunks * (int64_t)(DV * DK);
 
-    for (int it = 0; it < N; ++it) {
-        const int n = REVERSE ? N - 1 - it : it;
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        const float lm = chunk_log_cumsum(dec, b, h, tok0);
-        const float lamC = __shfl(lm, 63, 64);
-        lam[l] = lm;
-        __syncthreads();
-
-        // X rows scaled by exp(lamC - lam_j) (forward) or exp(lam_i) (reverse)
-        for (int idx = l; idx < CHUNK * (TF / VEC); idx += 64) {
-            const int r = idx / (TF / VEC), c = (idx % (TF / VEC)) * VEC;
-            const float s = REVERSE ? __expf(lam[r]) : __expf(lamC - lam[r]);
-            const T* src = xh + (tok0 + r) * X.st + c;
+    // row scale of the X vectors this lane stages, and the chunk decay; for a
+    // per-head (or absent) decay they are the same for every chunk
+    const bool const_decay = dec.kind != 2;
+    float lm = chunk_log_cumsum(dec, b, h, 0);
+    float lamC = __shfl(lm, 63, 64);
+    float xs[NV];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                put_split(Xs[0], Xs[1], r * XP + c + e, (float)src[e] * s);
+    for (int p = 0; p < NV; ++p) {
+        const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
+        xs[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
+    }
+
+    typedef typename Vec16<T>::type V;
+    const auto chunk_of = [&](int it) { return REVERSE ? N - 1 - it : it; };
+
+    // one pipeline stage: stage chunk `it` from `cur`, refill `cur` with chunk
+    // it+2, store the carried tile and advance the carry
+    const auto stage = [&](int it, ScanTile<T>& cur) {
+        const int n = chunk_of(it);
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        if (!const_decay) {
+            lm = chunk_log_cumsum(dec, b, h, tok0);
+            lamC = __shfl(lm, 63, 64);
+#pragma unroll
+            for (int p = 0; p < NV; ++p) {
+                const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
+                xs[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
+            }
         }
-        stage_rows<T, CHUNK, TC, 64>(Ys, YP, yh + tok0 * Y.st, Y.st);
+#pragma unroll
+        for (int p = 0; p < NV; ++p) {
+            const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
+            const V xv = __builtin_bit_cast(V, cur.x[p]);
+            V hi, lo;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float v = (float)xv[e] * xs[p];
+                hi[e] = (T)v;
+                lo[e] = (T)(v - (float)hi[e]);
+            }
+            *reinterpret_cast<V*>(&Xs[0][row * XP + col]) = hi;
+            if constexpr (sizeof(T) == 2)
+                *reinterpret_cast<V*>(&Xs[1][row * XP + col]) = lo;
+            *reinterpret_cast<uint4*>(&Ys[row * YP + col]) = cur.y[p];
+        }
+        if (it + 2 < N)
+            scan_load(cur, xh, yh, X.st, Y.st, (int64_t)chunk_of(it + 2) * CHUNK);
         __syncthreads();
 
         // store the carried tile, transposed ([c][f], f contiguous), fp32
@@ -127,6 +191,16 @@ __global__ __launch_bounds__(64) void state_scan_kernel(
             for (int cb = 0; cb < 2; ++cb)
                 carry[fb][cb] = gC * carry[fb][cb] + dlt[fb][cb];
         __syncthreads();
+    };
+
+    ScanTile<T> buf0, buf1;
+    scan_load(buf0, xh, yh, X.st, Y.st, (int64_t)chunk_of(0) * CHUNK);
+    if (N > 1)
+        scan_load(buf1, xh, yh, X.st, Y.st, (int64_t)chunk_of(1) * CHUNK);
+    for (int it = 0; it < N; it += 2) {
+        stage(it, buf0);
+        if (it + 1 < N)
+            stage(it + 1, buf1);
     }
 
 #pragma unroll

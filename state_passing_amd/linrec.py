@@ -37,8 +37,11 @@ EXPORTS = (
     "linrec_ctx_create", "linrec_ctx_destroy", "linrec_states_bytes",
     "linrec_bwd_workspace_bytes", "linrec_fwd", "linrec_bwd", "linrec_fwd_seq",
     "linrec_bwd_seq_workspace_bytes", "linrec_bwd_seq", "linrec_status_str",
-    "linrec_last_hip_error", "linrec_version",
+    "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
+    "linrec_ctx_kernel_times",
 )
+
+KERNEL_KINDS = {0: "fwd_scan", 1: "fwd_intra", 2: "bwd_scan", 3: "bwd_intra"}
 
 
 class LinrecError(RuntimeError):
@@ -87,6 +90,9 @@ def _lib():
         "linrec_status_str": ([ctypes.c_int], ctypes.c_char_p),
         "linrec_last_hip_error": ([], ctypes.c_int),
         "linrec_version": ([], ctypes.c_int),
+        "linrec_ctx_set_timing": ([P, ctypes.c_int], ctypes.c_int),
+        "linrec_ctx_kernel_times": ([P, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -118,6 +124,23 @@ def context(device: Optional[int] = None) -> int:
             raise LinrecError(rc, "linrec_ctx_create")
         _CTX[device] = p.value
     return _CTX[device]
+
+
+def set_kernel_timing(enable: bool, device: Optional[int] = None) -> None:
+    """Turn the context's per-kernel event timing on or off (resets totals)."""
+    _check(_lib().linrec_ctx_set_timing(context(device), 1 if enable else 0),
+           "linrec_ctx_set_timing")
+
+
+def kernel_times(device: Optional[int] = None) -> dict:
+    """{kernel name: (launches, total ms)} since timing was enabled."""
+    out = {}
+    for kind, name in KERNEL_KINDS.items():
+        n, ms = ctypes.c_int64(), ctypes.c_double()
+        _check(_lib().linrec_ctx_kernel_times(context(device), kind, ctypes.byref(n),
+                                              ctypes.byref(ms)), "linrec_ctx_kernel_times")
+        out[name] = (int(n.value), float(ms.value))
+    return out
 
 
 # ----------------------------------------------------------------- marshalling

@@ -17,16 +17,19 @@
  * the right-product form of linear attention with cached intermediate
  * states (Linear Attention Sequence Parallelism, abstract).
  *
- * Inside a piece the work is done chunkwise with C = 64 tokens per chunk:
- *   - a state-transition kernel walks the chunks in order, carrying S in
- *     fp32 registers and storing the state entering every chunk ("states");
- *   - an intra-chunk kernel computes, for every chunk independently,
+ * Inside a piece the work is done chunkwise with C = 64 tokens per chunk,
+ * chunks grouped into segments of 4:
+ *   - a state-transition kernel (the segment scan) carries S across the
+ *     piece in fp32 and stores the state entering every segment ("states");
+ *   - a segment kernel walks each segment's chunks with the state in
+ *     registers and computes, per chunk,
  *         O_n = [(Q_n K_n^T) .* D_n] V_n + (Q_n .* gamma) S_{n-1}
  *     where gamma_i is the chunk-local cumulative decay of token i and
  *     D_ij = gamma_i / gamma_j for j <= i (0 above the diagonal).
- *   The backward mirrors this: a reverse scan carries dS from dS_out back to
- *   dS_in and stores the gradient leaving every chunk; a per-chunk kernel
- *   computes dQ, dK, dV from the stored states.
+ *   The backward mirrors this: a reverse segment scan carries dS from
+ *   dS_out back to dS_in and stores the gradient leaving every segment; a
+ *   segment kernel rebuilds the per-chunk states and gradients from the
+ *   stored ones and computes dQ, dK, dV.
  *
  * ---------------------------------------------------------------- layouts
  *   Activations q, k (d_k wide), v, o, dO, dq, dk, dv (d_v or d_k wide) are
@@ -129,16 +132,21 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device);
 /* Destroy a context; waits for its auxiliary stream.  NULL is a no-op. */
 linrec_status linrec_ctx_destroy(linrec_ctx* ctx);
 
-/* Bytes of the per-chunk state store for `d` (0 if `d` is invalid).  It is
- * B*H*(T/64)*d_k*d_v fp32 values: the state entering every chunk, written by
- * linrec_fwd and read by linrec_bwd.  It depends on T only through T/64
- * (linear in the piece length, constant in the number of pieces already
- * processed). */
+/* Bytes of the state store of one piece described by `d` (0 if `d` is
+ * invalid): B*H*ceil(T/256)*d_k*d_v fp32 values, the state entering every
+ * segment of 4 chunks, written by linrec_fwd and read by linrec_bwd.  It
+ * depends on the piece length only (constant in the number of pieces
+ * already processed). */
 size_t linrec_states_bytes(const linrec_desc* d);
 
 /* Bytes of backward workspace for `d` (0 if `d` is invalid): the gradient
- * leaving every chunk, B*H*(T/64)*d_k*d_v fp32 values. */
+ * leaving every segment, B*H*ceil(T/256)*d_k*d_v fp32 values. */
 size_t linrec_bwd_workspace_bytes(const linrec_desc* d);
+
+/* Bytes of the state store linrec_fwd_seq / linrec_bwd_seq need for these
+ * pieces of the sequence `d` (the sum of the pieces' own stores; 0 if the
+ * arguments are invalid). */
+size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths);
 
 /* Forward over one piece.
  *   q, k: [B,H,T,d_k];  v, o: [B,H,T,d_v];  decay per d->decay.
@@ -177,7 +185,7 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d,
  * transition overlaps piece i's intra-chunk work (state transitions with
  * limited parallelism overlapped with surrounding computation: StateFlow,
  * Abstract).  `states` covers the whole sequence
- * (linrec_states_bytes(d) with the total T).  Same arguments and rules as
+ * (linrec_seq_states_bytes() bytes).  Same arguments and rules as
  * linrec_fwd otherwise. */
 linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              int32_t npieces, const int32_t* lengths,

@@ -42,6 +42,11 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int kChunk = 64;
+// Chunks per segment: the segment kernels rebuild every per-chunk state of a
+// segment in registers; only the state at each segment boundary is stored.
+constexpr int kSegChunks = 4;
+
+int64_t nseg_of(int64_t tokens) { return (tokens / kChunk + kSegChunks - 1) / kSegChunks; }
 
 linrec_status hip_fail(hipError_t e, linrec_status code)
 {
@@ -142,10 +147,26 @@ linrec_status check_pieces(const linrec_desc* d, int32_t npieces, const int32_t*
     return sum == d->T ? LINREC_OK : LINREC_E_SHAPE;
 }
 
-// Stored per-chunk states and gradients are fp32 whatever the activation dtype.
-size_t per_chunk_matrix_bytes(const linrec_desc* d)
+// Stored per-segment states and gradients are fp32 whatever the activation dtype.
+size_t per_seg_bytes(const linrec_desc* d)
 {
     return (size_t)d->dk * (size_t)d->dv * sizeof(float);
+}
+
+int64_t total_nseg(int32_t npieces, const int32_t* lengths)
+{
+    int64_t n = 0;
+    for (int32_t i = 0; i < npieces; ++i)
+        n += nseg_of(lengths[i]);
+    return n;
+}
+
+int64_t max_nseg(int32_t npieces, const int32_t* lengths)
+{
+    int64_t n = 0;
+    for (int32_t i = 0; i < npieces; ++i)
+        n = nseg_of(lengths[i]) > n ? nseg_of(lengths[i]) : n;
+    return n;
 }
 
 TensorArg targ(const linrec_tensor& t) { return TensorArg{t.ptr, t.sb, t.sh, t.st}; }
@@ -214,11 +235,12 @@ linrec_status check_bwd_args(const linrec_desc* d, const linrec_tensor& q,
 ScanLaunch fwd_scan_of(const linrec_desc* d, const linrec_tensor& k, const linrec_tensor& v,
                        const linrec_tensor& decay, int64_t tok0, int32_t len,
                        const float* carry_in, float* carry_out, void* states,
-                       int64_t chunk0, int64_t nchunks_total)
+                       int64_t seg0, int64_t nseg_total)
 {
     const int esz = elem_size(d->dtype);
     ScanLaunch s{};
     s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.m = kSegChunks;
     s.reverse = false;
     s.x = advance(k, tok0, esz);
     s.y = advance(v, tok0, esz);
@@ -226,28 +248,29 @@ ScanLaunch fwd_scan_of(const linrec_desc* d, const linrec_tensor& k, const linre
     s.decay_kind = d->decay;
     s.carry_in = carry_in;
     s.carry_out = carry_out;
-    s.store = (char*)states + chunk0 * per_chunk_matrix_bytes(d);
-    s.store_nchunks = nchunks_total;
+    s.store = (char*)states + seg0 * per_seg_bytes(d);
+    s.store_nseg = nseg_total;
     return s;
 }
 
 FwdIntraLaunch fwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const linrec_tensor& k,
                             const linrec_tensor& v, const linrec_tensor& decay,
                             const linrec_tensor& o, int64_t tok0, int32_t len,
-                            const void* states, int64_t chunk0, int64_t nchunks_total)
+                            const void* states, int64_t seg0, int64_t nseg_total)
 {
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     FwdIntraLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype;
     s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.m = kSegChunks;
     s.q = advance(q, tok0, esz);
     s.k = advance(k, tok0, esz);
     s.v = advance(v, tok0, esz);
     s.o = advance(o, tok0, osz);
     s.decay = advance_decay(d, decay, tok0);
     s.decay_kind = d->decay;
-    s.states = (const char*)states + chunk0 * per_chunk_matrix_bytes(d);
-    s.st_nchunks = nchunks_total;
+    s.states = (const char*)states + seg0 * per_seg_bytes(d);
+    s.st_nseg = nseg_total;
     return s;
 }
 
@@ -258,6 +281,7 @@ ScanLaunch bwd_scan_of(const linrec_desc* d, const linrec_tensor& q, const linre
     const int esz = elem_size(d->dtype);
     ScanLaunch s{};
     s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.m = kSegChunks;
     s.reverse = true;
     s.x = advance(q, tok0, esz);
     s.y = advance(dO, tok0, esz);
@@ -266,7 +290,7 @@ ScanLaunch bwd_scan_of(const linrec_desc* d, const linrec_tensor& q, const linre
     s.carry_in = carry_in;
     s.carry_out = carry_out;
     s.store = ghat;
-    s.store_nchunks = len / kChunk;
+    s.store_nseg = nseg_of(len);
     return s;
 }
 
@@ -274,13 +298,14 @@ BwdIntraLaunch bwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
                             const linrec_tensor& v, const linrec_tensor& decay,
                             const linrec_tensor& dO, const linrec_tensor& dq,
                             const linrec_tensor& dk, const linrec_tensor& dv, int64_t tok0,
-                            int32_t len, const void* states, int64_t chunk0,
-                            int64_t nchunks_total, const void* ghat)
+                            int32_t len, const void* states, int64_t seg0,
+                            int64_t nseg_total, const void* ghat)
 {
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     BwdIntraLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype;
     s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.m = kSegChunks;
     s.q = advance(q, tok0, esz);
     s.k = advance(k, tok0, esz);
     s.v = advance(v, tok0, esz);
@@ -290,10 +315,10 @@ BwdIntraLaunch bwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
     s.dv_ = advance(dv, tok0, osz);
     s.decay = advance_decay(d, decay, tok0);
     s.decay_kind = d->decay;
-    s.states = (const char*)states + chunk0 * per_chunk_matrix_bytes(d);
-    s.st_nchunks = nchunks_total;
+    s.states = (const char*)states + seg0 * per_seg_bytes(d);
+    s.st_nseg = nseg_total;
     s.ghat = ghat;
-    s.g_nchunks = len / kChunk;
+    s.g_nseg = nseg_of(len);
     return s;
 }
 
@@ -463,21 +488,25 @@ size_t linrec_states_bytes(const linrec_desc* d)
 {
     if (check_desc(d) != LINREC_OK)
         return 0;
-    return (size_t)d->B * (size_t)d->H * (size_t)(d->T / kChunk) * per_chunk_matrix_bytes(d);
+    return (size_t)d->B * (size_t)d->H * (size_t)nseg_of(d->T) * per_seg_bytes(d);
 }
 
 size_t linrec_bwd_workspace_bytes(const linrec_desc* d) { return linrec_states_bytes(d); }
+
+size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
+{
+    if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
+        return 0;
+    return (size_t)d->B * (size_t)d->H * (size_t)total_nseg(npieces, lengths) * per_seg_bytes(d);
+}
 
 size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
         return 0;
-    int32_t longest = 0;
-    for (int32_t i = 0; i < npieces; ++i)
-        longest = lengths[i] > longest ? lengths[i] : longest;
     const int slots = npieces > 1 ? 2 : 1;
-    return (size_t)slots * (size_t)d->B * (size_t)d->H * (size_t)(longest / kChunk) *
-           per_chunk_matrix_bytes(d);
+    return (size_t)slots * (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) *
+           per_seg_bytes(d);
 }
 
 linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
@@ -489,9 +518,9 @@ linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     if (st != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t N = d->T / kChunk;
-    const ScanLaunch sc = fwd_scan_of(d, k, v, decay, 0, d->T, S_in, S_out, states, 0, N);
-    const FwdIntraLaunch in = fwd_intra_of(d, q, k, v, decay, o, 0, d->T, states, 0, N);
+    const int64_t ns = nseg_of(d->T);
+    const ScanLaunch sc = fwd_scan_of(d, k, v, decay, 0, d->T, S_in, S_out, states, 0, ns);
+    const FwdIntraLaunch in = fwd_intra_of(d, q, k, v, decay, o, 0, d->T, states, 0, ns);
     LAUNCH_SCAN(ctx, sc, s);
     LAUNCH_FWD_INTRA(ctx, in, s);
     return LINREC_OK;
@@ -508,10 +537,10 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     if (st != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t N = d->T / kChunk;
+    const int64_t ns = nseg_of(d->T);
     const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
     const BwdIntraLaunch in =
-        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, N, workspace);
+        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, workspace);
     LAUNCH_SCAN(ctx, sc, s);
     LAUNCH_BWD_INTRA(ctx, in, s);
     return LINREC_OK;
@@ -527,23 +556,23 @@ linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t Ntot = d->T / kChunk;
+    const int64_t nseg_total = total_nseg(npieces, lengths);
     HIPCHECK(hipEventRecord(ctx->ev_start, s));
     HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_start, 0));
-    int64_t tok0 = 0;
+    int64_t tok0 = 0, seg0 = 0;
     for (int32_t i = 0; i < npieces; ++i) {
-        const int64_t chunk0 = tok0 / kChunk;
         // piece i's state transition: S carried in S_out from piece i-1
         const float* cin = i == 0 ? S_in : S_out;
         const ScanLaunch sc =
-            fwd_scan_of(d, k, v, decay, tok0, lengths[i], cin, S_out, states, chunk0, Ntot);
+            fwd_scan_of(d, k, v, decay, tok0, lengths[i], cin, S_out, states, seg0, nseg_total);
         const FwdIntraLaunch in =
-            fwd_intra_of(d, q, k, v, decay, o, tok0, lengths[i], states, chunk0, Ntot);
+            fwd_intra_of(d, q, k, v, decay, o, tok0, lengths[i], states, seg0, nseg_total);
         LAUNCH_SCAN(ctx, sc, ctx->aux);
         HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
         HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
         LAUNCH_FWD_INTRA(ctx, in, s);
         tok0 += lengths[i];
+        seg0 += nseg_of(lengths[i]);
     }
     return LINREC_OK;
 }
@@ -561,21 +590,19 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const int64_t Ntot = d->T / kChunk;
-    int32_t longest = 0;
-    for (int32_t i = 0; i < npieces; ++i)
-        longest = lengths[i] > longest ? lengths[i] : longest;
+    const int64_t nseg_total = total_nseg(npieces, lengths);
     const size_t slot_bytes =
-        (size_t)d->B * d->H * (size_t)(longest / kChunk) * per_chunk_matrix_bytes(d);
+        (size_t)d->B * d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
 
     HIPCHECK(hipEventRecord(ctx->ev_start, s));
     HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_start, 0));
     // Per-chunk gradients of piece i go to slot i % 2; before a scan
     // overwrites a slot it waits for the per-chunk kernel that read it.
     bool slot_used[2] = {false, false};
-    int64_t tok_end = d->T;
+    int64_t tok_end = d->T, seg_end = nseg_total;
     for (int32_t i = npieces - 1; i >= 0; --i) {
         const int64_t tok0 = tok_end - lengths[i];
+        const int64_t seg0 = seg_end - nseg_of(lengths[i]);
         const int slot = i & 1;
         void* ghat = (char*)workspace + slot * slot_bytes;
         if (slot_used[slot])
@@ -583,7 +610,7 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         const float* cin = i == npieces - 1 ? dS_out : dS_in;
         const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, ghat);
         const BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0, lengths[i],
-                                               states, tok0 / kChunk, Ntot, ghat);
+                                               states, seg0, nseg_total, ghat);
         LAUNCH_SCAN(ctx, sc, ctx->aux);
         HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
         HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
@@ -591,6 +618,7 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         HIPCHECK(hipEventRecord(ctx->ev_intra[slot], s));
         slot_used[slot] = true;
         tok_end = tok0;
+        seg_end = seg0;
     }
     return LINREC_OK;
 }

@@ -30,6 +30,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
+// 16 raw bytes as a native vector (HIP's uint4 is a struct: copies of it
+// become memcpy calls that keep staging registers in private memory)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Decay description as the kernels see it (kind: 0 none, 1 per head, 2 per token).
 struct DecayArg {
@@ -125,6 +128,58 @@ __device__ __forceinline__ Frag<float> frag_cols(const float* tile, int pitch, i
     return f;
 }
 
+// Fragments in the k-slot order of a pair of 16x16 result tiles: slot r < 4
+// is k = kbase + 4g + r (first tile's rows), slot r >= 4 is k = kbase + 16 +
+// 4g + (r - 4) (second tile's rows).  A result tile held in registers can
+// then serve as the other operand without moving between lanes.
+//   frag_rows_perm: lane (g,t) <- tile[rbase + t][k(slot)]
+//   frag_cols_perm: lane (g,t) <- tile[k(slot)][cbase + t]
+__device__ __forceinline__ Frag<bf16> frag_rows_perm(const bf16* tile, int pitch, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const bf16* p = tile + (rbase + t) * pitch + kbase + 4 * g;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+    Frag<bf16> f;
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_rows_perm(const float* tile, int pitch, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const float* p = tile + (rbase + t) * pitch + kbase + 4 * g;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 16);
+    Frag<float> f;
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+}
+
+__device__ __forceinline__ Frag<bf16> frag_cols_perm(const bf16* tile, int pitch, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const bf16* p = tile + (kbase + 4 * g + (t >> 2)) * pitch + cbase + 4 * (t & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * pitch));
+    Frag<bf16> f;
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
+
+__device__ __forceinline__ Frag<float> frag_cols_perm(const float* tile, int pitch, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f.v[r] = tile[(kbase + 4 * g + r) * pitch + cbase + t];
+        f.v[4 + r] = tile[(kbase + 16 + 4 * g + r) * pitch + cbase + t];
+    }
+    return f;
+}
+
 // Fragment read straight from global memory, k contiguous: lane (g,t) <-
 // base[(rbase + t) * ld + kbase + 8g + r].
 __device__ __forceinline__ Frag<bf16> frag_rows_global(const bf16* base, int64_t ld, int rbase, int kbase)
@@ -174,12 +229,107 @@ __device__ __forceinline__ void stage_rows(T* lds, int pitch, const T* src, int6
     static_assert(D % VEC == 0, "row must be a whole number of 16-byte vectors");
     for (int idx = threadIdx.x; idx < ROWS * PER_ROW; idx += NT) {
         const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-        *reinterpret_cast<uint4*>(lds + r * pitch + c) =
-            *reinterpret_cast<const uint4*>(src + r * ld + c);
+        *reinterpret_cast<u32x4*>(lds + r * pitch + c) =
+            *reinterpret_cast<const u32x4*>(src + r * ld + c);
     }
 }
 
+// A chunk's rows of one activation (64 x D elements) spread over the NT
+// threads of a workgroup as 16-byte vectors: chunk_load() issues the global
+// loads into registers, chunk_store() later writes them to LDS, so the loads
+// of the next chunk can be in flight while the current one is processed.
+template <typename T, int D, int NT>
+struct ChunkRegs {
+    static constexpr int VEC = 16 / sizeof(T);
+    static constexpr int PER_ROW = D / VEC;
+    static constexpr int NV = CHUNK * PER_ROW / NT;
+    static_assert(NV * NT == CHUNK * PER_ROW && NV >= 1 && NV <= 4,
+                  "chunk must split evenly over the threads, 1 to 4 vectors each");
+    u32x4 v0, v1, v2, v3;
+};
+
+template <int P, typename R>
+__device__ __forceinline__ u32x4& chunk_vec(R& r)
+{
+    if constexpr (P == 0)
+        return r.v0;
+    else if constexpr (P == 1)
+        return r.v1;
+    else if constexpr (P == 2)
+        return r.v2;
+    else
+        return r.v3;
+}
+
+template <int P, typename T, int D, int NT>
+__device__ __forceinline__ void chunk_load_one(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld)
+{
+    typedef ChunkRegs<T, D, NT> R;
+    if constexpr (P < R::NV) {
+        const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
+        chunk_vec<P>(r) = *reinterpret_cast<const u32x4*>(src + row * ld + col);
+    }
+}
+
+template <int P, typename T, int D, int NT>
+__device__ __forceinline__ void chunk_store_one(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+{
+    typedef ChunkRegs<T, D, NT> R;
+    if constexpr (P < R::NV) {
+        const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
+        *reinterpret_cast<u32x4*>(lds + row * pitch + col) = chunk_vec<P>(r);
+    }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void chunk_load(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld)
+{
+    chunk_load_one<0>(r, src, ld);
+    chunk_load_one<1>(r, src, ld);
+    chunk_load_one<2>(r, src, ld);
+    chunk_load_one<3>(r, src, ld);
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void chunk_store(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+{
+    chunk_store_one<0>(r, lds, pitch);
+    chunk_store_one<1>(r, lds, pitch);
+    chunk_store_one<2>(r, lds, pitch);
+    chunk_store_one<3>(r, lds, pitch);
+}
+
 // ---- decay ----------------------------------------------------------------
+
+// The raw decay this lane needs for the chunk starting at tok0 (token = lane
+// for per-token decay), so that it can be loaded a chunk ahead.
+__device__ __forceinline__ float decay_raw(const DecayArg& d, int b, int h, int64_t tok0)
+{
+    if (d.kind == 0)
+        return 1.f;
+    if (d.kind == 1)
+        return d.ptr[h * d.sh];
+    return d.ptr[b * d.sb + h * d.sh + (tok0 + lane_id()) * d.st];
+}
+
+// Inclusive cumulative log of the chunk's decays from decay_raw() values
+// (token = lane); called by a full wave.
+__device__ __forceinline__ float decay_log_cumsum(const DecayArg& d, float raw)
+{
+    const int lane = lane_id();
+    if (d.kind == 0)
+        return 0.f;
+    if (d.kind == 1)
+        return (float)(lane + 1) * logf(raw);
+    float x = logf(raw);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += y;
+    }
+    return x;
+}
 
 // Inclusive cumulative log-decay of the chunk's tokens, token = lane:
 // lam_i = sum_{r <= i} ln a_r over the chunk starting at token tok0.  Must be
@@ -264,6 +414,26 @@ __device__ __forceinline__ floatx4 mma(const Split<float>& a, const Frag<float>&
     return mma(a.hi, b, c);
 }
 
+// Split operand from two 16x16 result tiles in registers (k-slot order of
+// frag_rows_perm / frag_cols_perm).
+template <typename T>
+__device__ __forceinline__ Split<T> split_tiles(const floatx4& a, const floatx4& b)
+{
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return split8<T>(x);
+}
+
+// Split operand from a fragment of exact inputs times a per-slot factor.
+template <typename T>
+__device__ __forceinline__ Split<T> split_scaled(const Frag<T>& f, const float (&s)[8])
+{
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        x[r] = (float)f.v[r] * s[r];
+    return split8<T>(x);
+}
+
 // Write x into an LDS plane pair: hi[idx] and (bf16 only) lo[idx].
 template <typename T>
 __device__ __forceinline__ void put_split(T* hi, T* lo, int idx, float x)
@@ -317,6 +487,26 @@ __device__ __forceinline__ Split<T> gfrag_cols_split(const float* base, int64_t 
     for (int r = 0; r < 8; ++r)
         x[r] = base[(kbase + 8 * g + r) * ld + cbase + t];
     return split8<T>(x);
+}
+
+// Write the 4 values of a result tile a lane holds (rows 4g + r, column t) as
+// four consecutive elements of row `row` of an LDS plane pair (the tile
+// lands transposed: LDS row = tile column).
+template <typename T>
+__device__ __forceinline__ void put_split4(T* hi, T* lo, int idx, const floatx4& x)
+{
+    if constexpr (sizeof(T) == 2) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            h[r] = (bf16)x[r];
+            l[r] = (bf16)(x[r] - (float)h[r]);
+        }
+        *reinterpret_cast<bf16x4*>(hi + idx) = h;
+        *reinterpret_cast<bf16x4*>(lo + idx) = l;
+    } else {
+        *reinterpret_cast<float4*>(hi + idx) = float4{x[0], x[1], x[2], x[3]};
+    }
 }
 
 // Store a 16x16 fp32 result tile (lane (g,t) holds rows 4g + r, column t)

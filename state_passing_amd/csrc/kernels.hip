@@ -4,44 +4,65 @@
 // log-decay lam_i (token i inclusive), gamma_i = exp(lam_i), gamma_C =
 // exp(lam_63) and D_ij = exp(lam_i - lam_j) for j <= i (else 0):
 //
-//   state scan (forward):  store S_{n-1};  S_n = gamma_C S_{n-1} + (K .* gamma_C/gamma)^T V
-//   intra (forward):       O = [(Q K^T) .* D] V + (Q .* gamma) S_{n-1}
-//   state scan (reverse):  store G_n;  G_{n-1} = gamma_C G_n + (Q .* gamma)^T dO
-//   intra (backward):      dQ = [(dO V^T) .* D] K + (dO S_{n-1}^T) .* gamma
-//                          dK = [(V dO^T) .* D^T] Q + (V G_n^T) .* gamma_C/gamma
-//                          dV = [(K Q^T) .* D^T] dO + (K .* gamma_C/gamma) G_n
+//   forward    O_n = gamma .* (Q_n S_{n-1}) + [(Q_n K_n^T) .* D] V_n
+//              S_n = gamma_C S_{n-1} + (K_n .* gamma_C/gamma)^T V_n
+//   backward   G_{n-1} = gamma_C G_n + (Q_n .* gamma)^T dO_n
+//              dQ_n = gamma .* (dO_n S_{n-1}^T) + [(dO_n V_n^T) .* D] K_n
+//              dK_n = gamma_C/gamma .* (V_n G_n^T) + [(V_n dO_n^T) .* D^T] Q_n
+//              dV_n = gamma_C/gamma .* (K_n G_n)  + [(K_n Q_n^T) .* D^T] dO_n
 //
-// These are the chunk algebra of the token recurrence S_t = a_t S_{t-1} +
+// with G_n the gradient of the loss with respect to the state leaving chunk
+// n.  This is the chunk algebra of the token recurrence S_t = a_t S_{t-1} +
 // k_t^T v_t, o_t = q_t S_t: the right-product form of linear attention
 // (Linear Attention Sequence Parallelism, abstract) with a linear recurrence
 // inside each chunk and chunks joined by boundary states (StateFlow, the
-// gptget summary's method details).  G_n is the gradient of the loss with
-// respect to the state leaving chunk n.
+// gptget summary's method details).
 //
-// Stored per-chunk matrices (S_{n-1} and G_n) are kept transposed, [d_v][d_k]
-// with d_k contiguous, in the activation dtype: [B][H][nchunks][d_v][d_k].
+// Two levels.  Chunks are grouped into segments of m chunks.
+//   * The segment scan (one launch per direction and piece) is the serial
+//     state transition: it produces the state entering every segment (the
+//     gradient leaving every segment in the reverse direction) and the
+//     piece's boundary state.  Only those per-segment states reach memory.
+//   * The segment kernels (one workgroup per segment) walk the segment's
+//     chunks with the state in fp32 registers, rebuilding every per-chunk
+//     state on the fly; the backward walks forward for dQ (carrying S) and
+//     then in reverse for dK and dV (carrying G).
+// Per-segment states are stored transposed, [d_v][d_k] with d_k contiguous,
+// fp32: [B][H][nseg][d_v][d_k].
+//
+// Every operand these kernels compute (P, A, the decay-scaled K or Q, the
+// carried states) enters the MFMA as a bf16 hi + lo pair against an exact
+// bf16 activation; decay factors that depend only on an output row scale the
+// fp32 product instead of an operand.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace linrec {
 
+// Order this wave's LDS accesses (a wave's LDS operations complete in issue
+// order; this keeps the compiler from moving them across the point).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
-// State scan.  One wave per (b, h, 32x32 tile of the d_k x d_v state); the
-// tile is carried in fp32 MFMA accumulators across the chunks of the piece
-// (in order for the forward, reversed for the backward).  Per chunk: stage
-// the X tile (K or Q, rows scaled by the decay factor, split hi + lo) and the
-// Y tile (V or dO, exact) through LDS, store the carried tile (fp32), then
-// carry = gamma_C carry + X^T Y.
-//
-// The carry is the only serial dependency, so the kernel is a software
-// pipeline: the global loads of chunk it+2 are in flight while chunk it is
-// staged and multiplied (two register buffers, 16-byte loads).
+// Segment scan.  Workgroup = (b, h, 32x32 tile of the state), 4 waves.  In
+// round r wave w folds segment 4r + w (counted from the piece end in the
+// reverse direction) from a zero state: local = gamma_C local + X^T Y per
+// chunk, X = K rows scaled by gamma_C/gamma_j (forward) or Q rows scaled by
+// gamma_i (reverse), split hi + lo; Y = V or dO.  The four partial results
+// then go through LDS and every wave folds them in order into its copy of
+// the carried state; the wave that owns a segment writes the state at that
+// segment's boundary.  The fold is the only serial step; chunk loads run two
+// chunks ahead in registers.
 // ---------------------------------------------------------------------------
 template <typename T>
 struct ScanTile {
     static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte vector
     static constexpr int NV = 32 / VEC;            // vectors per lane per 64x32 tile
-    uint4 x[NV], y[NV];
+    u32x4 x[NV], y[NV];
 };
 
 template <typename T>
@@ -64,30 +85,36 @@ __device__ __forceinline__ void scan_load(ScanTile<T>& r, const T* xh, const T* 
 #pragma unroll
     for (int p = 0; p < ScanTile<T>::NV; ++p) {
         const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
-        r.x[p] = *reinterpret_cast<const uint4*>(xh + (tok0 + row) * xst + col);
-        r.y[p] = *reinterpret_cast<const uint4*>(yh + (tok0 + row) * yst + col);
+        r.x[p] = *reinterpret_cast<const u32x4*>(xh + (tok0 + row) * xst + col);
+        r.y[p] = *reinterpret_cast<const u32x4*>(yh + (tok0 + row) * yst + col);
     }
 }
 
 template <typename T, int DK, int DV, bool REVERSE>
-__global__ __launch_bounds__(64) void state_scan_kernel(
+__global__ __launch_bounds__(256) void seg_scan_kernel(
     Act<const T> X, Act<const T> Y, DecayArg dec, const float* __restrict__ carry_in,
-    float* __restrict__ carry_out, float* __restrict__ store, int64_t store_nchunks, int H, int N)
+    float* __restrict__ carry_out, float* __restrict__ store, int64_t store_nseg, int H, int N,
+    int m)
 {
     constexpr int TF = 32, TC = 32;
     constexpr int PAD = Pad<T>::value;
     constexpr int XP = TF + PAD, YP = TC + PAD;
     constexpr int NTC = DV / TC;
     constexpr int VEC = ScanTile<T>::VEC, NV = ScanTile<T>::NV, PR = 32 / VEC;
-    __shared__ __align__(16) T Xs[2][CHUNK * XP];
-    __shared__ __align__(16) T Ys[CHUNK * YP];
+    typedef typename Vec16<T>::type V;
+    __shared__ __align__(16) T Xs[4][2][CHUNK * XP];
+    __shared__ __align__(16) T Ys[4][CHUNK * YP];
+    __shared__ __align__(16) float part[4][16 * 64];   // one 32x32 fp32 tile per wave
+    __shared__ float part_log[4];
 
     const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int f0 = (tile / NTC) * TF, c0 = (tile % NTC) * TC;
-    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
+    const int nseg = (N + m - 1) / m;
 
-    // carry[fb][cb] holds S[f0 + 16fb + 4g + r][c0 + 16cb + t]
+    // carry[fb][cb] holds S[f0 + 16fb + 4g + r][c0 + 16cb + t]; every wave
+    // keeps the same copy
     floatx4 carry[2][2];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
@@ -101,130 +128,271 @@ __global__ __launch_bounds__(64) void state_scan_kernel(
 
     const T* xh = X.head(b, h) + f0;
     const T* yh = Y.head(b, h) + c0;
-    float* sh = store + bh * store_nchunks * (int64_t)(DV * DK);
+    float* sh = store + bh * store_nseg * (int64_t)(DV * DK);
+    T* xs_hi = Xs[w][0];
+    T* xs_lo = Xs[w][1];
+    T* ys = Ys[w];
 
-    // row scale of the X vectors this lane stages, and the chunk decay; for a
-    // per-head (or absent) decay they are the same for every chunk
     const bool const_decay = dec.kind != 2;
     float lm = chunk_log_cumsum(dec, b, h, 0);
     float lamC = __shfl(lm, 63, 64);
-    float xs[NV];
-#pragma unroll
-    for (int p = 0; p < NV; ++p) {
-        const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
-        xs[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
-    }
-
-    typedef typename Vec16<T>::type V;
-    const auto chunk_of = [&](int it) { return REVERSE ? N - 1 - it : it; };
-
-    // one pipeline stage: stage chunk `it` from `cur`, refill `cur` with chunk
-    // it+2, store the carried tile and advance the carry
-    const auto stage = [&](int it, ScanTile<T>& cur) {
-        const int n = chunk_of(it);
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        if (!const_decay) {
-            lm = chunk_log_cumsum(dec, b, h, tok0);
-            lamC = __shfl(lm, 63, 64);
-#pragma unroll
-            for (int p = 0; p < NV; ++p) {
-                const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
-                xs[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
-            }
-        }
+    float xsc[NV];
+    const auto factors = [&]() {
 #pragma unroll
         for (int p = 0; p < NV; ++p) {
-            const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
-            const V xv = __builtin_bit_cast(V, cur.x[p]);
-            V hi, lo;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float v = (float)xv[e] * xs[p];
-                hi[e] = (T)v;
-                lo[e] = (T)(v - (float)hi[e]);
-            }
-            *reinterpret_cast<V*>(&Xs[0][row * XP + col]) = hi;
-            if constexpr (sizeof(T) == 2)
-                *reinterpret_cast<V*>(&Xs[1][row * XP + col]) = lo;
-            *reinterpret_cast<uint4*>(&Ys[row * YP + col]) = cur.y[p];
+            const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
+            xsc[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
         }
-        if (it + 2 < N)
-            scan_load(cur, xh, yh, X.st, Y.st, (int64_t)chunk_of(it + 2) * CHUNK);
-        __syncthreads();
-
-        // store the carried tile, transposed ([c][f], f contiguous), fp32
-        float* sn = sh + (int64_t)n * (DV * DK);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                *reinterpret_cast<float4*>(sn + (int64_t)(c0 + 16 * cb + t) * DK + f0 + 16 * fb + 4 * g) =
-                    float4{carry[fb][cb][0], carry[fb][cb][1], carry[fb][cb][2], carry[fb][cb][3]};
-
-        // delta = X^T Y over the chunk's 64 tokens
-        floatx4 dlt[2][2];
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                dlt[fb][cb] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < CHUNK / 32; ++ks) {
-            Split<T> a[2];
-            Frag<T> bb[2];
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-                a[fb] = frag_cols_split(Xs[0], Xs[1], XP, 16 * fb, 32 * ks);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                bb[cb] = frag_cols(Ys, YP, 16 * cb, 32 * ks);
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    dlt[fb][cb] = mma(a[fb], bb[cb], dlt[fb][cb]);
-        }
-        const float gC = __expf(lamC);
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                carry[fb][cb] = gC * carry[fb][cb] + dlt[fb][cb];
-        __syncthreads();
     };
+    factors();
 
+    // chunk range of the segment with processing index sidx
+    const auto seg_range = [&](int sidx, int& n0, int& n1) {
+        const int s = REVERSE ? nseg - 1 - sidx : sidx;
+        n0 = s * m;
+        n1 = min(n0 + m, N);
+    };
     ScanTile<T> buf0, buf1;
-    scan_load(buf0, xh, yh, X.st, Y.st, (int64_t)chunk_of(0) * CHUNK);
-    if (N > 1)
-        scan_load(buf1, xh, yh, X.st, Y.st, (int64_t)chunk_of(1) * CHUNK);
-    for (int it = 0; it < N; it += 2) {
-        stage(it, buf0);
-        if (it + 1 < N)
-            stage(it + 1, buf1);
+    // the first two chunks of this wave's segment `sidx` (loads run ahead of
+    // the fold barriers)
+    const auto prefetch_segment = [&](int sidx) {
+        if (sidx >= nseg)
+            return;
+        int n0, n1;
+        seg_range(sidx, n0, n1);
+        scan_load(buf0, xh, yh, X.st, Y.st, (int64_t)(REVERSE ? n1 - 1 : n0) * CHUNK);
+        if (n1 - n0 > 1)
+            scan_load(buf1, xh, yh, X.st, Y.st, (int64_t)(REVERSE ? n1 - 2 : n0 + 1) * CHUNK);
+    };
+    prefetch_segment(w);
+
+    for (int r0 = 0; r0 < nseg; r0 += 4) {
+        // ---- wave w folds its segment from zero
+        const int sidx = r0 + w;   // segment index in processing order
+        floatx4 loc[2][2];
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                loc[fb][cb] = zero4();
+        float seg_log = 0.f;
+        if (sidx < nseg) {
+            int n0, n1;
+            seg_range(sidx, n0, n1);
+            const int cnt = n1 - n0;
+            const auto chunk_of = [&](int it) { return REVERSE ? n1 - 1 - it : n0 + it; };
+            const auto step = [&](int it, ScanTile<T>& cur) {
+                const int n = chunk_of(it);
+                const int64_t tok0 = (int64_t)n * CHUNK;
+                if (!const_decay) {
+                    lm = chunk_log_cumsum(dec, b, h, tok0);
+                    lamC = __shfl(lm, 63, 64);
+                    factors();
+                }
+                seg_log += lamC;
+#pragma unroll
+                for (int p = 0; p < NV; ++p) {
+                    const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
+                    const V xv = __builtin_bit_cast(V, cur.x[p]);
+                    V hi, lo;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const float v = (float)xv[e] * xsc[p];
+                        hi[e] = (T)v;
+                        lo[e] = (T)(v - (float)hi[e]);
+                    }
+                    *reinterpret_cast<V*>(&xs_hi[row * XP + col]) = hi;
+                    if constexpr (sizeof(T) == 2)
+                        *reinterpret_cast<V*>(&xs_lo[row * XP + col]) = lo;
+                    *reinterpret_cast<u32x4*>(&ys[row * YP + col]) = cur.y[p];
+                }
+                if (it + 2 < cnt)
+                    scan_load(cur, xh, yh, X.st, Y.st, (int64_t)chunk_of(it + 2) * CHUNK);
+                wave_lds_sync();
+                floatx4 dlt[2][2];
+#pragma unroll
+                for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        dlt[fb][cb] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < CHUNK / 32; ++ks) {
+                    Split<T> a[2];
+                    Frag<T> bb[2];
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+                        a[fb] = frag_cols_split(xs_hi, xs_lo, XP, 16 * fb, 32 * ks);
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        bb[cb] = frag_cols(ys, YP, 16 * cb, 32 * ks);
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb)
+                            dlt[fb][cb] = mma(a[fb], bb[cb], dlt[fb][cb]);
+                }
+                const float gC = __expf(lamC);
+#pragma unroll
+                for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        loc[fb][cb] = gC * loc[fb][cb] + dlt[fb][cb];
+                wave_lds_sync();
+            };
+            for (int it = 0; it < cnt; it += 2) {
+                step(it, buf0);
+                if (it + 1 < cnt)
+                    step(it + 1, buf1);
+            }
+        }
+        prefetch_segment(sidx + 4);
+        // ---- publish the partial folds, then fold them into the carry in order
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                *reinterpret_cast<floatx4*>(&part[w][(2 * fb + cb) * 256 + 4 * l]) = loc[fb][cb];
+        if (l == 0)
+            part_log[w] = seg_log;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int su = r0 + u;
+            if (su < nseg) {
+                const int s = REVERSE ? nseg - 1 - su : su;
+                if (u == w) {
+                    // state entering segment s (forward) / gradient leaving it (reverse)
+                    float* sn = sh + (int64_t)s * (DV * DK);
+#pragma unroll
+                    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb)
+                            *reinterpret_cast<float4*>(sn + (int64_t)(c0 + 16 * cb + t) * DK + f0 +
+                                                       16 * fb + 4 * g) =
+                                float4{carry[fb][cb][0], carry[fb][cb][1], carry[fb][cb][2],
+                                       carry[fb][cb][3]};
+                }
+                const float gS = __expf(part_log[u]);
+#pragma unroll
+                for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        carry[fb][cb] = gS * carry[fb][cb] +
+                            *reinterpret_cast<const floatx4*>(&part[u][(2 * fb + cb) * 256 + 4 * l]);
+            }
+        }
+        __syncthreads();
     }
 
+    if (w == 0) {
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
+        for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                carry_out[(bh * DK + f0 + 16 * fb + 4 * g + r) * DV + c0 + 16 * cb + t] =
-                    carry[fb][cb][r];
+                for (int r = 0; r < 4; ++r)
+                    carry_out[(bh * DK + f0 + 16 * fb + 4 * g + r) * DV + c0 + 16 * cb + t] =
+                        carry[fb][cb][r];
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Forward intra-chunk kernel.  One workgroup (4 waves) per (b, h, chunk).
-// Wave w builds row block w of P = (Q K^T) .* D (split hi + lo) into LDS;
-// then wave w owns output columns [w d_v/4, (w+1) d_v/4) of all 64 rows:
-//   O = P V + gamma .* (Q S_{n-1})
-// with the row scale gamma_i applied to the fp32 product.
+// Shared pieces of the segment kernels.
+// ---------------------------------------------------------------------------
+
+// Per-lane decay factors of a chunk for the k-slots of a frag_cols() read
+// over tokens (slot r of k32 step ks is token 32ks + 8g + r):
+// gamma_C / gamma_j when `towards_end`, else gamma_j.
+__device__ __forceinline__ void slot_factors(const float* lam, float lamC, bool towards_end,
+                                             float (&f)[2][8])
+{
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float lj = lam[32 * ks + 8 * g + r];
+            f[ks][r] = towards_end ? __expf(lamC - lj) : __expf(lj);
+        }
+}
+
+// carry[fb][cbl] (rows f = 16fb + 4g + r, column cbase0 + 16cbl + t) <-
+// gamma_C carry + X^T (Y .* yf) over the chunk: X (rows = tokens, d_k wide)
+// exact, Y (rows = tokens) scaled per token by yf and split.  The per-token
+// factor sits on the wave's own columns of Y, so each wave scales and splits
+// only the quarter of the chunk it multiplies.
+template <typename T, int DK, int NCB>
+__device__ __forceinline__ void state_update(floatx4 (&carry)[DK / 16][NCB], const T* Xs, int xp,
+                                             const T* Ys, int yp, int cbase0, float gC,
+                                             const float (&yf)[2][8])
+{
+#pragma unroll
+    for (int fb = 0; fb < DK / 16; ++fb)
+#pragma unroll
+        for (int cbl = 0; cbl < NCB; ++cbl)
+            carry[fb][cbl] *= gC;
+#pragma unroll
+    for (int ks = 0; ks < CHUNK / 32; ++ks) {
+        Split<T> y[NCB];
+#pragma unroll
+        for (int cbl = 0; cbl < NCB; ++cbl)
+            y[cbl] = split_scaled<T>(frag_cols(Ys, yp, cbase0 + 16 * cbl, 32 * ks), yf[ks]);
+#pragma unroll
+        for (int fb = 0; fb < DK / 16; ++fb) {
+            const Frag<T> a = frag_cols(Xs, xp, 16 * fb, 32 * ks);
+#pragma unroll
+            for (int cbl = 0; cbl < NCB; ++cbl)
+                carry[fb][cbl] = mma(a, y[cbl], carry[fb][cbl]);
+        }
+    }
+}
+
+// Load a wave's columns of a stored [d_v][d_k] fp32 state into register tiles.
+template <int DK, int NCB>
+__device__ __forceinline__ void load_state(floatx4 (&st)[DK / 16][NCB], const float* src, int cbase0)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+#pragma unroll
+    for (int fb = 0; fb < DK / 16; ++fb)
+#pragma unroll
+        for (int cbl = 0; cbl < NCB; ++cbl) {
+            const float4 v = *reinterpret_cast<const float4*>(
+                src + (int64_t)(cbase0 + 16 * cbl + t) * DK + 16 * fb + 4 * g);
+            st[fb][cbl] = floatx4{v.x, v.y, v.z, v.w};
+        }
+}
+
+// Write a wave's register tiles of a state into an LDS plane pair laid out
+// [c][f] (hi, lo).
+template <typename T, int DK, int NCB>
+__device__ __forceinline__ void put_state(T* hi, T* lo, int pitch, const floatx4 (&st)[DK / 16][NCB],
+                                          int cbase0)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+#pragma unroll
+    for (int fb = 0; fb < DK / 16; ++fb)
+#pragma unroll
+        for (int cbl = 0; cbl < NCB; ++cbl)
+            put_split4(hi, lo, (cbase0 + 16 * cbl + t) * pitch + 16 * fb + 4 * g, st[fb][cbl]);
+}
+
+// ---------------------------------------------------------------------------
+// Forward segment kernel.  Workgroup = (b, h, segment), one wave per 16
+// columns of d_v (8 waves at d_v = 128).  Wave w owns output and state
+// columns [16w, 16w + 16) and carries its state columns across the
+// segment's chunks in registers.  Per chunk the waves build P = (Q K^T) .* D
+// (split) in LDS, then wave w computes
+//   O[:, cols] = gamma .* (Q S_{n-1}[:, cols]) + P V[:, cols],
+//   S_n[:, cols] = gamma_C S_{n-1}[:, cols] + K^T (V[:, cols] .* gamma_C/gamma).
+// The state serves as the B operand straight from registers (k-slot order
+// of frag_rows_perm).  The next chunk's rows load while this one computes.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV>
-__global__ __launch_bounds__(256) void fwd_intra_kernel(
+__global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, DecayArg dec,
-    const float* __restrict__ states, int64_t st_nchunks, Act<OT> O, int H)
+    const float* __restrict__ bstates, int64_t bs_nseg, Act<OT> O, int H, int N, int m)
 {
+    constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, VP = DV + PAD, PP = CHUNK + PAD;
     __shared__ __align__(16) T Qs[CHUNK * QP];
@@ -233,214 +401,317 @@ __global__ __launch_bounds__(256) void fwd_intra_kernel(
     __shared__ __align__(16) T Ps[2][CHUNK * PP];
     __shared__ float lam[CHUNK];
 
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
-    const int64_t tok0 = (int64_t)n * CHUNK;
+    const int64_t bh = (int64_t)b * H + h;
+    const int cbase = 16 * w;
+    const int n0 = s * m, n1 = min(n0 + m, N);
 
-    stage_rows<T, CHUNK, DK, 256>(Qs, QP, Q.head(b, h) + tok0 * Q.st, Q.st);
-    stage_rows<T, CHUNK, DK, 256>(Ks, QP, K.head(b, h) + tok0 * K.st, K.st);
-    stage_rows<T, CHUNK, DV, 256>(Vs, VP, V.head(b, h) + tok0 * V.st, V.st);
-    if (w == 0)
-        lam[l] = chunk_log_cumsum(dec, b, h, tok0);
-    __syncthreads();
+    floatx4 S[DK / 16][1];
+    load_state<DK, 1>(S, bstates + (bh * bs_nseg + s) * (int64_t)(DV * DK), cbase);
 
-    // P row block w: P[i][j] = (q_i . k_j) exp(lam_i - lam_j) for j <= i
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        floatx4 acc = zero4();
-        if (jb <= w) {
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(frag_rows(Qs, QP, 16 * w, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
+    const T* qh = Q.head(b, h);
+    const T* kh = K.head(b, h);
+    const T* vh = V.head(b, h);
+    ChunkRegs<T, DK, NT> rq, rk;
+    ChunkRegs<T, DV, NT> rv;
+    chunk_load(rq, qh + (int64_t)n0 * CHUNK * Q.st, Q.st);
+    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
+    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
+    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
+
+    // P tiles of this wave: row block ib, column blocks jb0, jb0 + jstep, ...
+    const int ib_p = w % 4;
+    const int jb0 = NW == 8 ? w / 4 : 0, jstep = NW == 8 ? 2 : 1;
+
+    for (int n = n0; n < n1; ++n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        chunk_store(rq, Qs, QP);
+        chunk_store(rk, Ks, QP);
+        chunk_store(rv, Vs, VP);
+        if (w == 0)
+            lam[l] = decay_log_cumsum(dec, ra);
+        __syncthreads();
+        if (n + 1 < n1) {
+            const int64_t tn = (int64_t)(n + 1) * CHUNK;
+            chunk_load(rq, qh + tn * Q.st, Q.st);
+            chunk_load(rk, kh + tn * K.st, K.st);
+            chunk_load(rv, vh + tn * V.st, V.st);
+            ra = decay_raw(dec, b, h, tn);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * g + r, j = 16 * jb + t;
-            const float val = (j <= i) ? acc[r] * __expf(lam[i] - lam[j]) : 0.f;
-            put_split(Ps[0], Ps[1], i * PP + j, val);
-        }
-    }
-    __syncthreads();
+        const float lamC = lam[CHUNK - 1];
 
-    constexpr int CPW = DV / 4;
-    const float* St = states + ((int64_t)(b * H + h) * st_nchunks + n) * (int64_t)(DV * DK);
-    OT* oh = O.head(b, h) + tok0 * O.st;
 #pragma unroll
-    for (int cbl = 0; cbl < CPW / 16; ++cbl) {
-        const int cbase = w * CPW + 16 * cbl;
-        Split<T> sf[DK / 32];      // B = S[f][c], k = f
+        for (int jb = jb0; jb < 4; jb += jstep) {
+            floatx4 acc = zero4();
+            if (jb <= ib_p) {
 #pragma unroll
-        for (int fs = 0; fs < DK / 32; ++fs)
-            sf[fs] = gfrag_rows_split<T>(St, DK, cbase, 32 * fs);
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    acc = mma(frag_rows(Qs, QP, 16 * ib_p, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * ib_p + 4 * g + r, j = 16 * jb + t;
+                const float val = (j <= i) ? acc[r] * __expf(lam[i] - lam[j]) : 0.f;
+                put_split(Ps[0], Ps[1], i * PP + j, val);
+            }
+        }
+        // S_{n-1} as split B fragments (k = f in frag_rows_perm order)
+        Split<T> sf[DK / 32];
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+            sf[ks] = split_tiles<T>(S[2 * ks][0], S[2 * ks + 1][0]);
+        __syncthreads();
+
+        OT* oh = O.head(b, h) + tok0 * O.st;
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
-            floatx4 intra = zero4(), inter = zero4();
+            floatx4 acc = zero4();
 #pragma unroll
-            for (int js = 0; js <= ib / 2; ++js)
-                intra = mma(frag_rows_split(Ps[0], Ps[1], PP, 16 * ib, 32 * js),
-                            frag_cols(Vs, VP, cbase, 32 * js), intra);
-#pragma unroll
-            for (int fs = 0; fs < DK / 32; ++fs)
-                inter = mma(frag_rows(Qs, QP, 16 * ib, 32 * fs), sf[fs], inter);
-            floatx4 out;
+            for (int ks = 0; ks < DK / 32; ++ks)
+                acc = mma(frag_rows_perm(Qs, QP, 16 * ib, 32 * ks), sf[ks], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                out[r] = intra[r] + __expf(lam[16 * ib + 4 * g + r]) * inter[r];
-            store_tile<OT>(oh, O.st, 16 * ib, cbase, out);
+                acc[r] *= __expf(lam[16 * ib + 4 * g + r]);
+#pragma unroll
+            for (int js = 0; js <= ib / 2; ++js)
+                acc = mma(frag_rows_split(Ps[0], Ps[1], PP, 16 * ib, 32 * js),
+                          frag_cols(Vs, VP, cbase, 32 * js), acc);
+            store_tile<OT>(oh, O.st, 16 * ib, cbase, acc);
         }
+
+        // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma)
+        float vf[2][8];
+        slot_factors(lam, lamC, true, vf);
+        state_update<T, DK, 1>(S, Ks, QP, Vs, VP, cbase, __expf(lamC), vf);
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Backward per-chunk kernel.  One workgroup (4 waves) per (b, h, chunk).
-// Builds P = (Q K^T) .* D and A = (dO V^T) .* D in LDS (split hi + lo; wave
-// w: row block w), then each wave owns a quarter of the columns of dQ, dK
-// and dV.  The stored fp32 S_{n-1} and G_n are read as split fragments from
-// global memory; decay factors scale the fp32 products' rows.
+// Backward segment kernel.  Workgroup = (b, h, segment), one wave per 16
+// columns of d_v (8 waves at d_v = 128).  Wave w owns state/gradient columns
+// [16w, 16w + 16), row block rb = w % 4 of the outputs and, with 8 waves,
+// half w / 4 of their columns.
+//   Walk 1 (chunks in order, S carried from the stored segment state):
+//   S_{n-1} goes to LDS (split) and
+//       dQ = gamma .* (dO S_{n-1}^T) + A K,   A = (dO V^T) .* D  (rows rb),
+//   then S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma).
+//   Walk 2 (chunks in reverse, G carried from the stored segment gradient):
+//   G_n goes to LDS (split) and, for rows rb,
+//       dV = gamma_C/gamma .* (K G_n) + P^T dO,   P = (Q K^T) .* D,
+//       dK = gamma_C/gamma .* (V G_n^T) + A^T Q,
+//   then G_{n-1} = gamma_C G_n + Q^T (dO .* gamma).
+// P and A are built per wave in registers in the orientation their product
+// needs and used as split A operands directly (k-slot order of the
+// frag_cols_perm reads of the other operand).  The next chunk's rows load
+// while this one computes; walk 2 starts on walk 1's last chunk, whose K, V,
+// dO and decays are still in LDS, so only Q is loaded for it.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_intra_kernel(
+__global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, Act<const T> dO, DecayArg dec,
-    const float* __restrict__ states, int64_t st_nchunks, const float* __restrict__ ghat,
-    int64_t g_nchunks, Act<OT> dQ, Act<OT> dK, Act<OT> dV, int H)
+    const float* __restrict__ bstates, int64_t bs_nseg, const float* __restrict__ gstates,
+    int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, int H, int N, int m)
 {
+    constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
-    constexpr int QP = DK + PAD, VP = DV + PAD, PP = CHUNK + PAD;
+    constexpr int QP = DK + PAD, VP = DV + PAD;
+    constexpr int FBW = (DK / 16) / NH, CBW = (DV / 16) / NH;   // output blocks per wave
     __shared__ __align__(16) T Qs[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T dOs[CHUNK * VP];
-    __shared__ __align__(16) T Ps[2][CHUNK * PP];
-    __shared__ __align__(16) T As[2][CHUNK * PP];
+    __shared__ __align__(16) T Ms[2][DV * QP];     // state / gradient, [c][f], split
     __shared__ float lam[CHUNK];
 
-    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
-    const int64_t tok0 = (int64_t)n * CHUNK;
     const int64_t bh = (int64_t)b * H + h;
+    const int cbase = 16 * w;
+    const int rb = w % 4, fb0 = (w / 4) * FBW, cb0 = (w / 4) * CBW;
+    const int n0 = s * m, n1 = min(n0 + m, N);
 
-    stage_rows<T, CHUNK, DK, 256>(Qs, QP, Q.head(b, h) + tok0 * Q.st, Q.st);
-    stage_rows<T, CHUNK, DK, 256>(Ks, QP, K.head(b, h) + tok0 * K.st, K.st);
-    stage_rows<T, CHUNK, DV, 256>(Vs, VP, V.head(b, h) + tok0 * V.st, V.st);
-    stage_rows<T, CHUNK, DV, 256>(dOs, VP, dO.head(b, h) + tok0 * dO.st, dO.st);
-    if (w == 0)
-        lam[l] = chunk_log_cumsum(dec, b, h, tok0);
-    __syncthreads();
-    const float lamC = lam[CHUNK - 1];
-    const float* St = states + (bh * st_nchunks + n) * (int64_t)(DV * DK);   // S_{n-1}^T
-    const float* Gt = ghat + (bh * g_nchunks + n) * (int64_t)(DV * DK);      // G_n^T
+    floatx4 C[DK / 16][1];   // carried state (walk 1) / gradient (walk 2)
 
-    // P and A, row block w
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        floatx4 accp = zero4(), acca = zero4();
-        if (jb <= w) {
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                accp = mma(frag_rows(Qs, QP, 16 * w, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), accp);
-#pragma unroll
-            for (int ks = 0; ks < DV / 32; ++ks)
-                acca = mma(frag_rows(dOs, VP, 16 * w, 32 * ks), frag_rows(Vs, VP, 16 * jb, 32 * ks), acca);
+    const T* qh = Q.head(b, h);
+    const T* kh = K.head(b, h);
+    const T* vh = V.head(b, h);
+    const T* doh = dO.head(b, h);
+    ChunkRegs<T, DK, NT> rq, rk;
+    ChunkRegs<T, DV, NT> rv, rdo;
+
+    // ---------------- walk 1: dQ
+    load_state<DK, 1>(C, bstates + (bh * bs_nseg + s) * (int64_t)(DV * DK), cbase);
+    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
+    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
+    chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st);
+    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
+    for (int n = n0; n < n1; ++n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        chunk_store(rk, Ks, QP);
+        chunk_store(rv, Vs, VP);
+        chunk_store(rdo, dOs, VP);
+        if (w == 0)
+            lam[l] = decay_log_cumsum(dec, ra);
+        put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
+        __syncthreads();
+        if (n + 1 < n1) {
+            const int64_t tn = (int64_t)(n + 1) * CHUNK;
+            chunk_load(rk, kh + tn * K.st, K.st);
+            chunk_load(rv, vh + tn * V.st, V.st);
+            chunk_load(rdo, doh + tn * dO.st, dO.st);
+            ra = decay_raw(dec, b, h, tn);
+        } else {
+            chunk_load(rq, qh + tok0 * Q.st, Q.st);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * g + r, j = 16 * jb + t;
-            const float d = (j <= i) ? __expf(lam[i] - lam[j]) : 0.f;
-            put_split(Ps[0], Ps[1], i * PP + j, accp[r] * d);
-            put_split(As[0], As[1], i * PP + j, acca[r] * d);
-        }
-    }
-    __syncthreads();
+        const float lamC = lam[CHUNK - 1];
 
-    // dQ = A K + gamma .* (dO S_{n-1}^T) ; wave w owns d_k columns [w DK/4, (w+1) DK/4)
-    {
+        // A^T tiles of row block rb: T[j][i] = (v_j . dO_i) D_ij, j-block jb
+        floatx4 at[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            at[jb] = zero4();
+            if (jb <= rb) {
+#pragma unroll
+                for (int cs = 0; cs < DV / 32; ++cs)
+                    at[jb] = mma(frag_rows(Vs, VP, 16 * jb, 32 * cs), frag_rows(dOs, VP, 16 * rb, 32 * cs), at[jb]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * jb + 4 * g + r, i = 16 * rb + t;
+                    at[jb][r] = (j <= i) ? at[jb][r] * __expf(lam[i] - lam[j]) : 0.f;
+                }
+            }
+        }
+        const Split<T> a0 = split_tiles<T>(at[0], at[1]);
+        const Split<T> a1 = split_tiles<T>(at[2], at[3]);
+        float rowg[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            rowg[r] = __expf(lam[16 * rb + 4 * g + r]);
+
         OT* out = dQ.head(b, h) + tok0 * dQ.st;
 #pragma unroll
-        for (int fbl = 0; fbl < DK / 64; ++fbl) {
-            const int fbase = w * (DK / 4) + 16 * fbl;
-            Split<T> sf[DV / 32];  // B = S^T[c][f], k = c
+        for (int fbi = 0; fbi < FBW; ++fbi) {
+            const int fb = fb0 + fbi;
+            floatx4 acc = zero4();
 #pragma unroll
             for (int cs = 0; cs < DV / 32; ++cs)
-                sf[cs] = gfrag_cols_split<T>(St, DK, fbase, 32 * cs);
+                acc = mma(frag_rows(dOs, VP, 16 * rb, 32 * cs),
+                          frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs), acc);
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                floatx4 intra = zero4(), inter = zero4();
-#pragma unroll
-                for (int js = 0; js <= ib / 2; ++js)
-                    intra = mma(frag_rows_split(As[0], As[1], PP, 16 * ib, 32 * js),
-                                frag_cols(Ks, QP, fbase, 32 * js), intra);
-#pragma unroll
-                for (int cs = 0; cs < DV / 32; ++cs)
-                    inter = mma(frag_rows(dOs, VP, 16 * ib, 32 * cs), sf[cs], inter);
-                floatx4 res;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    res[r] = intra[r] + __expf(lam[16 * ib + 4 * g + r]) * inter[r];
-                store_tile<OT>(out, dQ.st, 16 * ib, fbase, res);
-            }
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= rowg[r];
+            acc = mma(a0, frag_cols_perm(Ks, QP, 16 * fb, 0), acc);
+            if (rb >= 2)
+                acc = mma(a1, frag_cols_perm(Ks, QP, 16 * fb, 32), acc);
+            store_tile<OT>(out, dQ.st, 16 * rb, 16 * fb, acc);
         }
+
+        float vf[2][8];
+        slot_factors(lam, lamC, true, vf);
+        state_update<T, DK, 1>(C, Ks, QP, Vs, VP, cbase, __expf(lamC), vf);
+        __syncthreads();
     }
 
-    // dK = A^T Q + (gamma_C / gamma) .* (V G_n^T) ; wave w owns d_k columns
-    {
-        OT* out = dK.head(b, h) + tok0 * dK.st;
+    // ---------------- walk 2: dK, dV
+    load_state<DK, 1>(C, gstates + (bh * gs_nseg + s) * (int64_t)(DV * DK), cbase);
+    for (int n = n1 - 1; n >= n0; --n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        chunk_store(rq, Qs, QP);
+        if (n < n1 - 1) {
+            chunk_store(rk, Ks, QP);
+            chunk_store(rv, Vs, VP);
+            chunk_store(rdo, dOs, VP);
+            if (w == 0)
+                lam[l] = decay_log_cumsum(dec, ra);
+        }
+        put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
+        __syncthreads();
+        if (n > n0) {
+            const int64_t tn = (int64_t)(n - 1) * CHUNK;
+            chunk_load(rq, qh + tn * Q.st, Q.st);
+            chunk_load(rk, kh + tn * K.st, K.st);
+            chunk_load(rv, vh + tn * V.st, V.st);
+            chunk_load(rdo, doh + tn * dO.st, dO.st);
+            ra = decay_raw(dec, b, h, tn);
+        }
+        const float lamC = lam[CHUNK - 1];
+
+        // P and A tiles of column block rb: rows i (i-block ib), column j = 16rb + t
+        floatx4 pt[4], atl[4];
 #pragma unroll
-        for (int fbl = 0; fbl < DK / 64; ++fbl) {
-            const int fbase = w * (DK / 4) + 16 * fbl;
-            Split<T> gf[DV / 32];  // B = G^T[c][f], k = c
+        for (int ib = 0; ib < 4; ++ib) {
+            pt[ib] = zero4();
+            atl[ib] = zero4();
+            if (ib >= rb) {
 #pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs)
-                gf[cs] = gfrag_cols_split<T>(Gt, DK, fbase, 32 * cs);
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                floatx4 intra = zero4(), inter = zero4();
-#pragma unroll
-                for (int is = jb / 2; is < 2; ++is)
-                    intra = mma(frag_cols_split(As[0], As[1], PP, 16 * jb, 32 * is),
-                                frag_cols(Qs, QP, fbase, 32 * is), intra);
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    pt[ib] = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * rb, 32 * ks), pt[ib]);
 #pragma unroll
                 for (int cs = 0; cs < DV / 32; ++cs)
-                    inter = mma(frag_rows(Vs, VP, 16 * jb, 32 * cs), gf[cs], inter);
-                floatx4 res;
+                    atl[ib] = mma(frag_rows(dOs, VP, 16 * ib, 32 * cs), frag_rows(Vs, VP, 16 * rb, 32 * cs), atl[ib]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    res[r] = intra[r] + __expf(lamC - lam[16 * jb + 4 * g + r]) * inter[r];
-                store_tile<OT>(out, dK.st, 16 * jb, fbase, res);
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * ib + 4 * g + r, j = 16 * rb + t;
+                    const float d = (i >= j) ? __expf(lam[i] - lam[j]) : 0.f;
+                    pt[ib][r] *= d;
+                    atl[ib][r] *= d;
+                }
             }
         }
-    }
-    // dV = P^T dO + (gamma_C / gamma) .* (K G_n) ; wave w owns d_v columns
-    {
-        OT* out = dV.head(b, h) + tok0 * dV.st;
+        const Split<T> p0 = split_tiles<T>(pt[0], pt[1]), p1 = split_tiles<T>(pt[2], pt[3]);
+        const Split<T> q0 = split_tiles<T>(atl[0], atl[1]), q1 = split_tiles<T>(atl[2], atl[3]);
+        float rowf[4];
 #pragma unroll
-        for (int cbl = 0; cbl < DV / 64; ++cbl) {
-            const int cbase = w * (DV / 4) + 16 * cbl;
-            Split<T> gf[DK / 32];  // B = G[f][c], k = f
+        for (int r = 0; r < 4; ++r)
+            rowf[r] = __expf(lamC - lam[16 * rb + 4 * g + r]);
+
+        OT* outv = dV.head(b, h) + tok0 * dV.st;
+#pragma unroll
+        for (int cbi = 0; cbi < CBW; ++cbi) {
+            const int cb = cb0 + cbi;
+            floatx4 acc = zero4();
 #pragma unroll
             for (int fs = 0; fs < DK / 32; ++fs)
-                gf[fs] = gfrag_rows_split<T>(Gt, DK, cbase, 32 * fs);
+                acc = mma(frag_rows(Ks, QP, 16 * rb, 32 * fs),
+                          frag_rows_split(Ms[0], Ms[1], QP, 16 * cb, 32 * fs), acc);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                floatx4 intra = zero4(), inter = zero4();
-#pragma unroll
-                for (int is = jb / 2; is < 2; ++is)
-                    intra = mma(frag_cols_split(Ps[0], Ps[1], PP, 16 * jb, 32 * is),
-                                frag_cols(dOs, VP, cbase, 32 * is), intra);
-#pragma unroll
-                for (int fs = 0; fs < DK / 32; ++fs)
-                    inter = mma(frag_rows(Ks, QP, 16 * jb, 32 * fs), gf[fs], inter);
-                floatx4 res;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    res[r] = intra[r] + __expf(lamC - lam[16 * jb + 4 * g + r]) * inter[r];
-                store_tile<OT>(out, dV.st, 16 * jb, cbase, res);
-            }
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= rowf[r];
+            if (rb < 2)
+                acc = mma(p0, frag_cols_perm(dOs, VP, 16 * cb, 0), acc);
+            acc = mma(p1, frag_cols_perm(dOs, VP, 16 * cb, 32), acc);
+            store_tile<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
         }
+        OT* outk = dK.head(b, h) + tok0 * dK.st;
+#pragma unroll
+        for (int fbi = 0; fbi < FBW; ++fbi) {
+            const int fb = fb0 + fbi;
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int cs = 0; cs < DV / 32; ++cs)
+                acc = mma(frag_rows(Vs, VP, 16 * rb, 32 * cs),
+                          frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= rowf[r];
+            if (rb < 2)
+                acc = mma(q0, frag_cols_perm(Qs, QP, 16 * fb, 0), acc);
+            acc = mma(q1, frag_cols_perm(Qs, QP, 16 * fb, 32), acc);
+            store_tile<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+        }
+
+        // G_{n-1} = gamma_C G_n + Q^T (dO .* gamma)
+        float of[2][8];
+        slot_factors(lam, lamC, false, of);
+        state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, __expf(lamC), of);
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers: dispatch (dtype, d_k, d_v) to a template instance.
+// Host-side launchers: dispatch (dtype, out dtype, d_k, d_v) to an instance.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -457,37 +728,37 @@ DecayArg decay_arg(const TensorArg& d, int kind)
 template <typename T, typename OT, int DK, int DV>
 hipError_t scan_impl(const ScanLaunch& s, hipStream_t stream)
 {
-    const dim3 grid((DK / 32) * (DV / 32), s.H, s.B), block(64);
+    const dim3 grid((DK / 32) * (DV / 32), s.H, s.B), block(256);
     if (s.reverse)
-        hipLaunchKernelGGL((state_scan_kernel<T, DK, DV, true>), grid, block, 0, stream,
+        hipLaunchKernelGGL((seg_scan_kernel<T, DK, DV, true>), grid, block, 0, stream,
                            cact<T>(s.x), cact<T>(s.y), decay_arg(s.decay, s.decay_kind),
-                           s.carry_in, s.carry_out, (float*)s.store, s.store_nchunks, s.H, s.N);
+                           s.carry_in, s.carry_out, (float*)s.store, s.store_nseg, s.H, s.N, s.m);
     else
-        hipLaunchKernelGGL((state_scan_kernel<T, DK, DV, false>), grid, block, 0, stream,
+        hipLaunchKernelGGL((seg_scan_kernel<T, DK, DV, false>), grid, block, 0, stream,
                            cact<T>(s.x), cact<T>(s.y), decay_arg(s.decay, s.decay_kind),
-                           s.carry_in, s.carry_out, (float*)s.store, s.store_nchunks, s.H, s.N);
+                           s.carry_in, s.carry_out, (float*)s.store, s.store_nseg, s.H, s.N, s.m);
     return hipGetLastError();
 }
 
 template <typename T, typename OT, int DK, int DV>
-hipError_t fwd_intra_impl(const FwdIntraLaunch& s, hipStream_t stream)
+hipError_t fwd_seg_impl(const FwdIntraLaunch& s, hipStream_t stream)
 {
-    const dim3 grid(s.N, s.H, s.B), block(256);
-    hipLaunchKernelGGL((fwd_intra_kernel<T, OT, DK, DV>), grid, block, 0, stream,
+    const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
+    hipLaunchKernelGGL((fwd_seg_kernel<T, OT, DK, DV>), grid, block, 0, stream,
                        cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), decay_arg(s.decay, s.decay_kind),
-                       (const float*)s.states, s.st_nchunks, mact<OT>(s.o), s.H);
+                       (const float*)s.states, s.st_nseg, mact<OT>(s.o), s.H, s.N, s.m);
     return hipGetLastError();
 }
 
 template <typename T, typename OT, int DK, int DV>
-hipError_t bwd_intra_impl(const BwdIntraLaunch& s, hipStream_t stream)
+hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
 {
-    const dim3 grid(s.N, s.H, s.B), block(256);
-    hipLaunchKernelGGL((bwd_intra_kernel<T, OT, DK, DV>), grid, block, 0, stream,
+    const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
+    hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV>), grid, block, 0, stream,
                        cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                       decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nchunks,
-                       (const float*)s.ghat, s.g_nchunks, mact<OT>(s.dq), mact<OT>(s.dk_),
-                       mact<OT>(s.dv_), s.H);
+                       decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                       (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                       mact<OT>(s.dv_), s.H, s.N, s.m);
     return hipGetLastError();
 }
 
@@ -523,12 +794,12 @@ hipError_t launch_state_scan(const ScanLaunch& s, hipStream_t stream)
 
 hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream)
 {
-    LINREC_DISPATCH(fwd_intra_impl, s, stream);
+    LINREC_DISPATCH(fwd_seg_impl, s, stream);
 }
 
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream)
 {
-    LINREC_DISPATCH(bwd_intra_impl, s, stream);
+    LINREC_DISPATCH(bwd_seg_impl, s, stream);
 }
 
 }  // namespace linrec

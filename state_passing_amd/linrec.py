@@ -34,7 +34,7 @@ STATUS = {
 
 # Every function include/linrec.h declares.
 EXPORTS = (
-    "linrec_ctx_create", "linrec_ctx_destroy", "linrec_states_bytes",
+    "linrec_ctx_create", "linrec_ctx_destroy", "linrec_states_bytes", "linrec_seq_states_bytes",
     "linrec_bwd_workspace_bytes", "linrec_fwd", "linrec_bwd", "linrec_fwd_seq",
     "linrec_bwd_seq_workspace_bytes", "linrec_bwd_seq", "linrec_status_str",
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
@@ -83,6 +83,7 @@ def _lib():
         "linrec_states_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_seq_workspace_bytes": ([D, I32, P], ctypes.c_size_t),
+        "linrec_seq_states_bytes": ([D, I32, P], ctypes.c_size_t),
         "linrec_fwd": ([P, D, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
@@ -203,6 +204,11 @@ def bwd_workspace_bytes(d: Desc) -> int:
     return int(_lib().linrec_bwd_workspace_bytes(ctypes.byref(d)))
 
 
+def seq_states_bytes(d: Desc, lengths: Sequence[int]) -> int:
+    arr = (ctypes.c_int32 * len(lengths))(*lengths)
+    return int(_lib().linrec_seq_states_bytes(ctypes.byref(d), len(lengths), arr))
+
+
 def bwd_seq_workspace_bytes(d: Desc, lengths: Sequence[int]) -> int:
     arr = (ctypes.c_int32 * len(lengths))(*lengths)
     return int(_lib().linrec_bwd_seq_workspace_bytes(ctypes.byref(d), len(lengths), arr))
@@ -279,7 +285,8 @@ def fwd_seq(q, k, v, decay, lengths: Sequence[int], S_in=None, *, o=None, S_out=
     o = torch.empty(B, H, T, dv, dtype=odt, device=q.device) if o is None else o
     S_out = _state_out(q, B, H, dk, dv, S_out)
     if states is None:
-        states = torch.empty(max(states_bytes(d), 16), dtype=torch.uint8, device=q.device)
+        states = torch.empty(max(seq_states_bytes(d, lengths), 16), dtype=torch.uint8,
+                             device=q.device)
     arr = (ctypes.c_int32 * len(lengths))(*lengths)
     rc = _lib().linrec_fwd_seq(context(q.device.index), ctypes.byref(d), len(lengths), arr,
                                _act(q), _act(k), _act(v), dec, _ptr(S_in), _act(o),

@@ -19,14 +19,15 @@
  *
  * Inside a piece the work is done chunkwise with C = 64 tokens per chunk,
  * chunks grouped into segments of 4:
- *   - a state-transition kernel (the segment scan) carries S across the
- *     piece in fp32 and stores the state entering every segment ("states");
+ *   - the state transition (a parallel segment-sum kernel and a serial fold
+ *     kernel) carries S across the piece in fp32 and stores the state
+ *     entering every segment ("states");
  *   - a segment kernel walks each segment's chunks with the state in
  *     registers and computes, per chunk,
  *         O_n = [(Q_n K_n^T) .* D_n] V_n + (Q_n .* gamma) S_{n-1}
  *     where gamma_i is the chunk-local cumulative decay of token i and
  *     D_ij = gamma_i / gamma_j for j <= i (0 above the diagonal).
- *   The backward mirrors this: a reverse segment scan carries dS from
+ *   The backward mirrors this: the reverse transition carries dS from
  *   dS_out back to dS_in and stores the gradient leaving every segment; a
  *   segment kernel rebuilds the per-chunk states and gradients from the
  *   stored ones and computes dQ, dK, dV.
@@ -133,14 +134,15 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device);
 linrec_status linrec_ctx_destroy(linrec_ctx* ctx);
 
 /* Bytes of the state store of one piece described by `d` (0 if `d` is
- * invalid): B*H*ceil(T/256)*d_k*d_v fp32 values, the state entering every
- * segment of 4 chunks, written by linrec_fwd and read by linrec_bwd.  It
- * depends on the piece length only (constant in the number of pieces
- * already processed). */
+ * invalid): B*H*ceil(T/256) records of d_k*d_v + 64 fp32 values, the state
+ * entering every segment of 4 chunks (row-major [d_k][d_v], as S_in) and the
+ * segment's log-decay, written by
+ * linrec_fwd and read by linrec_bwd.  It depends on the piece length only
+ * (constant in the number of pieces already processed). */
 size_t linrec_states_bytes(const linrec_desc* d);
 
 /* Bytes of backward workspace for `d` (0 if `d` is invalid): the gradient
- * leaving every segment, B*H*ceil(T/256)*d_k*d_v fp32 values. */
+ * leaving every segment, B*H*ceil(T/256) records as above. */
 size_t linrec_bwd_workspace_bytes(const linrec_desc* d);
 
 /* Bytes of the state store linrec_fwd_seq / linrec_bwd_seq need for these
@@ -212,11 +214,13 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
 
 /* Kernel kinds for linrec_ctx_kernel_times(). */
 enum {
-    LINREC_KERNEL_FWD_SCAN = 0,   /* forward state transition (S carried)      */
-    LINREC_KERNEL_FWD_INTRA = 1,  /* forward intra-chunk output                */
-    LINREC_KERNEL_BWD_SCAN = 2,   /* reverse state transition (dS carried)     */
-    LINREC_KERNEL_BWD_INTRA = 3,  /* backward per-chunk dQ, dK, dV             */
-    LINREC_KERNEL_KINDS = 4
+    LINREC_KERNEL_FWD_SUM = 0,    /* forward segment sums (parallel)           */
+    LINREC_KERNEL_FWD_FOLD = 1,   /* forward fold across segments (S carried)  */
+    LINREC_KERNEL_FWD_SEG = 2,    /* forward segment kernel: O                 */
+    LINREC_KERNEL_BWD_SUM = 3,    /* reverse segment sums (parallel)           */
+    LINREC_KERNEL_BWD_FOLD = 4,   /* reverse fold across segments (dS carried) */
+    LINREC_KERNEL_BWD_SEG = 5,    /* backward segment kernel: dQ, dK, dV       */
+    LINREC_KERNEL_KINDS = 6
 };
 
 /* Per-kernel timing (instrumentation, off by default).  While enabled, every

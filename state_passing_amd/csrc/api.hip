@@ -147,10 +147,11 @@ linrec_status check_pieces(const linrec_desc* d, int32_t npieces, const int32_t*
     return sum == d->T ? LINREC_OK : LINREC_E_SHAPE;
 }
 
-// Stored per-segment states and gradients are fp32 whatever the activation dtype.
+// Stored per-segment records (state or gradient, then the segment's
+// log-decay) are fp32 whatever the activation dtype.
 size_t per_seg_bytes(const linrec_desc* d)
 {
-    return (size_t)d->dk * (size_t)d->dv * sizeof(float);
+    return (size_t)linrec::seg_record_floats(d->dk, d->dv) * sizeof(float);
 }
 
 int64_t total_nseg(int32_t npieces, const int32_t* lengths)
@@ -366,14 +367,19 @@ hipError_t timed_launch(linrec_ctx* ctx, int kind, hipStream_t stream, F fn)
             return hip_fail(e_, LINREC_E_LAUNCH);                 \
     } while (0)
 
-#define LAUNCH_SCAN(ctx, desc, stream)                                                     \
-    LAUNCH(timed_launch((ctx), (desc).reverse ? LINREC_KERNEL_BWD_SCAN : LINREC_KERNEL_FWD_SCAN, \
-                        (stream), [&] { return linrec::launch_state_scan((desc), (stream)); }))
+// The state transition of a piece: segment sum, then fold.
+#define LAUNCH_SCAN(ctx, desc, stream)                                                       \
+    do {                                                                                    \
+        LAUNCH(timed_launch((ctx), (desc).reverse ? LINREC_KERNEL_BWD_SUM : LINREC_KERNEL_FWD_SUM, \
+                            (stream), [&] { return linrec::launch_seg_sum((desc), (stream)); })); \
+        LAUNCH(timed_launch((ctx), (desc).reverse ? LINREC_KERNEL_BWD_FOLD : LINREC_KERNEL_FWD_FOLD, \
+                            (stream), [&] { return linrec::launch_seg_fold((desc), (stream)); })); \
+    } while (0)
 #define LAUNCH_FWD_INTRA(ctx, desc, stream)                                                \
-    LAUNCH(timed_launch((ctx), LINREC_KERNEL_FWD_INTRA, (stream),                          \
+    LAUNCH(timed_launch((ctx), LINREC_KERNEL_FWD_SEG, (stream),                            \
                         [&] { return linrec::launch_fwd_intra((desc), (stream)); }))
 #define LAUNCH_BWD_INTRA(ctx, desc, stream)                                                \
-    LAUNCH(timed_launch((ctx), LINREC_KERNEL_BWD_INTRA, (stream),                          \
+    LAUNCH(timed_launch((ctx), LINREC_KERNEL_BWD_SEG, (stream),                            \
                         [&] { return linrec::launch_bwd_intra((desc), (stream)); }))
 
 #define HIPCHECK(call)                                            \

@@ -19,16 +19,18 @@
 // gptget summary's method details).
 //
 // Two levels.  Chunks are grouped into segments of m chunks.
-//   * The segment scan (one launch per direction and piece) is the serial
-//     state transition: it produces the state entering every segment (the
-//     gradient leaving every segment in the reverse direction) and the
-//     piece's boundary state.  Only those per-segment states reach memory.
+//   * The state transition (a parallel segment-sum launch and a serial fold
+//     launch per direction and piece) produces the state entering every
+//     segment (the gradient leaving every segment in the reverse direction)
+//     and the piece's boundary state.  Only those per-segment states reach
+//     memory.
 //   * The segment kernels (one workgroup per segment) walk the segment's
 //     chunks with the state in fp32 registers, rebuilding every per-chunk
 //     state on the fly; the backward walks forward for dQ (carrying S) and
 //     then in reverse for dK and dV (carrying G).
-// Per-segment states are stored transposed, [d_v][d_k] with d_k contiguous,
-// fp32: [B][H][nseg][d_v][d_k].
+// Per-segment records are fp32: the state [d_k][d_v] (the layout of S_in and
+// S_out), then the segment's total log-decay, padded to 64 floats:
+// [B][H][nseg][d_k * d_v + 64].
 //
 // Every operand these kernels compute (P, A, the decay-scaled K or Q, the
 // carried states) enters the MFMA as a bf16 hi + lo pair against an exact
@@ -38,263 +40,6 @@
 #include "launch.hpp"
 
 namespace linrec {
-
-// Order this wave's LDS accesses (a wave's LDS operations complete in issue
-// order; this keeps the compiler from moving them across the point).
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-// ---------------------------------------------------------------------------
-// Segment scan.  Workgroup = (b, h, 32x32 tile of the state), 4 waves.  In
-// round r wave w folds segment 4r + w (counted from the piece end in the
-// reverse direction) from a zero state: local = gamma_C local + X^T Y per
-// chunk, X = K rows scaled by gamma_C/gamma_j (forward) or Q rows scaled by
-// gamma_i (reverse), split hi + lo; Y = V or dO.  The four partial results
-// then go through LDS and every wave folds them in order into its copy of
-// the carried state; the wave that owns a segment writes the state at that
-// segment's boundary.  The fold is the only serial step; chunk loads run two
-// chunks ahead in registers.
-// ---------------------------------------------------------------------------
-template <typename T>
-struct ScanTile {
-    static constexpr int VEC = 16 / sizeof(T);     // elements per 16-byte vector
-    static constexpr int NV = 32 / VEC;            // vectors per lane per 64x32 tile
-    u32x4 x[NV], y[NV];
-};
-
-template <typename T>
-struct Vec16;
-template <>
-struct Vec16<bf16> {
-    typedef bf16x8 type;
-};
-template <>
-struct Vec16<float> {
-    typedef floatx4 type;
-};
-
-template <typename T>
-__device__ __forceinline__ void scan_load(ScanTile<T>& r, const T* xh, const T* yh, int64_t xst,
-                                          int64_t yst, int64_t tok0)
-{
-    constexpr int VEC = ScanTile<T>::VEC, PR = 32 / VEC;
-    const int l = lane_id();
-#pragma unroll
-    for (int p = 0; p < ScanTile<T>::NV; ++p) {
-        const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
-        r.x[p] = *reinterpret_cast<const u32x4*>(xh + (tok0 + row) * xst + col);
-        r.y[p] = *reinterpret_cast<const u32x4*>(yh + (tok0 + row) * yst + col);
-    }
-}
-
-template <typename T, int DK, int DV, bool REVERSE>
-__global__ __launch_bounds__(256) void seg_scan_kernel(
-    Act<const T> X, Act<const T> Y, DecayArg dec, const float* __restrict__ carry_in,
-    float* __restrict__ carry_out, float* __restrict__ store, int64_t store_nseg, int H, int N,
-    int m)
-{
-    constexpr int TF = 32, TC = 32;
-    constexpr int PAD = Pad<T>::value;
-    constexpr int XP = TF + PAD, YP = TC + PAD;
-    constexpr int NTC = DV / TC;
-    constexpr int VEC = ScanTile<T>::VEC, NV = ScanTile<T>::NV, PR = 32 / VEC;
-    typedef typename Vec16<T>::type V;
-    __shared__ __align__(16) T Xs[4][2][CHUNK * XP];
-    __shared__ __align__(16) T Ys[4][CHUNK * YP];
-    __shared__ __align__(16) float part[4][16 * 64];   // one 32x32 fp32 tile per wave
-    __shared__ float part_log[4];
-
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int f0 = (tile / NTC) * TF, c0 = (tile % NTC) * TC;
-    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
-    const int64_t bh = (int64_t)b * H + h;
-    const int nseg = (N + m - 1) / m;
-
-    // carry[fb][cb] holds S[f0 + 16fb + 4g + r][c0 + 16cb + t]; every wave
-    // keeps the same copy
-    floatx4 carry[2][2];
-#pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                carry[fb][cb][r] = carry_in
-                    ? carry_in[(bh * DK + f0 + 16 * fb + 4 * g + r) * DV + c0 + 16 * cb + t]
-                    : 0.f;
-
-    const T* xh = X.head(b, h) + f0;
-    const T* yh = Y.head(b, h) + c0;
-    float* sh = store + bh * store_nseg * (int64_t)(DV * DK);
-    T* xs_hi = Xs[w][0];
-    T* xs_lo = Xs[w][1];
-    T* ys = Ys[w];
-
-    const bool const_decay = dec.kind != 2;
-    float lm = chunk_log_cumsum(dec, b, h, 0);
-    float lamC = __shfl(lm, 63, 64);
-    float xsc[NV];
-    const auto factors = [&]() {
-#pragma unroll
-        for (int p = 0; p < NV; ++p) {
-            const float lr = __shfl(lm, (l + 64 * p) / PR, 64);
-            xsc[p] = REVERSE ? __expf(lr) : __expf(lamC - lr);
-        }
-    };
-    factors();
-
-    // chunk range of the segment with processing index sidx
-    const auto seg_range = [&](int sidx, int& n0, int& n1) {
-        const int s = REVERSE ? nseg - 1 - sidx : sidx;
-        n0 = s * m;
-        n1 = min(n0 + m, N);
-    };
-    ScanTile<T> buf0, buf1;
-    // the first two chunks of this wave's segment `sidx` (loads run ahead of
-    // the fold barriers)
-    const auto prefetch_segment = [&](int sidx) {
-        if (sidx >= nseg)
-            return;
-        int n0, n1;
-        seg_range(sidx, n0, n1);
-        scan_load(buf0, xh, yh, X.st, Y.st, (int64_t)(REVERSE ? n1 - 1 : n0) * CHUNK);
-        if (n1 - n0 > 1)
-            scan_load(buf1, xh, yh, X.st, Y.st, (int64_t)(REVERSE ? n1 - 2 : n0 + 1) * CHUNK);
-    };
-    prefetch_segment(w);
-
-    for (int r0 = 0; r0 < nseg; r0 += 4) {
-        // ---- wave w folds its segment from zero
-        const int sidx = r0 + w;   // segment index in processing order
-        floatx4 loc[2][2];
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                loc[fb][cb] = zero4();
-        float seg_log = 0.f;
-        if (sidx < nseg) {
-            int n0, n1;
-            seg_range(sidx, n0, n1);
-            const int cnt = n1 - n0;
-            const auto chunk_of = [&](int it) { return REVERSE ? n1 - 1 - it : n0 + it; };
-            const auto step = [&](int it, ScanTile<T>& cur) {
-                const int n = chunk_of(it);
-                const int64_t tok0 = (int64_t)n * CHUNK;
-                if (!const_decay) {
-                    lm = chunk_log_cumsum(dec, b, h, tok0);
-                    lamC = __shfl(lm, 63, 64);
-                    factors();
-                }
-                seg_log += lamC;
-#pragma unroll
-                for (int p = 0; p < NV; ++p) {
-                    const int idx = l + 64 * p, row = idx / PR, col = (idx % PR) * VEC;
-                    const V xv = __builtin_bit_cast(V, cur.x[p]);
-                    V hi, lo;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) {
-                        const float v = (float)xv[e] * xsc[p];
-                        hi[e] = (T)v;
-                        lo[e] = (T)(v - (float)hi[e]);
-                    }
-                    *reinterpret_cast<V*>(&xs_hi[row * XP + col]) = hi;
-                    if constexpr (sizeof(T) == 2)
-                        *reinterpret_cast<V*>(&xs_lo[row * XP + col]) = lo;
-                    *reinterpret_cast<u32x4*>(&ys[row * YP + col]) = cur.y[p];
-                }
-                if (it + 2 < cnt)
-                    scan_load(cur, xh, yh, X.st, Y.st, (int64_t)chunk_of(it + 2) * CHUNK);
-                wave_lds_sync();
-                floatx4 dlt[2][2];
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        dlt[fb][cb] = zero4();
-#pragma unroll
-                for (int ks = 0; ks < CHUNK / 32; ++ks) {
-                    Split<T> a[2];
-                    Frag<T> bb[2];
-#pragma unroll
-                    for (int fb = 0; fb < 2; ++fb)
-                        a[fb] = frag_cols_split(xs_hi, xs_lo, XP, 16 * fb, 32 * ks);
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        bb[cb] = frag_cols(ys, YP, 16 * cb, 32 * ks);
-#pragma unroll
-                    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb)
-                            dlt[fb][cb] = mma(a[fb], bb[cb], dlt[fb][cb]);
-                }
-                const float gC = __expf(lamC);
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        loc[fb][cb] = gC * loc[fb][cb] + dlt[fb][cb];
-                wave_lds_sync();
-            };
-            for (int it = 0; it < cnt; it += 2) {
-                step(it, buf0);
-                if (it + 1 < cnt)
-                    step(it + 1, buf1);
-            }
-        }
-        prefetch_segment(sidx + 4);
-        // ---- publish the partial folds, then fold them into the carry in order
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                *reinterpret_cast<floatx4*>(&part[w][(2 * fb + cb) * 256 + 4 * l]) = loc[fb][cb];
-        if (l == 0)
-            part_log[w] = seg_log;
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int su = r0 + u;
-            if (su < nseg) {
-                const int s = REVERSE ? nseg - 1 - su : su;
-                if (u == w) {
-                    // state entering segment s (forward) / gradient leaving it (reverse)
-                    float* sn = sh + (int64_t)s * (DV * DK);
-#pragma unroll
-                    for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                        for (int cb = 0; cb < 2; ++cb)
-                            *reinterpret_cast<float4*>(sn + (int64_t)(c0 + 16 * cb + t) * DK + f0 +
-                                                       16 * fb + 4 * g) =
-                                float4{carry[fb][cb][0], carry[fb][cb][1], carry[fb][cb][2],
-                                       carry[fb][cb][3]};
-                }
-                const float gS = __expf(part_log[u]);
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        carry[fb][cb] = gS * carry[fb][cb] +
-                            *reinterpret_cast<const floatx4*>(&part[u][(2 * fb + cb) * 256 + 4 * l]);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (w == 0) {
-#pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    carry_out[(bh * DK + f0 + 16 * fb + 4 * g + r) * DV + c0 + 16 * cb + t] =
-                        carry[fb][cb][r];
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Shared pieces of the segment kernels.
@@ -347,19 +92,32 @@ __device__ __forceinline__ void state_update(floatx4 (&carry)[DK / 16][NCB], con
     }
 }
 
-// Load a wave's columns of a stored [d_v][d_k] fp32 state into register tiles.
-template <int DK, int NCB>
+// Load a wave's columns of a stored [d_k][d_v] fp32 state into register tiles.
+template <int DK, int DV, int NCB>
 __device__ __forceinline__ void load_state(floatx4 (&st)[DK / 16][NCB], const float* src, int cbase0)
 {
     const int l = lane_id(), t = l & 15, g = l >> 4;
 #pragma unroll
     for (int fb = 0; fb < DK / 16; ++fb)
 #pragma unroll
-        for (int cbl = 0; cbl < NCB; ++cbl) {
-            const float4 v = *reinterpret_cast<const float4*>(
-                src + (int64_t)(cbase0 + 16 * cbl + t) * DK + 16 * fb + 4 * g);
-            st[fb][cbl] = floatx4{v.x, v.y, v.z, v.w};
-        }
+        for (int cbl = 0; cbl < NCB; ++cbl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st[fb][cbl][r] = src[(int64_t)(16 * fb + 4 * g + r) * DV + cbase0 + 16 * cbl + t];
+}
+
+// Store a wave's register tiles of a state as [d_k][d_v] fp32.
+template <int DK, int DV, int NCB>
+__device__ __forceinline__ void store_state(float* dst, const floatx4 (&st)[DK / 16][NCB], int cbase0)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+#pragma unroll
+    for (int fb = 0; fb < DK / 16; ++fb)
+#pragma unroll
+        for (int cbl = 0; cbl < NCB; ++cbl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(int64_t)(16 * fb + 4 * g + r) * DV + cbase0 + 16 * cbl + t] = st[fb][cbl][r];
 }
 
 // Write a wave's register tiles of a state into an LDS plane pair laid out
@@ -374,6 +132,121 @@ __device__ __forceinline__ void put_state(T* hi, T* lo, int pitch, const floatx4
 #pragma unroll
         for (int cbl = 0; cbl < NCB; ++cbl)
             put_split4(hi, lo, (cbase0 + 16 * cbl + t) * pitch + 16 * fb + 4 * g, st[fb][cbl]);
+}
+
+// ---------------------------------------------------------------------------
+// State transition across a piece, in two launches.
+//
+// Segment sum (parallel over segments): workgroup = (b, h, segment), one
+// wave per 16 state columns.  It folds the segment's chunks from a zero
+// state with the same update the segment kernels use,
+//   forward  U = gamma_C U + K^T (V .* gamma_C/gamma)      (chunks in order)
+//   reverse  U = gamma_C U + Q^T (dO .* gamma)             (chunks reversed)
+// and writes U and the segment's total log-decay into the segment's record.
+//
+// Fold (serial over segments, parallel over state elements): each thread
+// walks the records in order, replacing U_s by the carried value and
+// carrying  c <- exp(log Gamma_s) c + U_s;  it starts from S_in (dS_out) and
+// ends with S_out (dS_in).  In the forward direction record s then holds the
+// state entering segment s; in the reverse direction the gradient leaving it.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV, bool REVERSE>
+__global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
+    Act<const T> X, Act<const T> Y, DecayArg dec, float* __restrict__ store, int64_t store_nseg,
+    int H, int N, int m)
+{
+    constexpr int NW = DV / 16, NT = NW * 64;
+    constexpr int PAD = Pad<T>::value;
+    constexpr int XP = DK + PAD, YP = DV + PAD;
+    constexpr int64_t REC = seg_record_floats(DK, DV);
+    __shared__ __align__(16) T Xs[CHUNK * XP];
+    __shared__ __align__(16) T Ys[CHUNK * YP];
+    __shared__ float lam[CHUNK];
+
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int w = wave_id(), l = lane_id();
+    const int64_t bh = (int64_t)b * H + h;
+    const int cbase = 16 * w;
+    const int n0 = s * m, n1 = min(n0 + m, N), cnt = n1 - n0;
+    const T* xh = X.head(b, h);
+    const T* yh = Y.head(b, h);
+
+    floatx4 U[DK / 16][1];
+#pragma unroll
+    for (int fb = 0; fb < DK / 16; ++fb)
+        U[fb][0] = zero4();
+    float seg_log = 0.f;
+
+    ChunkRegs<T, DK, NT> rx;
+    ChunkRegs<T, DV, NT> ry;
+    int n = REVERSE ? n1 - 1 : n0;
+    chunk_load(rx, xh + (int64_t)n * CHUNK * X.st, X.st);
+    chunk_load(ry, yh + (int64_t)n * CHUNK * Y.st, Y.st);
+    float ra = decay_raw(dec, b, h, (int64_t)n * CHUNK);
+    for (int it = 0; it < cnt; ++it) {
+        chunk_store(rx, Xs, XP);
+        chunk_store(ry, Ys, YP);
+        if (w == 0)
+            lam[l] = decay_log_cumsum(dec, ra);
+        __syncthreads();
+        if (it + 1 < cnt) {
+            n = REVERSE ? n1 - 2 - it : n0 + 1 + it;
+            const int64_t tn = (int64_t)n * CHUNK;
+            chunk_load(rx, xh + tn * X.st, X.st);
+            chunk_load(ry, yh + tn * Y.st, Y.st);
+            ra = decay_raw(dec, b, h, tn);
+        }
+        const float lamC = lam[CHUNK - 1];
+        seg_log += lamC;
+        float yf[2][8];
+        slot_factors(lam, lamC, !REVERSE, yf);
+        state_update<T, DK, 1>(U, Xs, XP, Ys, YP, cbase, __expf(lamC), yf);
+        __syncthreads();
+    }
+
+    float* rec = store + (bh * store_nseg + s) * REC;
+    store_state<DK, DV, 1>(rec, U, cbase);
+    if (threadIdx.x == 0)
+        rec[DK * DV] = seg_log;
+}
+
+template <int DK, int DV, bool REVERSE>
+__global__ __launch_bounds__(256) void seg_fold_kernel(
+    const float* __restrict__ carry_in, float* __restrict__ carry_out, float* __restrict__ store,
+    int64_t store_nseg, int H, int nseg)
+{
+    constexpr int64_t REC = seg_record_floats(DK, DV);
+    const int e = blockIdx.x * 256 + threadIdx.x;          // element [f][c] of a record
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * H + h;
+    const int64_t io = bh * (DK * DV) + e;                   // S_in / S_out: same layout
+    float carry = carry_in ? carry_in[io] : 0.f;
+    float* base = store + bh * store_nseg * REC;
+    // loads of a batch of records are issued before any of the batch's
+    // stores (each store goes to a slot that was just read)
+    constexpr int BATCH = 16;
+    for (int k0 = 0; k0 < nseg; k0 += BATCH) {
+        float u[BATCH], lg[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int k = k0 + j;
+            if (k < nseg) {
+                const float* rec = base + (REVERSE ? nseg - 1 - k : k) * REC;
+                u[j] = rec[e];
+                lg[j] = rec[DK * DV];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            const int k = k0 + j;
+            if (k < nseg) {
+                float* rec = base + (REVERSE ? nseg - 1 - k : k) * REC;
+                rec[e] = carry;
+                carry = __expf(lg[j]) * carry + u[j];
+            }
+        }
+    }
+    carry_out[io] = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -408,7 +281,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     const int n0 = s * m, n1 = min(n0 + m, N);
 
     floatx4 S[DK / 16][1];
-    load_state<DK, 1>(S, bstates + (bh * bs_nseg + s) * (int64_t)(DV * DK), cbase);
+    load_state<DK, DV, 1>(S, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
 
     const T* qh = Q.head(b, h);
     const T* kh = K.head(b, h);
@@ -542,7 +415,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     ChunkRegs<T, DV, NT> rv, rdo;
 
     // ---------------- walk 1: dQ
-    load_state<DK, 1>(C, bstates + (bh * bs_nseg + s) * (int64_t)(DV * DK), cbase);
+    load_state<DK, DV, 1>(C, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
     chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
     chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
     chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st);
@@ -615,7 +488,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     }
 
     // ---------------- walk 2: dK, dV
-    load_state<DK, 1>(C, gstates + (bh * gs_nseg + s) * (int64_t)(DV * DK), cbase);
+    load_state<DK, DV, 1>(C, gstates + (bh * gs_nseg + s) * seg_record_floats(DK, DV), cbase);
     for (int n = n1 - 1; n >= n0; --n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         chunk_store(rq, Qs, QP);
@@ -726,17 +599,31 @@ DecayArg decay_arg(const TensorArg& d, int kind)
 }
 
 template <typename T, typename OT, int DK, int DV>
-hipError_t scan_impl(const ScanLaunch& s, hipStream_t stream)
+hipError_t sum_impl(const ScanLaunch& s, hipStream_t stream)
 {
-    const dim3 grid((DK / 32) * (DV / 32), s.H, s.B), block(256);
+    const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
     if (s.reverse)
-        hipLaunchKernelGGL((seg_scan_kernel<T, DK, DV, true>), grid, block, 0, stream,
-                           cact<T>(s.x), cact<T>(s.y), decay_arg(s.decay, s.decay_kind),
-                           s.carry_in, s.carry_out, (float*)s.store, s.store_nseg, s.H, s.N, s.m);
+        hipLaunchKernelGGL((seg_sum_kernel<T, DK, DV, true>), grid, block, 0, stream, cact<T>(s.x),
+                           cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                           s.store_nseg, s.H, s.N, s.m);
     else
-        hipLaunchKernelGGL((seg_scan_kernel<T, DK, DV, false>), grid, block, 0, stream,
-                           cact<T>(s.x), cact<T>(s.y), decay_arg(s.decay, s.decay_kind),
-                           s.carry_in, s.carry_out, (float*)s.store, s.store_nseg, s.H, s.N, s.m);
+        hipLaunchKernelGGL((seg_sum_kernel<T, DK, DV, false>), grid, block, 0, stream, cact<T>(s.x),
+                           cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                           s.store_nseg, s.H, s.N, s.m);
+    return hipGetLastError();
+}
+
+template <typename T, typename OT, int DK, int DV>
+hipError_t fold_impl(const ScanLaunch& s, hipStream_t stream)
+{
+    const int nseg = (s.N + s.m - 1) / s.m;
+    const dim3 grid(DK * DV / 256, s.H, s.B), block(256);
+    if (s.reverse)
+        hipLaunchKernelGGL((seg_fold_kernel<DK, DV, true>), grid, block, 0, stream, s.carry_in,
+                           s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
+    else
+        hipLaunchKernelGGL((seg_fold_kernel<DK, DV, false>), grid, block, 0, stream, s.carry_in,
+                           s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
     return hipGetLastError();
 }
 
@@ -783,12 +670,21 @@ hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
         return hipErrorInvalidValue;                                                   \
     } while (0)
 
-hipError_t launch_state_scan(const ScanLaunch& s, hipStream_t stream)
+hipError_t launch_seg_sum(const ScanLaunch& s, hipStream_t stream)
 {
     if (s.dtype == 0)
-        LINREC_DISPATCH_D(scan_impl, bf16, float, s, stream);
+        LINREC_DISPATCH_D(sum_impl, bf16, float, s, stream);
     else if (s.dk == 64 && s.dv == 64)
-        return scan_impl<float, float, 64, 64>(s, stream);
+        return sum_impl<float, float, 64, 64>(s, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_seg_fold(const ScanLaunch& s, hipStream_t stream)
+{
+    if (s.dtype == 0)
+        LINREC_DISPATCH_D(fold_impl, bf16, float, s, stream);
+    else if (s.dk == 64 && s.dv == 64)
+        return fold_impl<float, float, 64, 64>(s, stream);
     return hipErrorInvalidValue;
 }
 

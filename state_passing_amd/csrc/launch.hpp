@@ -7,14 +7,18 @@
 
 namespace linrec {
 
+// Floats per stored segment record: a d_k x d_v state, then the segment's
+// total log-decay, padded so records stay 256-byte aligned.
+constexpr __host__ __device__ int64_t seg_record_floats(int dk, int dv) { return (int64_t)dk * dv + 64; }
+
 struct TensorArg {
     const void* ptr;
     int64_t sb, sh, st;
 };
 
 // A piece has N chunks of 64 tokens, grouped into segments of m chunks (the
-// last one may be shorter).  Per-segment matrices are fp32 [d_v][d_k] in a
-// store laid out [B][H][nseg][d_v][d_k]; pointers are already offset to the
+// last one may be shorter).  Per-segment records (seg_record_floats) live in
+// a store laid out [B][H][nseg][record]; pointers are already offset to the
 // piece's first segment and *_nseg is the store's segments per (b, h).
 
 // Segment scan of one piece.  Forward: x = K, y = V, carry S_in -> S_out,
@@ -50,7 +54,10 @@ struct BwdIntraLaunch {
     int64_t g_nseg;
 };
 
-hipError_t launch_state_scan(const ScanLaunch& s, hipStream_t stream);
+// The state transition is two launches: the parallel segment sum, then the
+// serial fold (both from the same description).
+hipError_t launch_seg_sum(const ScanLaunch& s, hipStream_t stream);
+hipError_t launch_seg_fold(const ScanLaunch& s, hipStream_t stream);
 hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream);
 

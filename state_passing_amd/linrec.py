@@ -41,7 +41,8 @@ EXPORTS = (
     "linrec_ctx_kernel_times",
 )
 
-KERNEL_KINDS = {0: "fwd_scan", 1: "fwd_intra", 2: "bwd_scan", 3: "bwd_intra"}
+KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
+                5: "bwd_seg"}
 
 
 class LinrecError(RuntimeError):

@@ -50,17 +50,18 @@ def d(**kw):
 
 
 def test_sizes():
-    # one fp32 state per segment of 4 chunks (256 tokens), whatever the dtype
-    assert linrec.states_bytes(d()) == 16 * 16 * 128 * 128 * 4
-    assert linrec.states_bytes(d(dtype=linrec.F32, dk=64, dv=64)) == 16 * 16 * 64 * 64 * 4
+    # one fp32 record (state + 64 floats) per segment of 4 chunks (256 tokens)
+    rec = (128 * 128 + 64) * 4
+    assert linrec.states_bytes(d()) == 16 * 16 * rec
+    assert linrec.states_bytes(d(dtype=linrec.F32, dk=64, dv=64)) == 16 * 16 * (64 * 64 + 64) * 4
     assert linrec.states_bytes(d(out=linrec.F32)) == linrec.states_bytes(d())
-    assert linrec.states_bytes(d(T=320)) == 16 * 2 * 128 * 128 * 4     # a short last segment
+    assert linrec.states_bytes(d(T=320)) == 16 * 2 * rec     # a short last segment
     assert linrec.bwd_workspace_bytes(d()) == linrec.states_bytes(d())
     # the per-piece store is linear in the piece length only
     assert linrec.states_bytes(d(T=8192)) == 2 * linrec.states_bytes(d())
     # sequence store: the sum of the pieces' stores
     assert linrec.seq_states_bytes(d(T=8192), [2048, 4096, 2048]) == linrec.states_bytes(d(T=8192))
-    assert linrec.seq_states_bytes(d(T=384), [64, 320]) == 16 * 3 * 128 * 128 * 4
+    assert linrec.seq_states_bytes(d(T=384), [64, 320]) == 16 * 3 * rec
     assert linrec.seq_states_bytes(d(T=384), [64, 300]) == 0
     # two slots of the longest piece
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \

@@ -1,0 +1,70 @@
+"""Full-size parity: the five workloads at their real shapes, run through
+the sequence-accumulation drivers exactly as the benchmark runs them (pieces
+in order with S carried, then in reverse with dS carried), compared with the
+unsplit fp64 oracle on sampled heads over the whole sequence.
+
+  tiny-fp32        B=1 H=2  T=1024    4 x 256,    a_t = 1, fp32  (all heads;
+                   also unsplit)
+  decay-16k        B=1 H=16 T=16384   4 x 4096,   per-head decay   (all heads)
+  sa-256k          B=1 H=16 T=262144  64 x 4096,  per-head decay   (4 heads)
+  nonuniform-256k  B=1 H=32 T=262144  16 random pieces, S_in != 0  (4 heads)
+  gated-batch      B=8 H=32 T=32768   8 x 4096,   per-token gate   (8 heads)
+
+Outputs are checked twice: fp32 outputs against the plain 2e-2 bar, and the
+bf16 outputs the benchmark produces beyond their half-ulp representation
+limit (see parity_util)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from parity_util import TOL, compare, oracle_run
+from state_passing_amd import linrec
+from state_passing_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+CASES = {
+    1: [(0, 0), (0, 1)],
+    2: [(0, h) for h in range(16)],
+    3: [(0, 0), (0, 5), (0, 10), (0, 15)],
+    4: [(0, 0), (0, 11), (0, 22), (0, 31)],
+    5: [(0, 3), (1, 30), (2, 0), (3, 17), (4, 9), (5, 25), (6, 14), (7, 31)],
+}
+
+
+def run_sa(inp, lengths, out_dtype):
+    o, S_out, st = linrec.fwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, inp.S_in,
+                                  out_dtype=out_dtype)
+    dq, dk, dv, dS_in = linrec.bwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, st, inp.dO,
+                                       None, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS_in)
+
+
+@pytest.mark.parametrize("idx", sorted(CASES))
+def test_fullsize_sequence_accumulation(idx):
+    wl = WORKLOADS[idx]
+    heads = CASES[idx]
+    lengths = wl.pieces()
+    print(f"workload {wl.name}: {len(lengths)} pieces, heads {heads}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    nthreads = min(len(heads), len(os.sched_getaffinity(0)))
+    ref = oracle_run(inp, heads, nthreads=nthreads)
+    tol = TOL[wl.torch_dtype]
+    runs = [(lengths, torch.float32)]
+    if wl.dtype == "bf16":
+        runs.append((lengths, torch.bfloat16))
+    else:
+        runs.append(([wl.T], torch.float32))
+    for lens, odt in runs:
+        got = run_sa(inp, lens, odt)
+        errs, bad = compare(got, ref, heads, tol)
+        print(f"[{wl.name} {len(lens)} pieces {odt}] "
+              + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        assert not bad, f"{wl.name} {len(lens)} pieces, outputs {odt}: over {tol}: {bad}"
+        del got
+    torch.cuda.empty_cache()

@@ -201,8 +201,10 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
                                       const int32_t* lengths);
 
 /* Backward of linrec_fwd_seq: pieces in reverse order with dS carried back
- * from dS_out to dS_in; the reverse state scans run on the auxiliary stream
- * and overlap the per-chunk gradient kernels of the following piece. */
+ * from dS_out to dS_in.  Every launch goes to `stream` (the backward segment
+ * kernel occupies a whole CU, so a concurrent transition kernel would only
+ * delay it).  The workspace holds the gradient records of one piece, reused
+ * piece after piece. */
 linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              int32_t npieces, const int32_t* lengths,
                              linrec_tensor q, linrec_tensor k, linrec_tensor v,

@@ -28,7 +28,6 @@ struct linrec_ctx {
     hipStream_t aux;        // state transitions
     hipEvent_t ev_start;    // inputs ready on the caller's stream
     hipEvent_t ev_scan;     // a piece's scan finished (aux)
-    hipEvent_t ev_intra[2]; // a piece's per-chunk kernel finished (caller's stream)
     // opt-in per-kernel timing (linrec_ctx_set_timing)
     int timing;
     std::vector<TimedLaunch> pending;
@@ -411,10 +410,6 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device)
         e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&c->ev_scan, hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipEventCreateWithFlags(&c->ev_intra[0], hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipEventCreateWithFlags(&c->ev_intra[1], hipEventDisableTiming);
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         linrec_ctx_destroy(c);
@@ -434,9 +429,6 @@ linrec_status linrec_ctx_destroy(linrec_ctx* ctx)
         (void)hipEventDestroy(ctx->ev_start);
     if (ctx->ev_scan)
         (void)hipEventDestroy(ctx->ev_scan);
-    for (int i = 0; i < 2; ++i)
-        if (ctx->ev_intra[i])
-            (void)hipEventDestroy(ctx->ev_intra[i]);
     for (const TimedLaunch& t : ctx->pending) {
         (void)hipEventDestroy(t.begin);
         (void)hipEventDestroy(t.end);
@@ -510,9 +502,7 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces, con
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
         return 0;
-    const int slots = npieces > 1 ? 2 : 1;
-    return (size_t)slots * (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) *
-           per_seg_bytes(d);
+    return (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
 }
 
 linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
@@ -597,32 +587,20 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         return st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t nseg_total = total_nseg(npieces, lengths);
-    const size_t slot_bytes =
-        (size_t)d->B * d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
-
-    HIPCHECK(hipEventRecord(ctx->ev_start, s));
-    HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_start, 0));
-    // Per-chunk gradients of piece i go to slot i % 2; before a scan
-    // overwrites a slot it waits for the per-chunk kernel that read it.
-    bool slot_used[2] = {false, false};
+    // Every launch goes to the caller's stream, one piece after another.
+    // The backward segment kernel fills a CU's LDS, so transition kernels
+    // on a second stream cannot share a CU with it; running them
+    // concurrently only delays its workgroups.
     int64_t tok_end = d->T, seg_end = nseg_total;
     for (int32_t i = npieces - 1; i >= 0; --i) {
         const int64_t tok0 = tok_end - lengths[i];
         const int64_t seg0 = seg_end - nseg_of(lengths[i]);
-        const int slot = i & 1;
-        void* ghat = (char*)workspace + slot * slot_bytes;
-        if (slot_used[slot])
-            HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_intra[slot], 0));
         const float* cin = i == npieces - 1 ? dS_out : dS_in;
-        const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, ghat);
+        const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, workspace);
         const BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0, lengths[i],
-                                               states, seg0, nseg_total, ghat);
-        LAUNCH_SCAN(ctx, sc, ctx->aux);
-        HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
-        HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
+                                               states, seg0, nseg_total, workspace);
+        LAUNCH_SCAN(ctx, sc, s);
         LAUNCH_BWD_INTRA(ctx, in, s);
-        HIPCHECK(hipEventRecord(ctx->ev_intra[slot], s));
-        slot_used[slot] = true;
         tok_end = tok0;
         seg_end = seg0;
     }

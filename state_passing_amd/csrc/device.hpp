@@ -49,8 +49,13 @@ struct Act {
     __device__ __forceinline__ T* head(int b, int h) const { return ptr + b * sb + h * sh; }
 };
 
+// LDS row padding.  32 bytes per row keep 16-byte row reads (frag_rows) and
+// the transposing reads (frag_cols, frag_cols_perm) near the LDS peak;
+// 16 bytes suit 8-byte row reads (frag_rows_perm) better.
 template <typename T>
-struct Pad { static constexpr int value = 16 / sizeof(T); };  // 16 bytes of row padding
+struct Pad { static constexpr int value = 32 / sizeof(T); };
+template <typename T>
+struct Pad16 { static constexpr int value = 16 / sizeof(T); };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
@@ -519,6 +524,28 @@ __device__ __forceinline__ void store_tile(OT* base, int64_t ld, int rbase, int 
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         p[r * ld] = (OT)acc[r];
+}
+
+// Store a 16x16 fp32 result tile computed transposed (lane (g,t) holds
+// rows 4g + r of the transpose, i.e. row rbase + t, columns cbase + 4g + r of
+// the output) to row-major global memory as OT: one 8-byte (bf16) or 16-byte
+// (fp32) store per lane.
+template <typename OT>
+__device__ __forceinline__ void store_tile_t(OT* base, int64_t ld, int rbase, int cbase, floatx4 acc);
+
+template <>
+__device__ __forceinline__ void store_tile_t<bf16>(bf16* base, int64_t ld, int rbase, int cbase, floatx4 acc)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const bf16x4 v = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+    *reinterpret_cast<bf16x4*>(base + (rbase + t) * ld + cbase + 4 * g) = v;
+}
+
+template <>
+__device__ __forceinline__ void store_tile_t<float>(float* base, int64_t ld, int rbase, int cbase, floatx4 acc)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    *reinterpret_cast<floatx4*>(base + (rbase + t) * ld + cbase + 4 * g) = acc;
 }
 
 }  // namespace linrec

@@ -267,8 +267,11 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 {
     constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
+    // Q is read by 8-byte row reads (the Q S product), K, V and P by 16-byte
+    // row reads and transposing reads
+    constexpr int QQ = DK + Pad16<T>::value;
     constexpr int QP = DK + PAD, VP = DV + PAD, PP = CHUNK + PAD;
-    __shared__ __align__(16) T Qs[CHUNK * QP];
+    __shared__ __align__(16) T Qs[CHUNK * QQ];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T Ps[2][CHUNK * PP];
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rq, Qs, QP);
+        chunk_store(rq, Qs, QQ);
         chunk_store(rk, Ks, QP);
         chunk_store(rv, Vs, VP);
         if (w == 0)
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             if (jb <= ib_p) {
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mma(frag_rows(Qs, QP, 16 * ib_p, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
+                    acc = mma(frag_rows(Qs, QQ, 16 * ib_p, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -336,21 +339,21 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             sf[ks] = split_tiles<T>(S[2 * ks][0], S[2 * ks + 1][0]);
         __syncthreads();
 
+        // O^T tiles (rows = this wave's columns, columns = tokens), so each
+        // lane ends up holding four consecutive outputs of one token
         OT* oh = O.head(b, h) + tok0 * O.st;
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             floatx4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(frag_rows_perm(Qs, QP, 16 * ib, 32 * ks), sf[ks], acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] *= __expf(lam[16 * ib + 4 * g + r]);
+                acc = mma(sf[ks], frag_rows_perm(Qs, QQ, 16 * ib, 32 * ks), acc);
+            acc *= __expf(lam[16 * ib + t]);
 #pragma unroll
             for (int js = 0; js <= ib / 2; ++js)
-                acc = mma(frag_rows_split(Ps[0], Ps[1], PP, 16 * ib, 32 * js),
-                          frag_cols(Vs, VP, cbase, 32 * js), acc);
-            store_tile<OT>(oh, O.st, 16 * ib, cbase, acc);
+                acc = mma(frag_cols(Vs, VP, cbase, 32 * js),
+                          frag_rows_split(Ps[0], Ps[1], PP, 16 * ib, 32 * js), acc);
+            store_tile_t<OT>(oh, O.st, 16 * ib, cbase, acc);
         }
 
         // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma)
@@ -458,10 +461,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         }
         const Split<T> a0 = split_tiles<T>(at[0], at[1]);
         const Split<T> a1 = split_tiles<T>(at[2], at[3]);
-        float rowg[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            rowg[r] = __expf(lam[16 * rb + 4 * g + r]);
+        // dQ^T tiles: lane (g,t) holds token 16rb + t
+        const float rowg = __expf(lam[16 * rb + t]);
 
         OT* out = dQ.head(b, h) + tok0 * dQ.st;
 #pragma unroll
@@ -470,15 +471,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             floatx4 acc = zero4();
 #pragma unroll
             for (int cs = 0; cs < DV / 32; ++cs)
-                acc = mma(frag_rows(dOs, VP, 16 * rb, 32 * cs),
-                          frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs), acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] *= rowg[r];
-            acc = mma(a0, frag_cols_perm(Ks, QP, 16 * fb, 0), acc);
+                acc = mma(frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs),
+                          frag_rows(dOs, VP, 16 * rb, 32 * cs), acc);
+            acc *= rowg;
+            acc = mma(frag_cols_perm(Ks, QP, 16 * fb, 0), a0, acc);
             if (rb >= 2)
-                acc = mma(a1, frag_cols_perm(Ks, QP, 16 * fb, 32), acc);
-            store_tile<OT>(out, dQ.st, 16 * rb, 16 * fb, acc);
+                acc = mma(frag_cols_perm(Ks, QP, 16 * fb, 32), a1, acc);
+            store_tile_t<OT>(out, dQ.st, 16 * rb, 16 * fb, acc);
         }
 
         float vf[2][8];
@@ -535,10 +534,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         }
         const Split<T> p0 = split_tiles<T>(pt[0], pt[1]), p1 = split_tiles<T>(pt[2], pt[3]);
         const Split<T> q0 = split_tiles<T>(atl[0], atl[1]), q1 = split_tiles<T>(atl[2], atl[3]);
-        float rowf[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            rowf[r] = __expf(lamC - lam[16 * rb + 4 * g + r]);
+        // dV^T and dK^T tiles: lane (g,t) holds token 16rb + t
+        const float rowf = __expf(lamC - lam[16 * rb + t]);
 
         OT* outv = dV.head(b, h) + tok0 * dV.st;
 #pragma unroll
@@ -547,15 +544,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             floatx4 acc = zero4();
 #pragma unroll
             for (int fs = 0; fs < DK / 32; ++fs)
-                acc = mma(frag_rows(Ks, QP, 16 * rb, 32 * fs),
-                          frag_rows_split(Ms[0], Ms[1], QP, 16 * cb, 32 * fs), acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] *= rowf[r];
+                acc = mma(frag_rows_split(Ms[0], Ms[1], QP, 16 * cb, 32 * fs),
+                          frag_rows(Ks, QP, 16 * rb, 32 * fs), acc);
+            acc *= rowf;
             if (rb < 2)
-                acc = mma(p0, frag_cols_perm(dOs, VP, 16 * cb, 0), acc);
-            acc = mma(p1, frag_cols_perm(dOs, VP, 16 * cb, 32), acc);
-            store_tile<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
+                acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 0), p0, acc);
+            acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 32), p1, acc);
+            store_tile_t<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
         }
         OT* outk = dK.head(b, h) + tok0 * dK.st;
 #pragma unroll
@@ -564,15 +559,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             floatx4 acc = zero4();
 #pragma unroll
             for (int cs = 0; cs < DV / 32; ++cs)
-                acc = mma(frag_rows(Vs, VP, 16 * rb, 32 * cs),
-                          frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs), acc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] *= rowf[r];
+                acc = mma(frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs),
+                          frag_rows(Vs, VP, 16 * rb, 32 * cs), acc);
+            acc *= rowf;
             if (rb < 2)
-                acc = mma(q0, frag_cols_perm(Qs, QP, 16 * fb, 0), acc);
-            acc = mma(q1, frag_cols_perm(Qs, QP, 16 * fb, 32), acc);
-            store_tile<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+                acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 0), q0, acc);
+            acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 32), q1, acc);
+            store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
         }
 
         // G_{n-1} = gamma_C G_n + Q^T (dO .* gamma)

@@ -63,9 +63,9 @@ def test_sizes():
     assert linrec.seq_states_bytes(d(T=8192), [2048, 4096, 2048]) == linrec.states_bytes(d(T=8192))
     assert linrec.seq_states_bytes(d(T=384), [64, 320]) == 16 * 3 * rec
     assert linrec.seq_states_bytes(d(T=384), [64, 300]) == 0
-    # two slots of the longest piece
+    # one piece's records, sized for the longest piece
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \
-        2 * linrec.states_bytes(d(T=4096))
+        linrec.states_bytes(d(T=4096))
     assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == linrec.states_bytes(d())
     for bad in (d(T=100), d(T=0), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
         assert linrec.states_bytes(bad) == 0

@@ -28,11 +28,13 @@ constexpr int CHUNK = 64;
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef bf16x4 __attribute__((address_space(3))) lds_bf16x4;
 // 16 raw bytes as a native vector (HIP's uint4 is a struct: copies of it
 // become memcpy calls that keep staging registers in private memory)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Decay description as the kernels see it (kind: 0 none, 1 per head, 2 per token).
 struct DecayArg {
@@ -58,7 +60,8 @@ template <typename T>
 struct Pad16 { static constexpr int value = 16 / sizeof(T); };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <typename T>
 struct Frag;
@@ -357,6 +360,86 @@ __device__ __forceinline__ float chunk_log_cumsum(const DecayArg& d, int b, int 
     return x;
 }
 
+// Per-chunk decay tables in LDS, indexed by token within the chunk:
+//   lam  chunk-local inclusive cumulative log-decay,
+//   G    gamma   = exp(lam),
+//   F    gamma_C / gamma = exp(lam_C - lam)   (in (0, 1]),
+//   E    gamma / gamma_C = exp(lam - lam_C)   (>= 1; clamped),
+// so that D_ij = exp(lam_i - lam_j) = E_i F_j.  The product form is used
+// only when the chunk's total log-decay lam_C is at least FACTOR_MIN_LOG,
+// which keeps E far from overflow; otherwise masks take one exp per entry.
+enum { TAB_LAM = 0, TAB_G = CHUNK, TAB_F = 2 * CHUNK, TAB_E = 3 * CHUNK, TAB_SIZE = 4 * CHUNK };
+constexpr float FACTOR_MIN_LOG = -40.f;
+
+// Fill the tables from decay_raw() values (token = lane); one full wave.
+__device__ __forceinline__ void decay_tables(const DecayArg& d, float raw, float* tab)
+{
+    const int l = lane_id();
+    const float lam = decay_log_cumsum(d, raw);
+    const float lamC = __shfl(lam, CHUNK - 1, 64);
+    tab[TAB_LAM + l] = lam;
+    tab[TAB_G + l] = __expf(lam);
+    tab[TAB_F + l] = __expf(lamC - lam);
+    tab[TAB_E + l] = __expf(fminf(lam - lamC, 80.f));
+}
+
+// Whether the chunk's masks may use the E F product (wave-uniform).
+__device__ __forceinline__ bool decay_factored(const float* tab)
+{
+    return __builtin_amdgcn_readfirstlane((int)(tab[TAB_LAM + CHUNK - 1] >= FACTOR_MIN_LOG)) != 0;
+}
+
+// Causal decay mask of a 16x16 score tile in result layout (lane (g,t)
+// holds rows rbase + 4g + r, column cbase + t).  LATER_ROWS: the rows are
+// the later token i and the column the earlier token j, else the reverse.
+// Entries with j > i become 0, the others are multiplied by D_ij.
+template <bool LATER_ROWS>
+__device__ __forceinline__ floatx4 decay_mask(floatx4 x, const float* tab, int rbase, int cbase,
+                                              bool factored)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const int c = cbase + t;
+    floatx4 y;
+    if (factored) {
+        const floatx4 rv =
+            *reinterpret_cast<const floatx4*>(tab + (LATER_ROWS ? TAB_E : TAB_F) + rbase + 4 * g);
+        const float cv = tab[(LATER_ROWS ? TAB_F : TAB_E) + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = rbase + 4 * g + r;
+            const bool keep = LATER_ROWS ? rr >= c : rr <= c;
+            y[r] = keep ? x[r] * (rv[r] * cv) : 0.f;
+        }
+    } else {
+        const floatx4 rl = *reinterpret_cast<const floatx4*>(tab + TAB_LAM + rbase + 4 * g);
+        const float cl = tab[TAB_LAM + c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = rbase + 4 * g + r;
+            const bool keep = LATER_ROWS ? rr >= c : rr <= c;
+            y[r] = keep ? x[r] * __expf(LATER_ROWS ? rl[r] - cl : cl - rl[r]) : 0.f;
+        }
+    }
+    return y;
+}
+
+// Per-lane factors for the k-slots of a frag_cols() read over tokens (slot
+// r of k32 step ks is token 32ks + 8g + r), from one decay table.
+__device__ __forceinline__ void slot_factors(const float* table, float (&f)[2][8])
+{
+    const int g = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(table + 32 * ks + 8 * g);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(table + 32 * ks + 8 * g + 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f[ks][r] = a[r];
+            f[ks][4 + r] = b[r];
+        }
+    }
+}
+
 // ---- split operands ---------------------------------------------------------
 //
 // A computed MFMA operand (P, the decay-scaled K or Q, a carried state) is
@@ -376,19 +459,32 @@ struct Split<float> {
     Frag<float> hi;
 };
 
+// hi = x with its low 16 mantissa bits cleared (exactly the upper half of
+// the fp32 pattern, so a bf16 by truncation), lo = bf16(x - hi) rounded to
+// nearest even; x - hi is exact, and hi + lo carries ~16 significant bits.
+// Two values at a time: hi and lo each come back as one packed bf16 pair.
+// Returns {hi pair, lo pair}.
+__device__ __forceinline__ u32x2 split2(float x0, float x1)
+{
+    const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+    const float r0 = x0 - __uint_as_float(b0 & 0xffff0000u);
+    const float r1 = x1 - __uint_as_float(b1 & 0xffff0000u);
+    const bf16x2 l = {(bf16)r0, (bf16)r1};
+    return u32x2{(b1 & 0xffff0000u) | (b0 >> 16), __builtin_bit_cast(uint32_t, l)};
+}
+
 template <typename T>
 __device__ __forceinline__ Split<T> split8(const float (&x)[8]);
 
 template <>
 __device__ __forceinline__ Split<bf16> split8<bf16>(const float (&x)[8])
 {
+    const u32x2 p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
+    const u32x2 p2 = split2(x[4], x[5]), p3 = split2(x[6], x[7]);
+    const u32x4 h = {p0.x, p1.x, p2.x, p3.x}, l = {p0.y, p1.y, p2.y, p3.y};
     Split<bf16> s;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const bf16 h = (bf16)x[r];
-        s.hi.v[r] = h;
-        s.lo.v[r] = (bf16)(x[r] - (float)h);
-    }
+    s.hi.v = __builtin_bit_cast(bf16x8, h);
+    s.lo.v = __builtin_bit_cast(bf16x8, l);
     return s;
 }
 
@@ -439,15 +535,6 @@ __device__ __forceinline__ Split<T> split_scaled(const Frag<T>& f, const float (
     return split8<T>(x);
 }
 
-// Write x into an LDS plane pair: hi[idx] and (bf16 only) lo[idx].
-template <typename T>
-__device__ __forceinline__ void put_split(T* hi, T* lo, int idx, float x)
-{
-    const T h = (T)x;
-    hi[idx] = h;
-    if constexpr (sizeof(T) == 2)
-        lo[idx] = (T)(x - (float)h);
-}
 
 // Split fragments read from LDS plane pairs.
 template <typename T>
@@ -501,16 +588,11 @@ template <typename T>
 __device__ __forceinline__ void put_split4(T* hi, T* lo, int idx, const floatx4& x)
 {
     if constexpr (sizeof(T) == 2) {
-        bf16x4 h, l;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            h[r] = (bf16)x[r];
-            l[r] = (bf16)(x[r] - (float)h[r]);
-        }
-        *reinterpret_cast<bf16x4*>(hi + idx) = h;
-        *reinterpret_cast<bf16x4*>(lo + idx) = l;
+        const u32x2 p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
+        *reinterpret_cast<u32x2*>(hi + idx) = u32x2{p0.x, p1.x};
+        *reinterpret_cast<u32x2*>(lo + idx) = u32x2{p0.y, p1.y};
     } else {
-        *reinterpret_cast<float4*>(hi + idx) = float4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<floatx4*>(hi + idx) = x;
     }
 }
 

@@ -45,22 +45,6 @@ namespace linrec {
 // Shared pieces of the segment kernels.
 // ---------------------------------------------------------------------------
 
-// Per-lane decay factors of a chunk for the k-slots of a frag_cols() read
-// over tokens (slot r of k32 step ks is token 32ks + 8g + r):
-// gamma_C / gamma_j when `towards_end`, else gamma_j.
-__device__ __forceinline__ void slot_factors(const float* lam, float lamC, bool towards_end,
-                                             float (&f)[2][8])
-{
-    const int g = lane_id() >> 4;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float lj = lam[32 * ks + 8 * g + r];
-            f[ks][r] = towards_end ? __expf(lamC - lj) : __expf(lj);
-        }
-}
-
 // carry[fb][cbl] (rows f = 16fb + 4g + r, column cbase0 + 16cbl + t) <-
 // gamma_C carry + X^T (Y .* yf) over the chunk: X (rows = tokens, d_k wide)
 // exact, Y (rows = tokens) scaled per token by yf and split.  The per-token
@@ -161,10 +145,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     constexpr int64_t REC = seg_record_floats(DK, DV);
     __shared__ __align__(16) T Xs[CHUNK * XP];
     __shared__ __align__(16) T Ys[CHUNK * YP];
-    __shared__ float lam[CHUNK];
+    __shared__ __align__(16) float tab[TAB_SIZE];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int w = wave_id(), l = lane_id();
+    const int w = wave_id();
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
     const int n0 = s * m, n1 = min(n0 + m, N), cnt = n1 - n0;
@@ -187,7 +171,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
         chunk_store(rx, Xs, XP);
         chunk_store(ry, Ys, YP);
         if (w == 0)
-            lam[l] = decay_log_cumsum(dec, ra);
+            decay_tables(dec, ra, tab);
         __syncthreads();
         if (it + 1 < cnt) {
             n = REVERSE ? n1 - 2 - it : n0 + 1 + it;
@@ -196,11 +180,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
             chunk_load(ry, yh + tn * Y.st, Y.st);
             ra = decay_raw(dec, b, h, tn);
         }
-        const float lamC = lam[CHUNK - 1];
-        seg_log += lamC;
+        seg_log += tab[TAB_LAM + CHUNK - 1];
         float yf[2][8];
-        slot_factors(lam, lamC, !REVERSE, yf);
-        state_update<T, DK, 1>(U, Xs, XP, Ys, YP, cbase, __expf(lamC), yf);
+        slot_factors(tab + (REVERSE ? TAB_G : TAB_F), yf);
+        state_update<T, DK, 1>(U, Xs, XP, Ys, YP, cbase, tab[TAB_G + CHUNK - 1], yf);
         __syncthreads();
     }
 
@@ -275,7 +258,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T Ps[2][CHUNK * PP];
-    __shared__ float lam[CHUNK];
+    __shared__ __align__(16) float tab[TAB_SIZE];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
@@ -306,7 +289,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
         chunk_store(rk, Ks, QP);
         chunk_store(rv, Vs, VP);
         if (w == 0)
-            lam[l] = decay_log_cumsum(dec, ra);
+            decay_tables(dec, ra, tab);
         __syncthreads();
         if (n + 1 < n1) {
             const int64_t tn = (int64_t)(n + 1) * CHUNK;
@@ -315,22 +298,20 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             chunk_load(rv, vh + tn * V.st, V.st);
             ra = decay_raw(dec, b, h, tn);
         }
-        const float lamC = lam[CHUNK - 1];
+        const bool fac = decay_factored(tab);
 
+        // P^T tiles (rows = earlier tokens j, columns = later tokens i), so
+        // each lane writes four consecutive j of one row i of P
 #pragma unroll
         for (int jb = jb0; jb < 4; jb += jstep) {
             floatx4 acc = zero4();
             if (jb <= ib_p) {
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mma(frag_rows(Qs, QQ, 16 * ib_p, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
+                    acc = mma(frag_rows(Ks, QP, 16 * jb, 32 * ks), frag_rows(Qs, QQ, 16 * ib_p, 32 * ks), acc);
+                acc = decay_mask<false>(acc, tab, 16 * jb, 16 * ib_p, fac);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * ib_p + 4 * g + r, j = 16 * jb + t;
-                const float val = (j <= i) ? acc[r] * __expf(lam[i] - lam[j]) : 0.f;
-                put_split(Ps[0], Ps[1], i * PP + j, val);
-            }
+            put_split4(Ps[0], Ps[1], (16 * ib_p + t) * PP + 16 * jb + 4 * g, acc);
         }
         // S_{n-1} as split B fragments (k = f in frag_rows_perm order)
         Split<T> sf[DK / 32];
@@ -348,7 +329,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
                 acc = mma(sf[ks], frag_rows_perm(Qs, QQ, 16 * ib, 32 * ks), acc);
-            acc *= __expf(lam[16 * ib + t]);
+            acc *= tab[TAB_G + 16 * ib + t];
 #pragma unroll
             for (int js = 0; js <= ib / 2; ++js)
                 acc = mma(frag_cols(Vs, VP, cbase, 32 * js),
@@ -358,31 +339,34 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 
         // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma)
         float vf[2][8];
-        slot_factors(lam, lamC, true, vf);
-        state_update<T, DK, 1>(S, Ks, QP, Vs, VP, cbase, __expf(lamC), vf);
+        slot_factors(tab + TAB_F, vf);
+        state_update<T, DK, 1>(S, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
 // Backward segment kernel.  Workgroup = (b, h, segment), one wave per 16
-// columns of d_v (8 waves at d_v = 128).  Wave w owns state/gradient columns
-// [16w, 16w + 16), row block rb = w % 4 of the outputs and, with 8 waves,
-// half w / 4 of their columns.
+// columns of d_v (8 waves at d_v = 128).  Wave w carries state/gradient
+// columns [16w, 16w + 16) and works on row block rb = w % 4 of the outputs;
+// with 8 waves, half w / 4 selects what else it does.
 //   Walk 1 (chunks in order, S carried from the stored segment state):
-//   S_{n-1} goes to LDS (split) and
-//       dQ = gamma .* (dO S_{n-1}^T) + A K,   A = (dO V^T) .* D  (rows rb),
+//   S_{n-1} goes to LDS (split) and, for rows rb and the half's columns,
+//       dQ = gamma .* (dO S_{n-1}^T) + A K,   A = (dO V^T) .* D,
 //   then S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma).
 //   Walk 2 (chunks in reverse, G carried from the stored segment gradient):
-//   G_n goes to LDS (split) and, for rows rb,
+//   G_n goes to LDS (split); for rows rb, the first half computes
 //       dV = gamma_C/gamma .* (K G_n) + P^T dO,   P = (Q K^T) .* D,
-//       dK = gamma_C/gamma .* (V G_n^T) + A^T Q,
-//   then G_{n-1} = gamma_C G_n + Q^T (dO .* gamma).
+//   and the second half
+//       dK = gamma_C/gamma .* (V G_n^T) + A^T Q
+//   (with 4 waves, every wave does both); then
+//   G_{n-1} = gamma_C G_n + Q^T (dO .* gamma).
 // P and A are built per wave in registers in the orientation their product
-// needs and used as split A operands directly (k-slot order of the
-// frag_cols_perm reads of the other operand).  The next chunk's rows load
-// while this one computes; walk 2 starts on walk 1's last chunk, whose K, V,
-// dO and decays are still in LDS, so only Q is loaded for it.
+// needs and used as split B operands directly (k-slot order of the
+// frag_cols_perm reads of the other operand); outputs are computed
+// transposed (one vector store per lane and tile).  The next chunk's rows
+// load while this one computes; walk 2 starts on walk 1's last chunk, whose
+// K, V, dO and decay tables are still in LDS, so only Q is loaded for it.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
@@ -393,19 +377,19 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, VP = DV + PAD;
-    constexpr int FBW = (DK / 16) / NH, CBW = (DV / 16) / NH;   // output blocks per wave
+    constexpr int FBW = (DK / 16) / NH;   // walk-1 dQ blocks per wave
     __shared__ __align__(16) T Qs[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T dOs[CHUNK * VP];
     __shared__ __align__(16) T Ms[2][DV * QP];     // state / gradient, [c][f], split
-    __shared__ float lam[CHUNK];
+    __shared__ __align__(16) float tab[TAB_SIZE];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
+    const int w = wave_id(), l = lane_id(), t = l & 15;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
-    const int rb = w % 4, fb0 = (w / 4) * FBW, cb0 = (w / 4) * CBW;
+    const int rb = w % 4, half = w / 4, fb0 = half * FBW;
     const int n0 = s * m, n1 = min(n0 + m, N);
 
     floatx4 C[DK / 16][1];   // carried state (walk 1) / gradient (walk 2)
@@ -429,7 +413,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         chunk_store(rv, Vs, VP);
         chunk_store(rdo, dOs, VP);
         if (w == 0)
-            lam[l] = decay_log_cumsum(dec, ra);
+            decay_tables(dec, ra, tab);
         put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
         __syncthreads();
         if (n + 1 < n1) {
@@ -441,7 +425,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         } else {
             chunk_load(rq, qh + tok0 * Q.st, Q.st);
         }
-        const float lamC = lam[CHUNK - 1];
+        const bool fac = decay_factored(tab);
 
         // A^T tiles of row block rb: T[j][i] = (v_j . dO_i) D_ij, j-block jb
         floatx4 at[4];
@@ -452,17 +436,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
 #pragma unroll
                 for (int cs = 0; cs < DV / 32; ++cs)
                     at[jb] = mma(frag_rows(Vs, VP, 16 * jb, 32 * cs), frag_rows(dOs, VP, 16 * rb, 32 * cs), at[jb]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * jb + 4 * g + r, i = 16 * rb + t;
-                    at[jb][r] = (j <= i) ? at[jb][r] * __expf(lam[i] - lam[j]) : 0.f;
-                }
+                at[jb] = decay_mask<false>(at[jb], tab, 16 * jb, 16 * rb, fac);
             }
         }
         const Split<T> a0 = split_tiles<T>(at[0], at[1]);
         const Split<T> a1 = split_tiles<T>(at[2], at[3]);
         // dQ^T tiles: lane (g,t) holds token 16rb + t
-        const float rowg = __expf(lam[16 * rb + t]);
+        const float rowg = tab[TAB_G + 16 * rb + t];
 
         OT* out = dQ.head(b, h) + tok0 * dQ.st;
 #pragma unroll
@@ -481,8 +461,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         }
 
         float vf[2][8];
-        slot_factors(lam, lamC, true, vf);
-        state_update<T, DK, 1>(C, Ks, QP, Vs, VP, cbase, __expf(lamC), vf);
+        slot_factors(tab + TAB_F, vf);
+        state_update<T, DK, 1>(C, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
         __syncthreads();
     }
 
@@ -496,7 +476,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             chunk_store(rv, Vs, VP);
             chunk_store(rdo, dOs, VP);
             if (w == 0)
-                lam[l] = decay_log_cumsum(dec, ra);
+                decay_tables(dec, ra, tab);
         }
         put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
         __syncthreads();
@@ -508,70 +488,73 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             chunk_load(rdo, doh + tn * dO.st, dO.st);
             ra = decay_raw(dec, b, h, tn);
         }
-        const float lamC = lam[CHUNK - 1];
+        const bool fac = decay_factored(tab);
+        // dV^T and dK^T tiles: lane (g,t) holds token 16rb + t
+        const float rowf = tab[TAB_F + 16 * rb + t];
 
-        // P and A tiles of column block rb: rows i (i-block ib), column j = 16rb + t
-        floatx4 pt[4], atl[4];
+        if (NH == 1 || half == 0) {
+            // P tiles of column block rb: rows i (i-block ib), column j = 16rb + t
+            floatx4 pt[4];
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            pt[ib] = zero4();
-            atl[ib] = zero4();
-            if (ib >= rb) {
+            for (int ib = 0; ib < 4; ++ib) {
+                pt[ib] = zero4();
+                if (ib >= rb) {
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks)
-                    pt[ib] = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * rb, 32 * ks), pt[ib]);
-#pragma unroll
-                for (int cs = 0; cs < DV / 32; ++cs)
-                    atl[ib] = mma(frag_rows(dOs, VP, 16 * ib, 32 * cs), frag_rows(Vs, VP, 16 * rb, 32 * cs), atl[ib]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * ib + 4 * g + r, j = 16 * rb + t;
-                    const float d = (i >= j) ? __expf(lam[i] - lam[j]) : 0.f;
-                    pt[ib][r] *= d;
-                    atl[ib][r] *= d;
+                    for (int ks = 0; ks < DK / 32; ++ks)
+                        pt[ib] = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * rb, 32 * ks), pt[ib]);
+                    pt[ib] = decay_mask<true>(pt[ib], tab, 16 * ib, 16 * rb, fac);
                 }
             }
+            const Split<T> p0 = split_tiles<T>(pt[0], pt[1]), p1 = split_tiles<T>(pt[2], pt[3]);
+            OT* outv = dV.head(b, h) + tok0 * dV.st;
+#pragma unroll
+            for (int cb = 0; cb < DV / 16; ++cb) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int fs = 0; fs < DK / 32; ++fs)
+                    acc = mma(frag_rows_split(Ms[0], Ms[1], QP, 16 * cb, 32 * fs),
+                              frag_rows(Ks, QP, 16 * rb, 32 * fs), acc);
+                acc *= rowf;
+                if (rb < 2)
+                    acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 0), p0, acc);
+                acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 32), p1, acc);
+                store_tile_t<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
+            }
         }
-        const Split<T> p0 = split_tiles<T>(pt[0], pt[1]), p1 = split_tiles<T>(pt[2], pt[3]);
-        const Split<T> q0 = split_tiles<T>(atl[0], atl[1]), q1 = split_tiles<T>(atl[2], atl[3]);
-        // dV^T and dK^T tiles: lane (g,t) holds token 16rb + t
-        const float rowf = __expf(lamC - lam[16 * rb + t]);
-
-        OT* outv = dV.head(b, h) + tok0 * dV.st;
+        if (NH == 1 || half == 1) {
+            // A tiles of column block rb: rows i, column j = 16rb + t
+            floatx4 atl[4];
 #pragma unroll
-        for (int cbi = 0; cbi < CBW; ++cbi) {
-            const int cb = cb0 + cbi;
-            floatx4 acc = zero4();
+            for (int ib = 0; ib < 4; ++ib) {
+                atl[ib] = zero4();
+                if (ib >= rb) {
 #pragma unroll
-            for (int fs = 0; fs < DK / 32; ++fs)
-                acc = mma(frag_rows_split(Ms[0], Ms[1], QP, 16 * cb, 32 * fs),
-                          frag_rows(Ks, QP, 16 * rb, 32 * fs), acc);
-            acc *= rowf;
-            if (rb < 2)
-                acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 0), p0, acc);
-            acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 32), p1, acc);
-            store_tile_t<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
-        }
-        OT* outk = dK.head(b, h) + tok0 * dK.st;
+                    for (int cs = 0; cs < DV / 32; ++cs)
+                        atl[ib] = mma(frag_rows(dOs, VP, 16 * ib, 32 * cs), frag_rows(Vs, VP, 16 * rb, 32 * cs), atl[ib]);
+                    atl[ib] = decay_mask<true>(atl[ib], tab, 16 * ib, 16 * rb, fac);
+                }
+            }
+            const Split<T> q0 = split_tiles<T>(atl[0], atl[1]), q1 = split_tiles<T>(atl[2], atl[3]);
+            OT* outk = dK.head(b, h) + tok0 * dK.st;
 #pragma unroll
-        for (int fbi = 0; fbi < FBW; ++fbi) {
-            const int fb = fb0 + fbi;
-            floatx4 acc = zero4();
+            for (int fb = 0; fb < DK / 16; ++fb) {
+                floatx4 acc = zero4();
 #pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs)
-                acc = mma(frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs),
-                          frag_rows(Vs, VP, 16 * rb, 32 * cs), acc);
-            acc *= rowf;
-            if (rb < 2)
-                acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 0), q0, acc);
-            acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 32), q1, acc);
-            store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+                for (int cs = 0; cs < DV / 32; ++cs)
+                    acc = mma(frag_cols_split(Ms[0], Ms[1], QP, 16 * fb, 32 * cs),
+                              frag_rows(Vs, VP, 16 * rb, 32 * cs), acc);
+                acc *= rowf;
+                if (rb < 2)
+                    acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 0), q0, acc);
+                acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 32), q1, acc);
+                store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+            }
         }
 
         // G_{n-1} = gamma_C G_n + Q^T (dO .* gamma)
         float of[2][8];
-        slot_factors(lam, lamC, false, of);
-        state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, __expf(lamC), of);
+        slot_factors(tab + TAB_G, of);
+        state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, tab[TAB_G + CHUNK - 1], of);
         __syncthreads();
     }
 }

@@ -179,6 +179,31 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d,
                          linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
                          float* dS_in, void* workspace, void* stream);
 
+/* Bytes of workspace linrec_bwd_recompute needs (0 if `d` is invalid): the
+ * piece's rebuilt state records, its gradient records and one fp32 state
+ * of scratch, 2 * linrec_states_bytes(d) + B*H*d_k*d_v*4.  It depends on
+ * the piece length only. */
+size_t linrec_bwd_recompute_workspace_bytes(const linrec_desc* d);
+
+/* Backward over one piece without states kept from the forward: the states
+ * entering every segment are rebuilt from S_in, the boundary state the
+ * piece's forward started from, by the forward state transition (one more
+ * read of k and v), then the backward runs as linrec_bwd.  A caller of the
+ * sequence accumulation then keeps one boundary state per piece instead of
+ * the pieces' state records, so its memory does not grow with the sequence
+ * (activation recomputation: the gptget summary of StateFlow, "Key
+ * results"; constant memory in sequence length: Sequence Accumulation and
+ * Beyond, "Key results").
+ *   S_in: fp32 [B,H,d_k,d_v] or NULL (zeros).  Other arguments as
+ *   linrec_bwd; workspace: linrec_bwd_recompute_workspace_bytes(d) bytes.
+ * Results equal linrec_bwd's bit for bit. */
+linrec_status linrec_bwd_recompute(linrec_ctx* ctx, const linrec_desc* d,
+                                   linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                                   linrec_tensor decay, const float* S_in,
+                                   linrec_tensor dO, const float* dS_out,
+                                   linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                   float* dS_in, void* workspace, void* stream);
+
 /* Sequence accumulation over `npieces` consecutive pieces of the sequence
  * described by `d` (d->T = total tokens; lengths[i] % 64 == 0, sum = T;
  * lengths is host memory).  Piece i is processed as its own sub-sequence,

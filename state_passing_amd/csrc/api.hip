@@ -491,6 +491,13 @@ size_t linrec_states_bytes(const linrec_desc* d)
 
 size_t linrec_bwd_workspace_bytes(const linrec_desc* d) { return linrec_states_bytes(d); }
 
+size_t linrec_bwd_recompute_workspace_bytes(const linrec_desc* d)
+{
+    if (check_desc(d) != LINREC_OK)
+        return 0;
+    return 2 * linrec_states_bytes(d) + (size_t)d->B * d->H * d->dk * d->dv * sizeof(float);
+}
+
 size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
@@ -538,6 +545,34 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     const BwdIntraLaunch in =
         bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, workspace);
     LAUNCH_SCAN(ctx, sc, s);
+    LAUNCH_BWD_INTRA(ctx, in, s);
+    return LINREC_OK;
+}
+
+linrec_status linrec_bwd_recompute(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                                   linrec_tensor k, linrec_tensor v, linrec_tensor decay,
+                                   const float* S_in, linrec_tensor dO, const float* dS_out,
+                                   linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                   float* dS_in, void* workspace, void* stream)
+{
+    // workspace: [state records | gradient records | one scratch state]
+    linrec_status st = check_bwd_args(d, q, k, v, decay, workspace, dO, dS_out, dq, dk, dv,
+                                      dS_in, workspace);
+    if (st != LINREC_OK || (st = check_state_ptr(S_in, false)) != LINREC_OK ||
+        (st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ns = nseg_of(d->T);
+    char* ws = (char*)workspace;
+    void* states = ws;
+    void* grads = ws + linrec_states_bytes(d);
+    float* scratch = (float*)(ws + 2 * linrec_states_bytes(d));
+    const ScanLaunch fsc = fwd_scan_of(d, k, v, decay, 0, d->T, S_in, scratch, states, 0, ns);
+    const ScanLaunch bsc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, grads);
+    const BwdIntraLaunch in =
+        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, grads);
+    LAUNCH_SCAN(ctx, fsc, s);
+    LAUNCH_SCAN(ctx, bsc, s);
     LAUNCH_BWD_INTRA(ctx, in, s);
     return LINREC_OK;
 }

@@ -38,7 +38,7 @@ EXPORTS = (
     "linrec_bwd_workspace_bytes", "linrec_fwd", "linrec_bwd", "linrec_fwd_seq",
     "linrec_bwd_seq_workspace_bytes", "linrec_bwd_seq", "linrec_status_str",
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
-    "linrec_ctx_kernel_times",
+    "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
@@ -87,6 +87,8 @@ def _lib():
         "linrec_seq_states_bytes": ([D, I32, P], ctypes.c_size_t),
         "linrec_fwd": ([P, D, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
+        "linrec_bwd_recompute_workspace_bytes": ([D], ctypes.c_size_t),
+        "linrec_bwd_recompute": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -270,6 +272,34 @@ def bwd(q, k, v, decay, states, dO, dS_out=None, *, dq=None, dk=None, dv=None,
                            dec, _ptr(states), _act(dO), _ptr(dS_out), _act(dq), _act(dk),
                            _act(dv), _ptr(dS_in), _ptr(workspace), _stream(q.device))
     _check(rc, "linrec_bwd")
+    return dq, dk, dv, dS_in
+
+
+def bwd_recompute_workspace_bytes(d: Desc) -> int:
+    return int(_lib().linrec_bwd_recompute_workspace_bytes(ctypes.byref(d)))
+
+
+def bwd_recompute(q, k, v, decay, S_in, dO, dS_out=None, *, dq=None, dk=None, dv=None,
+                  dS_in=None, workspace=None, out_dtype=None):
+    """Backward over one piece from its boundary state S_in alone (the
+    per-segment states are rebuilt).  Returns (dq, dk, dv, dS_in)."""
+    kind, dec = _decay(decay)
+    odt = _out_dtype(q, out_dtype, dq)
+    d = _desc_of(q, v, kind, odt)
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    dS_in = _state_out(q, B, H, DK, DV, dS_in)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_recompute_workspace_bytes(d), 16), dtype=torch.uint8,
+                                device=q.device)
+    rc = _lib().linrec_bwd_recompute(context(q.device.index), ctypes.byref(d), _act(q), _act(k),
+                                     _act(v), dec, _ptr(S_in), _act(dO), _ptr(dS_out), _act(dq),
+                                     _act(dk), _act(dv), _ptr(dS_in), _ptr(workspace),
+                                     _stream(q.device))
+    _check(rc, "linrec_bwd_recompute")
     return dq, dk, dv, dS_in
 
 

@@ -91,6 +91,13 @@ def call_bwd(desc, dq=None, workspace=FAKE, dS_in=FAKE, states=FAKE, ctx=None):
                           dq or act(), act(), act(), dS_in, workspace, None)
 
 
+def call_bwd_recompute(desc, S_in=None, workspace=FAKE, dS_in=FAKE, ctx=None):
+    lib = linrec._lib()
+    return lib.linrec_bwd_recompute(ctx, ctypes.byref(desc), act(), act(), act(),
+                                    linrec.Tensor(FAKE, 0, 1, 0), S_in, act(), None,
+                                    act(), act(), act(), dS_in, workspace, None)
+
+
 E = {v: k for k, v in linrec.STATUS.items()}
 
 
@@ -137,6 +144,23 @@ def test_valid_arguments_stop_at_missing_context():
     # every argument check passes; the NULL context is the first thing rejected
     assert call_fwd(d()) == E["LINREC_E_NULL"]
     assert call_bwd(d()) == E["LINREC_E_NULL"]
+    assert call_bwd_recompute(d()) == E["LINREC_E_NULL"]
+    assert call_bwd_recompute(d(), S_in=FAKE) == E["LINREC_E_NULL"]
+
+
+def test_recompute_arguments():
+    good = d()
+    rec = (128 * 128 + 64) * 4
+    # two record sets of the piece plus one fp32 state of scratch
+    assert linrec.bwd_recompute_workspace_bytes(good) == 2 * 16 * 16 * rec + 16 * 128 * 128 * 4
+    assert linrec.bwd_recompute_workspace_bytes(d(T=8192)) == \
+        2 * linrec.states_bytes(d(T=8192)) + 16 * 128 * 128 * 4
+    assert linrec.bwd_recompute_workspace_bytes(d(T=100)) == 0
+    assert call_bwd_recompute(d(T=100)) == E["LINREC_E_SHAPE"]
+    assert call_bwd_recompute(good, workspace=None) == E["LINREC_E_WORKSPACE"]
+    assert call_bwd_recompute(good, workspace=FAKE + 8) == E["LINREC_E_WORKSPACE"]
+    assert call_bwd_recompute(good, S_in=FAKE + 2) == E["LINREC_E_ALIGN"]
+    assert call_bwd_recompute(good, dS_in=None) == E["LINREC_E_NULL"]
 
 
 def test_bad_piece_lists():

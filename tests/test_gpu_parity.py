@@ -123,6 +123,57 @@ def test_small_split_matches_oracle_and_unsplit(wl):
                 assert all(same.values()), same
 
 
+RECOMPUTE_CASES = [SMALL[1], SMALL[4], SMALL[6], SMALL[9]]
+
+
+@pytest.mark.parametrize("wl", RECOMPUTE_CASES, ids=[w.name for w in RECOMPUTE_CASES])
+def test_recompute_equals_stored_states(wl):
+    """The backward that rebuilds the segment states from S_in gives the
+    backward over stored states bit for bit."""
+    inp = gpu_inputs(wl)
+    o, S_out, st = linrec.fwd(inp.q, inp.k, inp.v, inp.decay, inp.S_in)
+    ref = linrec.bwd(inp.q, inp.k, inp.v, inp.decay, st, inp.dO, inp.dS_out)
+    got = linrec.bwd_recompute(inp.q, inp.k, inp.v, inp.decay, inp.S_in, inp.dO, inp.dS_out)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dS_in"), got, ref):
+        assert torch.equal(a, b), name
+
+
+def test_recompute_sequence_keeps_boundary_states_only():
+    """Sequence accumulation that keeps one boundary state per piece: the
+    forward reuses one state store, the backward rebuilds each piece's
+    states; results against the oracle."""
+    wl = SMALL[9]
+    inp = gpu_inputs(wl)
+    ref = oracle_run(inp)
+    lengths = [256, 768, 512, 768]
+    bounds = np.cumsum([0] + lengths)
+    q, k, v, dO = inp.q, inp.k, inp.v, inp.dO
+    o = torch.empty(v.shape, dtype=torch.float32, device=DEV)
+    store = torch.empty(linrec.states_bytes(linrec.desc(wl.B, wl.H, max(lengths), wl.dk, wl.dv,
+                                                        linrec.BF16, linrec.DECAY_TOKEN)),
+                        dtype=torch.uint8, device=DEV)
+    S = inp.S_in
+    boundary = []
+    for i, L in enumerate(lengths):
+        sl = slice(int(bounds[i]), int(bounds[i + 1]))
+        boundary.append(S)
+        pd = linrec.desc(wl.B, wl.H, L, wl.dk, wl.dv, linrec.BF16, linrec.DECAY_TOKEN)
+        _, S, _ = linrec.fwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], inp.decay[:, :, sl], S,
+                             o=o[:, :, sl], states=store[:linrec.states_bytes(pd)])
+    S_out = S
+    dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device=DEV) for x in (q, k, v))
+    dS = inp.dS_out
+    for i in reversed(range(len(lengths))):
+        sl = slice(int(bounds[i]), int(bounds[i + 1]))
+        _, _, _, dS = linrec.bwd_recompute(q[:, :, sl], k[:, :, sl], v[:, :, sl],
+                                           inp.decay[:, :, sl], boundary[i], dO[:, :, sl], dS,
+                                           dq=dq[:, :, sl], dk=dk[:, :, sl], dv=dv[:, :, sl])
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    check(dict(o=o, S_out=S_out, dq=dq, dk=dk, dv=dv, dS_in=dS), ref, heads, wl, "recompute-seq")
+
+
 def test_deterministic_run_to_run():
     wl = SMALL[1]
     inp = gpu_inputs(wl)

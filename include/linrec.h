@@ -204,6 +204,37 @@ linrec_status linrec_bwd_recompute(linrec_ctx* ctx, const linrec_desc* d,
                                    linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
                                    float* dS_in, void* workspace, void* stream);
 
+/* Bytes of workspace linrec_bwd_da needs (0 if `d` is invalid): the
+ * gradient records of linrec_bwd plus one fp32 total per segment. */
+size_t linrec_bwd_da_workspace_bytes(const linrec_desc* d);
+
+/* linrec_bwd plus the gradient of the loss with respect to the decay, for
+ * trained gates.  With g_t = q_t . dq_t - k_t . dk_t (the gradient with
+ * respect to the cumulative log-decay at token t), the log-decay of token r
+ * has gradient sum_{t >= r} g_t over the rest of the sequence, and
+ *   da[r] = (sum_{t >= r in this piece} g_t + da_carry_in) / a_r.
+ * da_carry_in is that sum over everything after the piece, which equals
+ * <dS_out, S_out>: in a reverse loop over pieces it is the next piece's
+ * da_carry_out, and after the last piece it is <dS_out, S_out> of the whole
+ * sequence (0 when dS_out = 0).  NULL means 0.
+ *   da: fp32 [B,H,T] (strides in elements, like a per-token decay), one
+ *       value per token for per-token and per-head decay alike (the
+ *       gradient of a per-head decay is the sum over tokens);
+ *   da_carry_out: fp32 [B,H], required; may alias da_carry_in.
+ *   d->decay must not be LINREC_DECAY_NONE (LINREC_E_LAYOUT).
+ *   workspace: linrec_bwd_da_workspace_bytes(d) bytes.
+ * dq, dk, dv and dS_in equal linrec_bwd's bit for bit.  g_t is formed from
+ * the fp32 dq and dk before they are rounded to the output dtype.
+ * Reference: gated (per-token) decay in the recurrences StateFlow trains
+ * (the gptget summary, "Experimental design"). */
+linrec_status linrec_bwd_da(linrec_ctx* ctx, const linrec_desc* d,
+                            linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                            linrec_tensor decay, const void* states,
+                            linrec_tensor dO, const float* dS_out,
+                            linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                            float* dS_in, linrec_tensor da, const float* da_carry_in,
+                            float* da_carry_out, void* workspace, void* stream);
+
 /* Sequence accumulation over `npieces` consecutive pieces of the sequence
  * described by `d` (d->T = total tokens; lengths[i] % 64 == 0, sum = T;
  * lengths is host memory).  Piece i is processed as its own sub-sequence,
@@ -247,7 +278,8 @@ enum {
     LINREC_KERNEL_BWD_SUM = 3,    /* reverse segment sums (parallel)           */
     LINREC_KERNEL_BWD_FOLD = 4,   /* reverse fold across segments (dS carried) */
     LINREC_KERNEL_BWD_SEG = 5,    /* backward segment kernel: dQ, dK, dV       */
-    LINREC_KERNEL_KINDS = 6
+    LINREC_KERNEL_DA_FINISH = 6,  /* decay gradient, last step                 */
+    LINREC_KERNEL_KINDS = 7
 };
 
 /* Per-kernel timing (instrumentation, off by default).  While enabled, every

@@ -14,6 +14,7 @@
 #include "linrec.h"
 
 using linrec::BwdIntraLaunch;
+using linrec::DaFinishLaunch;
 using linrec::FwdIntraLaunch;
 using linrec::ScanLaunch;
 using linrec::TensorArg;
@@ -498,6 +499,20 @@ size_t linrec_bwd_recompute_workspace_bytes(const linrec_desc* d)
     return 2 * linrec_states_bytes(d) + (size_t)d->B * d->H * d->dk * d->dv * sizeof(float);
 }
 
+// Per-segment totals of the decay gradient, after the gradient records.
+size_t da_tot_bytes(const linrec_desc* d)
+{
+    const size_t raw = (size_t)d->B * d->H * (size_t)nseg_of(d->T) * sizeof(float);
+    return (raw + 255) / 256 * 256;
+}
+
+size_t linrec_bwd_da_workspace_bytes(const linrec_desc* d)
+{
+    if (check_desc(d) != LINREC_OK)
+        return 0;
+    return linrec_states_bytes(d) + da_tot_bytes(d);
+}
+
 size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
@@ -546,6 +561,51 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
         bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, workspace);
     LAUNCH_SCAN(ctx, sc, s);
     LAUNCH_BWD_INTRA(ctx, in, s);
+    return LINREC_OK;
+}
+
+linrec_status linrec_bwd_da(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                            linrec_tensor k, linrec_tensor v, linrec_tensor decay,
+                            const void* states, linrec_tensor dO, const float* dS_out,
+                            linrec_tensor dq, linrec_tensor dk, linrec_tensor dv, float* dS_in,
+                            linrec_tensor da, const float* da_carry_in, float* da_carry_out,
+                            void* workspace, void* stream)
+{
+    linrec_status st = check_bwd_args(d, q, k, v, decay, states, dO, dS_out, dq, dk, dv,
+                                      dS_in, workspace);
+    if (st != LINREC_OK)
+        return st;
+    if (d->decay == LINREC_DECAY_NONE)
+        return LINREC_E_LAYOUT;
+    if (!da.ptr || !da_carry_out)
+        return LINREC_E_NULL;
+    if (!aligned(da.ptr, 4))
+        return LINREC_E_ALIGN;
+    if (da.sb < 0 || da.sh < 0 || da.st < 1)
+        return LINREC_E_LAYOUT;
+    if ((st = check_state_ptr(da_carry_in, false)) != LINREC_OK ||
+        (st = check_state_ptr(da_carry_out, true)) != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ns = nseg_of(d->T);
+    float* tot = (float*)((char*)workspace + linrec_states_bytes(d));
+    const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
+    BwdIntraLaunch in =
+        bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, workspace);
+    in.da = targ(da);
+    in.da_tot = tot;
+    DaFinishLaunch fin{};
+    fin.B = d->B; fin.H = d->H; fin.N = d->T / kChunk; fin.m = kSegChunks;
+    fin.da = targ(da);
+    fin.decay = targ(decay);
+    fin.decay_kind = d->decay;
+    fin.tot = tot;
+    fin.carry_in = da_carry_in;
+    fin.carry_out = da_carry_out;
+    LAUNCH_SCAN(ctx, sc, s);
+    LAUNCH_BWD_INTRA(ctx, in, s);
+    LAUNCH(timed_launch(ctx, LINREC_KERNEL_DA_FINISH, s,
+                        [&] { return linrec::launch_da_finish(fin, s); }));
     return LINREC_OK;
 }
 

@@ -608,6 +608,14 @@ __device__ __forceinline__ void store_tile(OT* base, int64_t ld, int rbase, int 
         p[r * ld] = (OT)acc[r];
 }
 
+// Four consecutive values of an activation row as fp32.
+__device__ __forceinline__ floatx4 load4(const bf16* p)
+{
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ floatx4 load4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+
 // Store a 16x16 fp32 result tile computed transposed (lane (g,t) holds
 // rows 4g + r of the transpose, i.e. row rbase + t, columns cbase + 4g + r of
 // the output) to row-major global memory as OT: one 8-byte (bf16) or 16-byte

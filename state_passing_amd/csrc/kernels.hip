@@ -368,25 +368,30 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 // load while this one computes; walk 2 starts on walk 1's last chunk, whose
 // K, V, dO and decay tables are still in LDS, so only Q is loaded for it.
 // ---------------------------------------------------------------------------
-template <typename T, typename OT, int DK, int DV>
+template <typename T, typename OT, int DK, int DV, bool DA>
 __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, Act<const T> dO, DecayArg dec,
     const float* __restrict__ bstates, int64_t bs_nseg, const float* __restrict__ gstates,
-    int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, int H, int N, int m)
+    int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, Act<float> da, float* __restrict__ da_tot,
+    int H, int N, int m)
 {
     constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, VP = DV + PAD;
     constexpr int FBW = (DK / 16) / NH;   // walk-1 dQ blocks per wave
+    constexpr int MAXM = 4;               // chunks per segment (launcher: m <= MAXM)
     __shared__ __align__(16) T Qs[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T dOs[CHUNK * VP];
     __shared__ __align__(16) T Ms[2][DV * QP];     // state / gradient, [c][f], split
     __shared__ __align__(16) float tab[TAB_SIZE];
+    // decay gradient: q.dq per token (per half, per chunk of the segment), g per token
+    __shared__ float qdq_s[DA ? NH * MAXM * CHUNK : 1];
+    __shared__ float g_s[DA ? CHUNK : 1];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int w = wave_id(), l = lane_id(), t = l & 15;
+    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
     const int rb = w % 4, half = w / 4, fb0 = half * FBW;
@@ -445,6 +450,14 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         const float rowg = tab[TAB_G + 16 * rb + t];
 
         OT* out = dQ.head(b, h) + tok0 * dQ.st;
+        // decay gradient: this lane's q values for its dQ^T entries
+        floatx4 qv[DA ? FBW : 1];
+        if constexpr (DA) {
+#pragma unroll
+            for (int fbi = 0; fbi < FBW; ++fbi)
+                qv[fbi] = load4(qh + (tok0 + 16 * rb + t) * Q.st + 16 * (fb0 + fbi) + 4 * g);
+        }
+        float qdq = 0.f;
 #pragma unroll
         for (int fbi = 0; fbi < FBW; ++fbi) {
             const int fb = fb0 + fbi;
@@ -457,7 +470,17 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             acc = mma(frag_cols_perm(Ks, QP, 16 * fb, 0), a0, acc);
             if (rb >= 2)
                 acc = mma(frag_cols_perm(Ks, QP, 16 * fb, 32), a1, acc);
+            if constexpr (DA)
+                qdq += acc[0] * qv[fbi][0] + acc[1] * qv[fbi][1] + acc[2] * qv[fbi][2] +
+                       acc[3] * qv[fbi][3];
             store_tile_t<OT>(out, dQ.st, 16 * rb, 16 * fb, acc);
+        }
+        if constexpr (DA) {
+            // sum over the four lane groups: this half's share of q.dq per token
+            qdq += __shfl_xor(qdq, 16, 64);
+            qdq += __shfl_xor(qdq, 32, 64);
+            if (g == 0)
+                qdq_s[(half * MAXM + (n - n0)) * CHUNK + 16 * rb + t] = qdq;
         }
 
         float vf[2][8];
@@ -468,6 +491,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
 
     // ---------------- walk 2: dK, dV
     load_state<DK, DV, 1>(C, gstates + (bh * gs_nseg + s) * seg_record_floats(DK, DV), cbase);
+    float dcarry = 0.f;   // decay gradient: sum of g over the segment's later chunks (wave 0)
     for (int n = n1 - 1; n >= n0; --n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         chunk_store(rq, Qs, QP);
@@ -536,6 +560,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             }
             const Split<T> q0 = split_tiles<T>(atl[0], atl[1]), q1 = split_tiles<T>(atl[2], atl[3]);
             OT* outk = dK.head(b, h) + tok0 * dK.st;
+            float kdk = 0.f;
 #pragma unroll
             for (int fb = 0; fb < DK / 16; ++fb) {
                 floatx4 acc = zero4();
@@ -547,7 +572,23 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
                 if (rb < 2)
                     acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 0), q0, acc);
                 acc = mma(frag_cols_perm(Qs, QP, 16 * fb, 32), q1, acc);
+                if constexpr (DA) {
+                    const floatx4 kk = load4(Ks + (16 * rb + t) * QP + 16 * fb + 4 * g);
+                    kdk += acc[0] * kk[0] + acc[1] * kk[1] + acc[2] * kk[2] + acc[3] * kk[3];
+                }
                 store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+            }
+            if constexpr (DA) {
+                // g = q.dq - k.dk for the tokens of row block rb
+                kdk += __shfl_xor(kdk, 16, 64);
+                kdk += __shfl_xor(kdk, 32, 64);
+                if (g == 0) {
+                    const int c = n - n0, tok = 16 * rb + t;
+                    float qd = qdq_s[c * CHUNK + tok];
+                    if constexpr (NH == 2)
+                        qd += qdq_s[(MAXM + c) * CHUNK + tok];
+                    g_s[tok] = qd - kdk;
+                }
             }
         }
 
@@ -556,7 +597,61 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         slot_factors(tab + TAB_G, of);
         state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, tab[TAB_G + CHUNK - 1], of);
         __syncthreads();
+        if constexpr (DA) {
+            // reverse cumulative sum of g over the chunk (token = lane), plus
+            // the segment's later chunks; g_s is next written after the next
+            // iteration's first barrier
+            if (w == 0) {
+                float x = g_s[l];
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float y = __shfl_down(x, off, 64);
+                    if (l + off < 64)
+                        x += y;
+                }
+                da.ptr[b * da.sb + h * da.sh + (tok0 + l) * da.st] = x + dcarry;
+                dcarry += __shfl(x, 0, 64);
+            }
+        }
     }
+    if constexpr (DA) {
+        if (w == 0 && l == 0)
+            da_tot[bh * gridDim.x + s] = dcarry;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decay gradient of a piece, last step.  With g_t = q_t.dq_t - k_t.dk_t the
+// gradient of the loss with respect to the log-decay of token r is the sum
+// of g_t over t >= r (through the end of the sequence: the carry from later
+// pieces), and da_r = that / a_r.  The segment kernel left the within-segment
+// sums in da and the segment totals in tot.  One workgroup per (b, h)
+// walks the segments from the last; carry_out = carry_in + the piece's sum
+// of g is the carry for the previous piece (it may alias carry_in).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void da_finish_kernel(Act<float> da, DecayArg dec,
+                                                        const float* __restrict__ tot,
+                                                        const float* carry_in, float* carry_out,
+                                                        int H, int T, int seg_len, int nseg)
+{
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = (int64_t)b * H + h;
+    float suffix = carry_in ? carry_in[bh] : 0.f;
+    float* dh = da.head(b, h);
+    __syncthreads();   // every thread has read carry_in before it may be overwritten
+    for (int sg = nseg - 1; sg >= 0; --sg) {
+        for (int i = threadIdx.x; i < seg_len; i += 256) {
+            const int tok = sg * seg_len + i;
+            if (tok < T) {
+                const float a = dec.kind == 1 ? dec.ptr[h * dec.sh]
+                                              : dec.ptr[b * dec.sb + h * dec.sh + tok * dec.st];
+                dh[tok * da.st] = (dh[tok * da.st] + suffix) / a;
+            }
+        }
+        suffix += tot[bh * nseg + sg];
+    }
+    if (threadIdx.x == 0)
+        carry_out[bh] = suffix;
 }
 
 // ---------------------------------------------------------------------------
@@ -617,11 +712,21 @@ template <typename T, typename OT, int DK, int DV>
 hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
 {
     const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
-    hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV>), grid, block, 0, stream,
-                       cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                       decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
-                       (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                       mact<OT>(s.dv_), s.H, s.N, s.m);
+    if (s.m > 4)
+        return hipErrorInvalidValue;
+    if (s.da.ptr)
+        hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV, true>), grid, block, 0, stream,
+                           cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                           decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                           (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                           mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m);
+    else
+        hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, 0, stream,
+                           cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                           decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                           (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                           mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
+                           s.m);
     return hipGetLastError();
 }
 
@@ -672,6 +777,15 @@ hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream)
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream)
 {
     LINREC_DISPATCH(bwd_seg_impl, s, stream);
+}
+
+hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream)
+{
+    const int seg_len = s.m * CHUNK, nseg = (s.N + s.m - 1) / s.m;
+    hipLaunchKernelGGL(da_finish_kernel, dim3(s.H, s.B), dim3(256), 0, stream, mact<float>(s.da),
+                       decay_arg(s.decay, s.decay_kind), s.tot, s.carry_in, s.carry_out, s.H,
+                       s.N * CHUNK, seg_len, nseg);
+    return hipGetLastError();
 }
 
 }  // namespace linrec

@@ -44,6 +44,9 @@ struct FwdIntraLaunch {
     int64_t st_nseg;
 };
 
+// da.ptr != NULL asks for the decay gradient: the kernel writes, per token,
+// the reverse cumulative sum within its segment of q.dq - k.dk into da and
+// each segment's total into da_tot ([B][H][nseg of the piece]).
 struct BwdIntraLaunch {
     int dtype, out_dtype, dk, dv, B, H, N, m;
     TensorArg q, k, v, dO, decay, dq, dk_, dv_;
@@ -52,6 +55,20 @@ struct BwdIntraLaunch {
     int64_t st_nseg;
     const void* ghat;
     int64_t g_nseg;
+    TensorArg da;
+    float* da_tot;
+};
+
+// Finishes the decay gradient of one piece: adds the totals of later
+// segments and the carry from later pieces, divides by the decay, and
+// writes the carry for the previous piece.
+struct DaFinishLaunch {
+    int B, H, N, m;
+    TensorArg da, decay;
+    int decay_kind;
+    const float* tot;
+    const float* carry_in;   // may be NULL (zeros); may alias carry_out
+    float* carry_out;
 };
 
 // The state transition is two launches: the parallel segment sum, then the
@@ -60,5 +77,6 @@ hipError_t launch_seg_sum(const ScanLaunch& s, hipStream_t stream);
 hipError_t launch_seg_fold(const ScanLaunch& s, hipStream_t stream);
 hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream);
+hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream);
 
 }  // namespace linrec

@@ -39,10 +39,11 @@ EXPORTS = (
     "linrec_bwd_seq_workspace_bytes", "linrec_bwd_seq", "linrec_status_str",
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
     "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
+    "linrec_bwd_da_workspace_bytes", "linrec_bwd_da",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
-                5: "bwd_seg"}
+                5: "bwd_seg", 6: "da_finish"}
 
 
 class LinrecError(RuntimeError):
@@ -89,6 +90,8 @@ def _lib():
         "linrec_bwd": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_bwd_recompute_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_recompute": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
+        "linrec_bwd_da_workspace_bytes": ([D], ctypes.c_size_t),
+        "linrec_bwd_da": ([P, D, T, T, T, T, P, T, P, T, T, T, P, T, P, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_status_str": ([ctypes.c_int], ctypes.c_char_p),
@@ -301,6 +304,42 @@ def bwd_recompute(q, k, v, decay, S_in, dO, dS_out=None, *, dq=None, dk=None, dv
                                      _stream(q.device))
     _check(rc, "linrec_bwd_recompute")
     return dq, dk, dv, dS_in
+
+
+def bwd_da_workspace_bytes(d: Desc) -> int:
+    return int(_lib().linrec_bwd_da_workspace_bytes(ctypes.byref(d)))
+
+
+def bwd_da(q, k, v, decay, states, dO, dS_out=None, da_carry=None, *, dq=None, dk=None,
+           dv=None, dS_in=None, da=None, da_carry_out=None, workspace=None, out_dtype=None):
+    """Backward over one piece plus the decay gradient.
+
+    da_carry: fp32 [B,H], the gradient carried from later pieces (<dS_out,
+    S_out>; None = 0).  Returns (dq, dk, dv, dS_in, da, da_carry_out) with
+    da fp32 [B,H,T] and da_carry_out the carry for the previous piece."""
+    kind, dec = _decay(decay)
+    odt = _out_dtype(q, out_dtype, dq)
+    d = _desc_of(q, v, kind, odt)
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    dS_in = _state_out(q, B, H, DK, DV, dS_in)
+    da = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if da is None else da
+    if da_carry_out is None:
+        da_carry_out = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_da_workspace_bytes(d), 16), dtype=torch.uint8,
+                                device=q.device)
+    rc = _lib().linrec_bwd_da(context(q.device.index), ctypes.byref(d), _act(q), _act(k), _act(v),
+                              dec, _ptr(states), _act(dO), _ptr(dS_out), _act(dq), _act(dk),
+                              _act(dv), _ptr(dS_in), Tensor(da.data_ptr(), da.stride(0),
+                                                            da.stride(1), da.stride(2)),
+                              _ptr(da_carry), _ptr(da_carry_out), _ptr(workspace),
+                              _stream(q.device))
+    _check(rc, "linrec_bwd_da")
+    return dq, dk, dv, dS_in, da, da_carry_out
 
 
 def fwd_seq(q, k, v, decay, lengths: Sequence[int], S_in=None, *, o=None, S_out=None,

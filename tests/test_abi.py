@@ -98,6 +98,14 @@ def call_bwd_recompute(desc, S_in=None, workspace=FAKE, dS_in=FAKE, ctx=None):
                                     act(), act(), act(), dS_in, workspace, None)
 
 
+def call_bwd_da(desc, da=None, carry_in=None, carry_out=FAKE, workspace=FAKE, ctx=None):
+    lib = linrec._lib()
+    return lib.linrec_bwd_da(ctx, ctypes.byref(desc), act(), act(), act(),
+                             linrec.Tensor(FAKE, 0, 1, 0), FAKE, act(), None, act(), act(), act(),
+                             FAKE, da or linrec.Tensor(FAKE, 16 * 4096, 4096, 1), carry_in,
+                             carry_out, workspace, None)
+
+
 E = {v: k for k, v in linrec.STATUS.items()}
 
 
@@ -146,6 +154,23 @@ def test_valid_arguments_stop_at_missing_context():
     assert call_bwd(d()) == E["LINREC_E_NULL"]
     assert call_bwd_recompute(d()) == E["LINREC_E_NULL"]
     assert call_bwd_recompute(d(), S_in=FAKE) == E["LINREC_E_NULL"]
+
+
+def test_decay_gradient_arguments():
+    good = d(decay=linrec.DECAY_TOKEN)
+    rec = (128 * 128 + 64) * 4
+    # the gradient records plus one fp32 total per segment (padded to 256 bytes)
+    assert linrec.bwd_da_workspace_bytes(good) == 16 * 16 * rec + 1024
+    assert linrec.bwd_da_workspace_bytes(d(T=100)) == 0
+    assert call_bwd_da(good) == E["LINREC_E_NULL"]            # all checks pass, no context
+    assert call_bwd_da(d(decay=linrec.DECAY_HEAD)) == E["LINREC_E_NULL"]
+    assert call_bwd_da(d(decay=linrec.DECAY_NONE)) == E["LINREC_E_LAYOUT"]
+    assert call_bwd_da(good, da=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
+    assert call_bwd_da(good, da=linrec.Tensor(FAKE + 2, 0, 0, 1)) == E["LINREC_E_ALIGN"]
+    assert call_bwd_da(good, da=linrec.Tensor(FAKE, 0, 0, 0)) == E["LINREC_E_LAYOUT"]
+    assert call_bwd_da(good, carry_out=None) == E["LINREC_E_NULL"]
+    assert call_bwd_da(good, carry_in=FAKE + 2) == E["LINREC_E_ALIGN"]
+    assert call_bwd_da(good, workspace=None) == E["LINREC_E_WORKSPACE"]
 
 
 def test_recompute_arguments():

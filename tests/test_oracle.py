@@ -169,6 +169,35 @@ def test_backward_matches_finite_differences():
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, idx, fd, an)
 
 
+def test_decay_gradient_identity():
+    """The decay gradient the GPU path forms: with g_t = q_t.dq_t - k_t.dk_t,
+    a_r da_r = sum_{t >= r} g_t + <dS_out, S_out>.  Checked on the oracle's
+    own gradients (da pinned by finite differences above), per-token and
+    per-head decay, with S_in and dS_out nonzero, and across a split where
+    the later piece's sum becomes the earlier piece's carry."""
+    rng = np.random.default_rng(21)
+    B, H, T, dk, dv = 2, 3, 40, 4, 6
+    for decay in ("token", "head"):
+        q, k, v, a, S_in = rand_case(rng, B, H, T, dk, dv, decay=decay, lo=0.7)
+        dO = rng.standard_normal((B, H, T, dv))
+        dS_out = rng.standard_normal((B, H, dk, dv))
+        dq, dk_, dv_, dS_in, da = oracle.bwd(q, k, v, a, S_in, dO, dS_out, want_da=True)
+        _, S_out = oracle.fwd(q, k, v, a, S_in)
+        g = np.sum(q * dq, -1) - np.sum(k * dk_, -1)
+        carry = np.sum(dS_out * S_out, axis=(-2, -1))
+        suffix = np.cumsum(g[..., ::-1], -1)[..., ::-1] + carry[..., None]
+        af = decay_full(a, B, H, T)
+        np.testing.assert_allclose(af * da, suffix, rtol=1e-10, atol=1e-10)
+        # the carry entering a piece boundary is <dS, S> there
+        cut = 17
+        S_mid = oracle.fwd(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut],
+                           a if a.ndim == 1 else a[:, :, :cut], S_in)[1]
+        dS_mid = oracle.bwd(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:],
+                            a if a.ndim == 1 else a[:, :, cut:], S_mid, dO[:, :, cut:], dS_out)[3]
+        np.testing.assert_allclose(np.sum(dS_mid * S_mid, axis=(-2, -1)), suffix[:, :, cut],
+                                   rtol=1e-10, atol=1e-10)
+
+
 # ------------------------------------------------------ torch autograd
 
 

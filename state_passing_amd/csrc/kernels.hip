@@ -266,9 +266,6 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     const int cbase = 16 * w;
     const int n0 = s * m, n1 = min(n0 + m, N);
 
-    floatx4 S[DK / 16][1];
-    load_state<DK, DV, 1>(S, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
-
     const T* qh = Q.head(b, h);
     const T* kh = K.head(b, h);
     const T* vh = V.head(b, h);
@@ -277,10 +274,15 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     chunk_load(rq, qh + (int64_t)n0 * CHUNK * Q.st, Q.st);
     chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
     chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
+    // the state load is in flight together with the first chunk's
+    floatx4 S[DK / 16][1];
+    load_state<DK, DV, 1>(S, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
     float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
 
     // P tiles of this wave: row block ib, column blocks jb0, jb0 + jstep, ...
-    const int ib_p = w % 4;
+    // (the second four waves take row blocks in reverse order, so the two
+    // waves sharing a SIMD have 3 or 2 non-zero tiles between them)
+    const int ib_p = (NW == 8 && w >= 4) ? 3 - (w & 3) : (w & 3);
     const int jb0 = NW == 8 ? w / 4 : 0, jstep = NW == 8 ? 2 : 1;
 
     for (int n = n0; n < n1; ++n) {
@@ -337,10 +339,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             store_tile_t<OT>(oh, O.st, 16 * ib, cbase, acc);
         }
 
-        // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma)
-        float vf[2][8];
-        slot_factors(tab + TAB_F, vf);
-        state_update<T, DK, 1>(S, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
+        // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma); the state after
+        // the segment's last chunk is not needed here
+        if (n + 1 < n1) {
+            float vf[2][8];
+            slot_factors(tab + TAB_F, vf);
+            state_update<T, DK, 1>(S, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
+        }
         __syncthreads();
     }
 }
@@ -348,8 +353,9 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 // ---------------------------------------------------------------------------
 // Backward segment kernel.  Workgroup = (b, h, segment), one wave per 16
 // columns of d_v (8 waves at d_v = 128).  Wave w carries state/gradient
-// columns [16w, 16w + 16) and works on row block rb = w % 4 of the outputs;
-// with 8 waves, half w / 4 selects what else it does.
+// columns [16w, 16w + 16) and works on one row block rb of the outputs
+// (w % 4 in the first half of the waves, 3 - w % 4 in the second); with 8
+// waves, half w / 4 selects what else it does.
 //   Walk 1 (chunks in order, S carried from the stored segment state):
 //   S_{n-1} goes to LDS (split) and, for rows rb and the half's columns,
 //       dQ = gamma .* (dO S_{n-1}^T) + A K,   A = (dO V^T) .* D,
@@ -394,7 +400,9 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
-    const int rb = w % 4, half = w / 4, fb0 = half * FBW;
+    // waves w and w + 4 share a SIMD; giving them row blocks rb and 3 - rb
+    // evens out the row-block-dependent tile work per SIMD
+    const int half = w / 4, rb = half ? 3 - (w & 3) : (w & 3), fb0 = half * FBW;
     const int n0 = s * m, n1 = min(n0 + m, N);
 
     floatx4 C[DK / 16][1];   // carried state (walk 1) / gradient (walk 2)
@@ -407,10 +415,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     ChunkRegs<T, DV, NT> rv, rdo;
 
     // ---------------- walk 1: dQ
-    load_state<DK, DV, 1>(C, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
     chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
     chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
     chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st);
+    load_state<DK, DV, 1>(C, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
     float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
@@ -483,9 +491,11 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
                 qdq_s[(half * MAXM + (n - n0)) * CHUNK + 16 * rb + t] = qdq;
         }
 
-        float vf[2][8];
-        slot_factors(tab + TAB_F, vf);
-        state_update<T, DK, 1>(C, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
+        if (n + 1 < n1) {
+            float vf[2][8];
+            slot_factors(tab + TAB_F, vf);
+            state_update<T, DK, 1>(C, Ks, QP, Vs, VP, cbase, tab[TAB_G + CHUNK - 1], vf);
+        }
         __syncthreads();
     }
 
@@ -592,10 +602,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             }
         }
 
-        // G_{n-1} = gamma_C G_n + Q^T (dO .* gamma)
-        float of[2][8];
-        slot_factors(tab + TAB_G, of);
-        state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, tab[TAB_G + CHUNK - 1], of);
+        // G_{n-1} = gamma_C G_n + Q^T (dO .* gamma); not needed after the
+        // segment's first chunk
+        if (n > n0) {
+            float of[2][8];
+            slot_factors(tab + TAB_G, of);
+            state_update<T, DK, 1>(C, Qs, QP, dOs, VP, cbase, tab[TAB_G + CHUNK - 1], of);
+        }
         __syncthreads();
         if constexpr (DA) {
             // reverse cumulative sum of g over the chunk (token = lane), plus

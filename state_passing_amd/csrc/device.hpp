@@ -307,6 +307,41 @@ __device__ __forceinline__ void chunk_store(ChunkRegs<T, D, NT>& r, T* lds, int 
     chunk_store_one<3>(r, lds, pitch);
 }
 
+// chunk_store() into a tile whose rows hold the k index permuted so that
+// the k-slot order of frag_rows_perm() becomes contiguous: within every 32
+// elements, the 4-element unit u (k = 4u .. 4u + 3) sits at unit position
+// 2 (u % 4) + u / 4.  frag_rows() of such a tile then returns exactly what
+// frag_rows_perm() returns from the plain tile, with one 16-byte read; two
+// such tiles contract correctly with each other as well.
+__device__ __forceinline__ int perm_unit(int u) { return 8 * (u >> 3) + 2 * (u & 3) + ((u >> 2) & 1); }
+
+template <int P, typename T, int D, int NT>
+__device__ __forceinline__ void chunk_store_perm_one(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+{
+    typedef ChunkRegs<T, D, NT> R;
+    if constexpr (P < R::NV) {
+        const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
+        const u32x4 v = chunk_vec<P>(r);
+        T* base = lds + row * pitch;
+        if constexpr (sizeof(T) == 2) {   // two 4-element units per vector
+            const int u = col / 4;
+            *reinterpret_cast<u32x2*>(base + 4 * perm_unit(u)) = u32x2{v.x, v.y};
+            *reinterpret_cast<u32x2*>(base + 4 * perm_unit(u + 1)) = u32x2{v.z, v.w};
+        } else {                           // one unit per vector
+            *reinterpret_cast<u32x4*>(base + 4 * perm_unit(col / 4)) = v;
+        }
+    }
+}
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void chunk_store_perm(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+{
+    chunk_store_perm_one<0>(r, lds, pitch);
+    chunk_store_perm_one<1>(r, lds, pitch);
+    chunk_store_perm_one<2>(r, lds, pitch);
+    chunk_store_perm_one<3>(r, lds, pitch);
+}
+
 // ---- decay ----------------------------------------------------------------
 
 // The raw decay this lane needs for the chunk starting at tok0 (token = lane

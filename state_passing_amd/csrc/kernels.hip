@@ -250,11 +250,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 {
     constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
-    // Q is read by 8-byte row reads (the Q S product), K, V and P by 16-byte
-    // row reads and transposing reads
-    constexpr int QQ = DK + Pad16<T>::value;
     constexpr int QP = DK + PAD, VP = DV + PAD, PP = CHUNK + PAD;
-    __shared__ __align__(16) T Qs[CHUNK * QQ];
+    // Q and a second copy of K are staged with their d_k index permuted
+    // (chunk_store_perm), so that the Q S product reads Q in the state's
+    // k-slot order with 16-byte reads; P = Q K^T contracts the two permuted
+    // copies.  The plain K serves the state update.
+    __shared__ __align__(16) T Qs[CHUNK * QP];
+    __shared__ __align__(16) T Kp[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) T Ps[2][CHUNK * PP];
@@ -287,7 +289,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rq, Qs, QQ);
+        chunk_store_perm(rq, Qs, QP);
+        chunk_store_perm(rk, Kp, QP);
         chunk_store(rk, Ks, QP);
         chunk_store(rv, Vs, VP);
         if (w == 0)
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             if (jb <= ib_p) {
 #pragma unroll
                 for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mma(frag_rows(Ks, QP, 16 * jb, 32 * ks), frag_rows(Qs, QQ, 16 * ib_p, 32 * ks), acc);
+                    acc = mma(frag_rows(Kp, QP, 16 * jb, 32 * ks), frag_rows(Qs, QP, 16 * ib_p, 32 * ks), acc);
                 acc = decay_mask<false>(acc, tab, 16 * jb, 16 * ib_p, fac);
             }
             put_split4(Ps[0], Ps[1], (16 * ib_p + t) * PP + 16 * jb + 4 * g, acc);
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             floatx4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(sf[ks], frag_rows_perm(Qs, QQ, 16 * ib, 32 * ks), acc);
+                acc = mma(sf[ks], frag_rows(Qs, QP, 16 * ib, 32 * ks), acc);
             acc *= tab[TAB_G + 16 * ib + t];
 #pragma unroll
             for (int js = 0; js <= ib / 2; ++js)

@@ -54,6 +54,18 @@ KERNEL_BYTES = {
     "bwd_fold": 0,
     "bwd_seg": 1792,       # reads q, k, v, dO, writes dq, dk, dv
 }
+# per-launch bytes of each kernel as designed, per token-head: one fp32
+# d_k x d_v record or state per 256-token segment is 256 B per token-head
+KERNEL_DESIGN_BYTES = {
+    "fwd_sum": 512 + 256,          # k, v; writes the segment records
+    "fwd_fold": 256 + 256,         # reads records, writes segment-start states
+    "fwd_seg": 1024 + 256,         # q, k, v, o; reads the segment-start state
+    "bwd_sum": 512 + 256,          # q, dO; writes the gradient records
+    "bwd_fold": 256 + 256,
+    # k, v, dO for dQ; q, and k, v, dO again except on the chunk both walks
+    # share (one of four); dq, dk, dv; the S and G segment states
+    "bwd_seg": 768 + 256 + 576 + 768 + 512,
+}
 KERNEL_SYMBOL = {
     "fwd_sum": "seg_sum_kernel<bf16,128,128,false>",
     "fwd_fold": "seg_fold_kernel<128,128,false>",
@@ -171,17 +183,19 @@ def main():
         bounds.append(bounds[-1] + L)
 
     def step_seq(record=None):
-        e0 = e1 = None
+        ev = None
         if record is not None:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
         linrec.fwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, inp.S_in, o=o, S_out=S_out,
                        states=states)
-        if record is not None:
-            e1.record()
-            record.append((e0, e1))
+        if ev is not None:
+            ev[1].record()
         linrec.bwd_seq(inp.q, inp.k, inp.v, inp.decay, lengths, states, inp.dO, None, dq=dq,
                        dk=dk, dv=dv, dS_in=dS_in, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+            record.append(ev)
 
     # serialized pass: the same pieces through the per-piece calls on one stream
     pd = linrec.desc(B, H, lengths[0], DK, DV, linrec.BF16, linrec.DECAY_HEAD)
@@ -224,7 +238,8 @@ def main():
         t0 = time.perf_counter()
         ms_step = timed(lambda: step_seq(fwd_ev), args.steps)
         wall = time.perf_counter() - t0
-        fwd_only_ms = sum(a.elapsed_time(b_) for a, b_ in fwd_ev) / len(fwd_ev)
+        fwd_only_ms = sum(e[0].elapsed_time(e[1]) for e in fwd_ev) / len(fwd_ev)
+        per_step = sorted(e[0].elapsed_time(e[2]) for e in fwd_ev)
 
     # serialized pass with per-kernel events on each kernel's own stream
     for _ in range(args.warmup):
@@ -244,6 +259,7 @@ def main():
             "launches_per_step": n // args.steps, "avg_us": avg_ms * 1e3,
             "ms_per_step": ms / args.steps,
             "algorithmic_GBs": KERNEL_BYTES[name] * token_heads_piece / (avg_ms * 1e-3) / 1e9,
+            "design_GBs": KERNEL_DESIGN_BYTES[name] * token_heads_piece / (avg_ms * 1e-3) / 1e9,
         }
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dom = kernels[dominant]
@@ -253,6 +269,7 @@ def main():
                 "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": KERNEL_BYTES[dominant] * token_heads_piece,
+                "design_bytes_per_launch": KERNEL_DESIGN_BYTES[dominant] * token_heads_piece,
                 "avg_launch_us": dom["avg_us"]}
     if args.profile:
         print(json.dumps({"ms_per_step_serialized": ms_serial, "kernels": kernels,
@@ -268,6 +285,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": per_step[len(per_step) // 2],
+        "ms_per_step_min": per_step[0],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -281,6 +300,10 @@ def main():
         "mfma_util_pct": 100.0 * flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "hbm_roof_pct_minimal_bytes": 100.0 * (FWD_BYTES + BWD_BYTES) * B * H * T
                                       / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "fwd_mfma_util_pct": 100.0 * FWD_FLOPS * B * H * T / (fwd_only_ms * 1e-3)
+                             / (PEAK_BF16_TFLOPS * 1e12),
+        "fwd_hbm_roof_pct_minimal_bytes": 100.0 * FWD_BYTES * B * H * T / (fwd_only_ms * 1e-3)
+                                          / (PEAK_HBM_GBS * 1e9),
         "roofline": roofline,
         "ms_per_step_serialized": ms_serial,
         "kernels": kernels,

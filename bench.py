@@ -20,6 +20,11 @@ the stream it runs on) is its own duration.  The dominant kernel is the one
 with the largest share of that pass; its roofline "achieved" figure is its
 algorithmic bytes per launch over its mean duration.
 
+The line also carries the two backward variants, timed the same way over
+the 64 pieces in reverse: from boundary states alone (the per-segment states
+rebuilt, so only one state per piece is kept between the passes) and with the
+decay gradient.
+
 Flags: --gpus N (only 1 is supported: one GPU), --steps K, --warmup W,
 --no-cpu-baseline, --copy-probe BYTES (run only a device copy of that size,
 for calibrating rocprofv3 byte counters), --profile (run only the
@@ -276,6 +281,52 @@ def main():
                           "roofline": roofline}))
         return
 
+    # The backward variants, each over the 64 pieces in reverse with dS
+    # carried, against the plain per-piece backward of the serialized pass
+    # (whose forward left piece_states and o in place).
+    bnd = torch.zeros(len(lengths) + 1, B, H, DK, DV, dtype=torch.float32, device=dev)
+    if inp.S_in is not None:
+        bnd[0].copy_(inp.S_in)
+    for i in range(len(lengths)):
+        sl = slice(bounds[i], bounds[i + 1])
+        linrec.fwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.decay, bnd[i],
+                   o=o[:, :, sl], S_out=bnd[i + 1], states=piece_states[i])
+    ws_rc = torch.empty(linrec.bwd_recompute_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+    ws_da = torch.empty(linrec.bwd_da_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+    da = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    carry = torch.zeros(B, H, dtype=torch.float32, device=dev)
+
+    def pieces_bwd(kind):
+        dS = None
+        if kind == "da":
+            carry.zero_()
+        for i in reversed(range(len(lengths))):
+            sl = slice(bounds[i], bounds[i + 1])
+            a = (inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.decay)
+            outs = dict(dq=dq[:, :, sl], dk=dk[:, :, sl], dv=dv[:, :, sl], dS_in=dS_in)
+            if kind == "plain":
+                linrec.bwd(*a, piece_states[i], inp.dO[:, :, sl], dS, workspace=piece_ws, **outs)
+            elif kind == "recompute":
+                linrec.bwd_recompute(*a, bnd[i], inp.dO[:, :, sl], dS, workspace=ws_rc, **outs)
+            else:
+                linrec.bwd_da(*a, piece_states[i], inp.dO[:, :, sl], dS, carry, da=da[:, :, sl],
+                              da_carry_out=carry, workspace=ws_da, **outs)
+            dS = dS_in
+
+    variants = {}
+    for kind in ("plain", "recompute", "da"):
+        pieces_bwd(kind)
+        variants[kind] = timed(lambda: pieces_bwd(kind), args.steps)
+    next_rows = {
+        "bwd_per_piece_ms": variants["plain"],
+        "bwd_recompute_ms": variants["recompute"],
+        "bwd_recompute_tokens_per_s_fwd_plus_bwd": tokens / ((fwd_only_ms + variants["recompute"]) * 1e-3),
+        "bwd_da_ms": variants["da"],
+        "kept_between_passes_bytes": {
+            "stored_states": linrec.seq_states_bytes(d, lengths),
+            "boundary_states_only": (len(lengths) + 1) * B * H * DK * DV * 4},
+    }
+
     flops_step = (FWD_FLOPS + BWD_FLOPS) * B * H * T
     result = {
         "metric": "fwd+bwd tokens/s at T=256K,H=16,d=128 bf16; MFMA util % of peak",
@@ -307,6 +358,7 @@ def main():
         "roofline": roofline,
         "ms_per_step_serialized": ms_serial,
         "kernels": kernels,
+        "backward_variants": next_rows,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

@@ -622,12 +622,21 @@ __device__ __forceinline__ Split<T> gfrag_cols_split(const float* base, int64_t 
 template <typename T>
 __device__ __forceinline__ void put_split4(T* hi, T* lo, int idx, const floatx4& x)
 {
+    // idx: the lane's row and the tile's first column; lane (g, t) holds
+    // columns 4g .. 4g + 3 of that row.  bf16: lanes g and g ^ 1 trade
+    // halves (v_permlane16_swap swaps odd 16-lane rows of one register with
+    // even rows of the other), so that even g writes the hi plane and odd g
+    // the lo plane, each 8 consecutive columns in one 16-byte store: 16
+    // lanes at 16 rows with 8-byte stores conflict in the LDS banks.
+    const int g = lane_id() >> 4;
     if constexpr (sizeof(T) == 2) {
         const u32x2 p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
-        *reinterpret_cast<u32x2*>(hi + idx) = u32x2{p0.x, p1.x};
-        *reinterpret_cast<u32x2*>(lo + idx) = u32x2{p0.y, p1.y};
+        const auto s0 = __builtin_amdgcn_permlane16_swap(p0.x, p0.y, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(p1.x, p1.y, false, false);
+        T* plane = (g & 1) ? lo : hi;
+        *reinterpret_cast<u32x4*>(plane + idx + 8 * (g >> 1)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     } else {
-        *reinterpret_cast<floatx4*>(hi + idx) = x;
+        *reinterpret_cast<floatx4*>(hi + idx + 4 * g) = x;
     }
 }
 

@@ -115,7 +115,7 @@ __device__ __forceinline__ void put_state(T* hi, T* lo, int pitch, const floatx4
     for (int fb = 0; fb < DK / 16; ++fb)
 #pragma unroll
         for (int cbl = 0; cbl < NCB; ++cbl)
-            put_split4(hi, lo, (cbase0 + 16 * cbl + t) * pitch + 16 * fb + 4 * g, st[fb][cbl]);
+            put_split4(hi, lo, (cbase0 + 16 * cbl + t) * pitch + 16 * fb, st[fb][cbl]);
 }
 
 // ---------------------------------------------------------------------------
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
                     acc = mma(frag_rows(Kp, QP, 16 * jb, 32 * ks), frag_rows(Qs, QP, 16 * ib_p, 32 * ks), acc);
                 acc = decay_mask<false>(acc, tab, 16 * jb, 16 * ib_p, fac);
             }
-            put_split4(Ps[0], Ps[1], (16 * ib_p + t) * PP + 16 * jb + 4 * g, acc);
+            put_split4(Ps[0], Ps[1], (16 * ib_p + t) * PP + 16 * jb, acc);
         }
         // S_{n-1} as split B fragments (k = f in frag_rows_perm order)
         Split<T> sf[DK / 32];

@@ -80,6 +80,7 @@ KERNEL_SYMBOL = {
     "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128>",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_seg_sa256k_traffic.txt")
+SQ_FILE = os.path.join(ROOT, "profiles", "linrec_kernels_sa256k_sq_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "state_passing_amd", "csrc", f)
                   for f in ("kernels.hip", "device.hpp", "launch.hpp")]
 
@@ -113,6 +114,19 @@ def traffic_from_profile(kernel: str, launch_units: int):
     if not m or m.group(1) != kernel_source_hash():
         return None
     m = re.search(r"bytes_per_launch_calibrated:\s*([0-9.eE+]+)", txt)
+    return float(m.group(1)) if m else None
+
+
+def mfma_busy_from_profile():
+    """The dominant kernel's MFMA busy percentage from the committed shader
+    counter summary; None if missing or taken on other kernel code."""
+    if not os.path.exists(SQ_FILE):
+        return None
+    txt = open(SQ_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", txt)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"mfma_busy_pct_bwd_seg:\s*([0-9.eE+]+)", txt)
     return float(m.group(1)) if m else None
 
 
@@ -349,6 +363,7 @@ def main():
         "fwd_tokens_per_s": tokens / (fwd_only_ms * 1e-3),
         "fwd_ms": fwd_only_ms,
         "mfma_util_pct": 100.0 * flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "bwd_seg_mfma_busy_pct_counters": mfma_busy_from_profile(),
         "hbm_roof_pct_minimal_bytes": 100.0 * (FWD_BYTES + BWD_BYTES) * B * H * T
                                       / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "fwd_mfma_util_pct": 100.0 * FWD_FLOPS * B * H * T / (fwd_only_ms * 1e-3)

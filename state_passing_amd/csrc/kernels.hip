@@ -143,9 +143,11 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     constexpr int PAD = Pad<T>::value;
     constexpr int XP = DK + PAD, YP = DV + PAD;
     constexpr int64_t REC = seg_record_floats(DK, DV);
-    __shared__ __align__(16) T Xs[CHUNK * XP];
-    __shared__ __align__(16) T Ys[CHUNK * YP];
-    __shared__ __align__(16) float tab[TAB_SIZE];
+    // two buffers: chunk it + 1 is staged while chunk it may still be read,
+    // so one barrier per chunk suffices
+    __shared__ __align__(16) T Xs[2][CHUNK * XP];
+    __shared__ __align__(16) T Ys[2][CHUNK * YP];
+    __shared__ __align__(16) float tab[2][TAB_SIZE];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id();
@@ -168,10 +170,15 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     chunk_load(ry, yh + (int64_t)n * CHUNK * Y.st, Y.st);
     float ra = decay_raw(dec, b, h, (int64_t)n * CHUNK);
     for (int it = 0; it < cnt; ++it) {
-        chunk_store(rx, Xs, XP);
-        chunk_store(ry, Ys, YP);
+        // buffer it % 2 was last read in chunk it - 2, before every wave
+        // passed the previous chunk's barrier
+        T* xs = Xs[it & 1];
+        T* ys = Ys[it & 1];
+        float* tb = tab[it & 1];
+        chunk_store(rx, xs, XP);
+        chunk_store(ry, ys, YP);
         if (w == 0)
-            decay_tables(dec, ra, tab);
+            decay_tables(dec, ra, tb);
         __syncthreads();
         if (it + 1 < cnt) {
             n = REVERSE ? n1 - 2 - it : n0 + 1 + it;
@@ -180,11 +187,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
             chunk_load(ry, yh + tn * Y.st, Y.st);
             ra = decay_raw(dec, b, h, tn);
         }
-        seg_log += tab[TAB_LAM + CHUNK - 1];
+        seg_log += tb[TAB_LAM + CHUNK - 1];
         float yf[2][8];
-        slot_factors(tab + (REVERSE ? TAB_G : TAB_F), yf);
-        state_update<T, DK, 1>(U, Xs, XP, Ys, YP, cbase, tab[TAB_G + CHUNK - 1], yf);
-        __syncthreads();
+        slot_factors(tb + (REVERSE ? TAB_G : TAB_F), yf);
+        state_update<T, DK, 1>(U, xs, XP, ys, YP, cbase, tb[TAB_G + CHUNK - 1], yf);
     }
 
     float* rec = store + (bh * store_nseg + s) * REC;
@@ -199,23 +205,25 @@ __global__ __launch_bounds__(256) void seg_fold_kernel(
     int64_t store_nseg, int H, int nseg)
 {
     constexpr int64_t REC = seg_record_floats(DK, DV);
-    const int e = blockIdx.x * 256 + threadIdx.x;          // element [f][c] of a record
+    // four consecutive elements [f][c] of a record per thread
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
     const int h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * H + h;
     const int64_t io = bh * (DK * DV) + e;                   // S_in / S_out: same layout
-    float carry = carry_in ? carry_in[io] : 0.f;
+    floatx4 carry = carry_in ? *reinterpret_cast<const floatx4*>(carry_in + io) : floatx4{0.f, 0.f, 0.f, 0.f};
     float* base = store + bh * store_nseg * REC;
     // loads of a batch of records are issued before any of the batch's
     // stores (each store goes to a slot that was just read)
     constexpr int BATCH = 16;
     for (int k0 = 0; k0 < nseg; k0 += BATCH) {
-        float u[BATCH], lg[BATCH];
+        floatx4 u[BATCH];
+        float lg[BATCH];
 #pragma unroll
         for (int j = 0; j < BATCH; ++j) {
             const int k = k0 + j;
             if (k < nseg) {
                 const float* rec = base + (REVERSE ? nseg - 1 - k : k) * REC;
-                u[j] = rec[e];
+                u[j] = *reinterpret_cast<const floatx4*>(rec + e);
                 lg[j] = rec[DK * DV];
             }
         }
@@ -224,12 +232,15 @@ __global__ __launch_bounds__(256) void seg_fold_kernel(
             const int k = k0 + j;
             if (k < nseg) {
                 float* rec = base + (REVERSE ? nseg - 1 - k : k) * REC;
-                rec[e] = carry;
-                carry = __expf(lg[j]) * carry + u[j];
+                *reinterpret_cast<floatx4*>(rec + e) = carry;
+                const float f = __expf(lg[j]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    carry[i] = f * carry[i] + u[j][i];
             }
         }
     }
-    carry_out[io] = carry;
+    *reinterpret_cast<floatx4*>(carry_out + io) = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -704,7 +715,7 @@ template <typename T, typename OT, int DK, int DV>
 hipError_t fold_impl(const ScanLaunch& s, hipStream_t stream)
 {
     const int nseg = (s.N + s.m - 1) / s.m;
-    const dim3 grid(DK * DV / 256, s.H, s.B), block(256);
+    const dim3 grid(DK * DV / 1024, s.H, s.B), block(256);
     if (s.reverse)
         hipLaunchKernelGGL((seg_fold_kernel<DK, DV, true>), grid, block, 0, stream, s.carry_in,
                            s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);

@@ -652,33 +652,68 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
 // gradient of the loss with respect to the log-decay of token r is the sum
 // of g_t over t >= r (through the end of the sequence: the carry from later
 // pieces), and da_r = that / a_r.  The segment kernel left the within-segment
-// sums in da and the segment totals in tot.  One workgroup per (b, h)
-// walks the segments from the last; carry_out = carry_in + the piece's sum
-// of g is the carry for the previous piece (it may alias carry_in).
+// sums in da and the segment totals in tot.  One workgroup per (b, h): the
+// totals of up to 1024 segments at a time are turned into suffix sums in LDS
+// (an inclusive scan from the last segment), then every token of those
+// segments is finished independently, four per thread with their loads
+// issued together.  carry_out = carry_in + the piece's sum of g is the carry
+// for the previous piece (it may alias carry_in: every thread reads carry_in
+// before the first barrier, thread 0 writes carry_out after the last).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void da_finish_kernel(Act<float> da, DecayArg dec,
-                                                        const float* __restrict__ tot,
-                                                        const float* carry_in, float* carry_out,
-                                                        int H, int T, int seg_len, int nseg)
+__global__ __launch_bounds__(1024) void da_finish_kernel(Act<float> da, DecayArg dec,
+                                                         const float* __restrict__ tot,
+                                                         const float* carry_in, float* carry_out,
+                                                         int H, int T, int seg_len, int nseg)
 {
-    const int h = blockIdx.x, b = blockIdx.y;
+    constexpr int NT = 1024;
+    __shared__ float suf[NT + 1];   // suf[i]: sum of the block's totals from segment i on
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int64_t bh = (int64_t)b * H + h;
-    float suffix = carry_in ? carry_in[bh] : 0.f;
+    float running = carry_in ? carry_in[bh] : 0.f;   // sum over every later segment
     float* dh = da.head(b, h);
-    __syncthreads();   // every thread has read carry_in before it may be overwritten
-    for (int sg = nseg - 1; sg >= 0; --sg) {
-        for (int i = threadIdx.x; i < seg_len; i += 256) {
-            const int tok = sg * seg_len + i;
-            if (tok < T) {
-                const float a = dec.kind == 1 ? dec.ptr[h * dec.sh]
-                                              : dec.ptr[b * dec.sb + h * dec.sh + tok * dec.st];
-                dh[tok * da.st] = (dh[tok * da.st] + suffix) / a;
+    for (int end = nseg; end > 0; end -= NT) {
+        const int start = max(0, end - NT), nb = end - start;
+        // inclusive suffix scan of this block's totals
+        float x = tid < nb ? tot[bh * nseg + start + tid] : 0.f;
+        suf[tid] = x;
+        if (tid == 0)
+            suf[NT] = 0.f;
+        __syncthreads();
+        for (int off = 1; off < nb; off <<= 1) {
+            const float y = tid + off < nb ? suf[tid + off] : 0.f;
+            __syncthreads();
+            x += y;
+            suf[tid] = x;
+            __syncthreads();
+        }
+        // tokens of segments start .. end - 1, four per thread
+        const int t0 = start * seg_len, t1 = min(end * seg_len, T);
+        for (int base = t0; base < t1; base += 4 * NT) {
+            float v[4], a[4];
+            int tok[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                tok[j] = base + j * NT + tid;
+                if (tok[j] < t1) {
+                    v[j] = dh[tok[j] * da.st];
+                    a[j] = dec.kind == 1 ? dec.ptr[h * dec.sh]
+                                         : dec.ptr[b * dec.sb + h * dec.sh + (int64_t)tok[j] * dec.st];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (tok[j] < t1) {
+                    const int i = tok[j] / seg_len - start;
+                    // totals of the later segments of this block, then of later blocks
+                    dh[tok[j] * da.st] = (v[j] + suf[i + 1 < nb ? i + 1 : NT] + running) / a[j];
+                }
             }
         }
-        suffix += tot[bh * nseg + sg];
+        running += suf[0];
+        __syncthreads();   // suf is rewritten by the next block
     }
-    if (threadIdx.x == 0)
-        carry_out[bh] = suffix;
+    if (tid == 0)
+        carry_out[bh] = running;
 }
 
 // ---------------------------------------------------------------------------
@@ -809,7 +844,7 @@ hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream)
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream)
 {
     const int seg_len = s.m * CHUNK, nseg = (s.N + s.m - 1) / s.m;
-    hipLaunchKernelGGL(da_finish_kernel, dim3(s.H, s.B), dim3(256), 0, stream, mact<float>(s.da),
+    hipLaunchKernelGGL(da_finish_kernel, dim3(s.H, s.B), dim3(1024), 0, stream, mact<float>(s.da),
                        decay_arg(s.decay, s.decay_kind), s.tot, s.carry_in, s.carry_out, s.H,
                        s.N * CHUNK, seg_len, nseg);
     return hipGetLastError();

@@ -88,8 +88,8 @@ KERNEL_SOURCES = [os.path.join(ROOT, "state_passing_amd", "csrc", f)
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=5)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0)
     p.add_argument("--profile", action="store_true")
@@ -161,12 +161,14 @@ def cpu_baseline(inp, wl, sample_tokens: int):
     threads = min(wl.B * wl.H, len(os.sched_getaffinity(0)))
     t0 = time.perf_counter()
     oracle.fwd(q, k, v, a, None, nthreads=threads)
+    t1 = time.perf_counter()
     oracle.bwd(q, k, v, a, None, dO, None, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": wl.B * sample_tokens / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"fwd+bwd, unsplit, all {wl.B * wl.H} heads, first {sample_tokens} of "
-                      f"{wl.T} tokens ({dt:.1f} s)"}
+                      f"{wl.T} tokens ({dt:.1f} s)",
+            "fwd_tokens_per_s": wl.B * sample_tokens / (t1 - t0)}
 
 
 def main():

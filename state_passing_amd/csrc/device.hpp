@@ -52,12 +52,9 @@ struct Act {
 };
 
 // LDS row padding.  32 bytes per row keep 16-byte row reads (frag_rows) and
-// the transposing reads (frag_cols, frag_cols_perm) near the LDS peak;
-// 16 bytes suit 8-byte row reads (frag_rows_perm) better.
+// the transposing reads (frag_cols, frag_cols_perm) near the LDS peak.
 template <typename T>
 struct Pad { static constexpr int value = 32 / sizeof(T); };
-template <typename T>
-struct Pad16 { static constexpr int value = 16 / sizeof(T); };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // Wave index as a wave-uniform (scalar) value.
@@ -592,33 +589,9 @@ __device__ __forceinline__ Split<T> frag_cols_split(const T* hi, const T* lo, in
     return s;
 }
 
-// Split fragment of an fp32 matrix in global memory.
-//   contiguous k: lane (g,t) <- base[(rbase + t) * ld + kbase + 8g + r]
-//   strided k:    lane (g,t) <- base[(kbase + 8g + r) * ld + cbase + t]
-template <typename T>
-__device__ __forceinline__ Split<T> gfrag_rows_split(const float* base, int64_t ld, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    const float4* p = reinterpret_cast<const float4*>(base + (rbase + t) * ld + kbase + 8 * g);
-    const float4 a = p[0], b = p[1];
-    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    return split8<T>(x);
-}
-
-template <typename T>
-__device__ __forceinline__ Split<T> gfrag_cols_split(const float* base, int64_t ld, int cbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        x[r] = base[(kbase + 8 * g + r) * ld + cbase + t];
-    return split8<T>(x);
-}
-
 // Write the 4 values of a result tile a lane holds (rows 4g + r, column t) as
-// four consecutive elements of row `row` of an LDS plane pair (the tile
-// lands transposed: LDS row = tile column).
+// four consecutive elements of an LDS row of a plane pair (the tile lands
+// transposed: LDS row = tile column).
 template <typename T>
 __device__ __forceinline__ void put_split4(T* hi, T* lo, int idx, const floatx4& x)
 {
@@ -638,18 +611,6 @@ __device__ __forceinline__ void put_split4(T* hi, T* lo, int idx, const floatx4&
     } else {
         *reinterpret_cast<floatx4*>(hi + idx + 4 * g) = x;
     }
-}
-
-// Store a 16x16 fp32 result tile (lane (g,t) holds rows 4g + r, column t)
-// to row-major global memory as OT.
-template <typename OT>
-__device__ __forceinline__ void store_tile(OT* base, int64_t ld, int rbase, int cbase, floatx4 acc)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    OT* p = base + (rbase + 4 * g) * ld + cbase + t;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        p[r * ld] = (OT)acc[r];
 }
 
 // Four consecutive values of an activation row as fp32.

@@ -6,7 +6,8 @@ unsplit fp64 oracle on sampled heads over the whole sequence.
   tiny-fp32        B=1 H=2  T=1024    4 x 256,    a_t = 1, fp32  (all heads;
                    also unsplit)
   decay-16k        B=1 H=16 T=16384   4 x 4096,   per-head decay   (all heads)
-  sa-256k          B=1 H=16 T=262144  64 x 4096,  per-head decay   (4 heads)
+  sa-256k          B=1 H=16 T=262144  64 x 4096,  per-head decay   (4 heads;
+                   also unsplit)
   nonuniform-256k  B=1 H=32 T=262144  16 random pieces, S_in != 0  (4 heads)
   gated-batch      B=8 H=32 T=32768   8 x 4096,   per-token gate   (8 heads)
 
@@ -58,7 +59,8 @@ def test_fullsize_sequence_accumulation(idx):
     runs = [(lengths, torch.float32)]
     if wl.dtype == "bf16":
         runs.append((lengths, torch.bfloat16))
-    else:
+    if wl.dtype != "bf16" or idx == 3:
+        # the whole sequence as one piece (for sa-256k: 1024 segments a head)
         runs.append(([wl.T], torch.float32))
     for lens, odt in runs:
         got = run_sa(inp, lens, odt)

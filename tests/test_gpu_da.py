@@ -73,6 +73,26 @@ def test_decay_gradient_one_piece(wl):
     assert err <= tol and cerr <= tol, (err, cerr)
 
 
+def test_decay_gradient_strong_decay():
+    """Per-token decays in [0.3, 1): chunks on both sides of the threshold
+    below which the mask is taken one exp per entry."""
+    wl = small("da-strong", 1, 2, 512, 128, 128, "bf16", "token", s_in=0.1)
+    inp = inputs(wl)
+    g = torch.Generator().manual_seed(37)
+    inp.decay = (0.3 + 0.7 * torch.rand(tuple(inp.decay.shape), generator=g)).to(DEV)
+    ref, carry, a = oracle_da(inp)
+    _, _, st = linrec.fwd(inp.q, inp.k, inp.v, inp.decay, inp.S_in, out_dtype=torch.float32)
+    carry_t = torch.tensor(carry, dtype=torch.float32, device=DEV)
+    da, cout = linrec.bwd_da(inp.q, inp.k, inp.v, inp.decay, st, inp.dO, inp.dS_out, carry_t,
+                             out_dtype=torch.float32)[4:]
+    torch.cuda.synchronize()
+    err = rel_err(da, ref["da"])
+    ada = a * ref["da"]
+    cerr = float(np.max(np.abs(np64(cout) - ada[:, :, 0])) / np.sqrt(np.mean(ada * ada)))
+    print(f"[da-strong] da={err:.2e} carry_out={cerr:.2e}", flush=True)
+    assert err <= TOL[torch.bfloat16] and cerr <= TOL[torch.bfloat16], (err, cerr)
+
+
 def test_decay_gradient_sequence_with_carry():
     """Pieces in reverse with dS and the decay-gradient carry handed back give
     the unsplit oracle's da over the whole sequence."""

@@ -123,6 +123,28 @@ def test_small_split_matches_oracle_and_unsplit(wl):
                 assert all(same.values()), same
 
 
+@pytest.mark.parametrize("decay", ["token", "head"])
+def test_strong_decay_unfactored_mask(decay):
+    """Decays strong enough that a chunk's total log-decay falls below the
+    threshold under which the mask factor is no longer taken as a product of
+    two table entries (the later one would overflow): there the kernels take
+    one exp per mask entry.  Per-token decays drawn in [0.3, 1) mix both
+    paths chunk by chunk; a per-head decay of 0.5 (chunk decay 2^-64) takes
+    the per-entry path everywhere.  Unsplit and split against the oracle."""
+    wl = small(f"strong-{decay}", 2, 2, 768, 128, 128, "bf16", decay, s_in=0.1)
+    inp = gpu_inputs(wl)
+    g = torch.Generator().manual_seed(31)
+    if decay == "token":
+        a = 0.3 + 0.7 * torch.rand(tuple(inp.decay.shape), generator=g)
+    else:
+        a = torch.full(tuple(inp.decay.shape), 0.5)
+    inp.decay = a.to(torch.float32).to(DEV)
+    ref = oracle_run(inp)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    check(run_unsplit(inp, torch.float32), ref, heads, wl, "unsplit/f32-out")
+    check(run_seq(inp, [256, 448, 64], torch.float32), ref, heads, wl, "run_seq/f32-out")
+
+
 RECOMPUTE_CASES = [SMALL[1], SMALL[4], SMALL[6], SMALL[9]]
 
 

@@ -257,10 +257,14 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
                                       const int32_t* lengths);
 
 /* Backward of linrec_fwd_seq: pieces in reverse order with dS carried back
- * from dS_out to dS_in.  Every launch goes to `stream` (the backward segment
- * kernel occupies a whole CU, so a concurrent transition kernel would only
- * delay it).  The workspace holds the gradient records of one piece, reused
- * piece after piece. */
+ * from dS_out to dS_in, each piece's backward running over the states its
+ * forward stored (the backward pass over stored states of Sequence
+ * Accumulation and Beyond, "Approach"; boundary gradients carried from piece
+ * to piece: StateFlow, Abstract).  Every launch goes to `stream` (the
+ * backward segment kernel occupies a whole CU, so a concurrent transition
+ * kernel would only delay it).  The workspace holds the gradient records of
+ * one piece, reused piece after piece.  Same arguments and rules as
+ * linrec_bwd otherwise; `states` as written by linrec_fwd_seq. */
 linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              int32_t npieces, const int32_t* lengths,
                              linrec_tensor q, linrec_tensor k, linrec_tensor v,

@@ -137,31 +137,9 @@ __device__ __forceinline__ Frag<float> frag_cols(const float* tile, int pitch, i
 // is k = kbase + 4g + r (first tile's rows), slot r >= 4 is k = kbase + 16 +
 // 4g + (r - 4) (second tile's rows).  A result tile held in registers can
 // then serve as the other operand without moving between lanes.
-//   frag_rows_perm: lane (g,t) <- tile[rbase + t][k(slot)]
 //   frag_cols_perm: lane (g,t) <- tile[k(slot)][cbase + t]
-__device__ __forceinline__ Frag<bf16> frag_rows_perm(const bf16* tile, int pitch, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    const bf16* p = tile + (rbase + t) * pitch + kbase + 4 * g;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
-    Frag<bf16> f;
-    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return f;
-}
-
-__device__ __forceinline__ Frag<float> frag_rows_perm(const float* tile, int pitch, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    const float* p = tile + (rbase + t) * pitch + kbase + 4 * g;
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 16);
-    Frag<float> f;
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-}
-
+// (a row read in that order is frag_rows() of a tile staged with
+// chunk_store_perm()).
 __device__ __forceinline__ Frag<bf16> frag_cols_perm(const bf16* tile, int pitch, int cbase, int kbase)
 {
     const int l = lane_id(), t = l & 15, g = l >> 4;
@@ -183,60 +161,6 @@ __device__ __forceinline__ Frag<float> frag_cols_perm(const float* tile, int pit
         f.v[4 + r] = tile[(kbase + 16 + 4 * g + r) * pitch + cbase + t];
     }
     return f;
-}
-
-// Fragment read straight from global memory, k contiguous: lane (g,t) <-
-// base[(rbase + t) * ld + kbase + 8g + r].
-__device__ __forceinline__ Frag<bf16> frag_rows_global(const bf16* base, int64_t ld, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    Frag<bf16> f;
-    f.v = *reinterpret_cast<const bf16x8*>(base + (rbase + t) * ld + kbase + 8 * g);
-    return f;
-}
-
-__device__ __forceinline__ Frag<float> frag_rows_global(const float* base, int64_t ld, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    const float4* p = reinterpret_cast<const float4*>(base + (rbase + t) * ld + kbase + 8 * g);
-    const float4 a = p[0], b = p[1];
-    Frag<float> f;
-    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-    return f;
-}
-
-__device__ __forceinline__ Frag<bf16> scaled(Frag<bf16> f, float s)
-{
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        f.v[r] = (bf16)((float)f.v[r] * s);
-    return f;
-}
-
-__device__ __forceinline__ Frag<float> scaled(Frag<float> f, float s)
-{
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        f.v[r] *= s;
-    return f;
-}
-
-// ---- global <-> LDS staging ---------------------------------------------
-
-// Copy ROWS x D elements (row stride `ld` in global) into LDS (row pitch
-// `pitch`) with 16-byte accesses, all NT threads cooperating.
-template <typename T, int ROWS, int D, int NT>
-__device__ __forceinline__ void stage_rows(T* lds, int pitch, const T* src, int64_t ld)
-{
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int PER_ROW = D / VEC;
-    static_assert(D % VEC == 0, "row must be a whole number of 16-byte vectors");
-    for (int idx = threadIdx.x; idx < ROWS * PER_ROW; idx += NT) {
-        const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-        *reinterpret_cast<u32x4*>(lds + r * pitch + c) =
-            *reinterpret_cast<const u32x4*>(src + r * ld + c);
-    }
 }
 
 // A chunk's rows of one activation (64 x D elements) spread over the NT
@@ -305,10 +229,10 @@ __device__ __forceinline__ void chunk_store(ChunkRegs<T, D, NT>& r, T* lds, int 
 }
 
 // chunk_store() into a tile whose rows hold the k index permuted so that
-// the k-slot order of frag_rows_perm() becomes contiguous: within every 32
+// the k-slot order of the result tiles becomes contiguous: within every 32
 // elements, the 4-element unit u (k = 4u .. 4u + 3) sits at unit position
 // 2 (u % 4) + u / 4.  frag_rows() of such a tile then returns exactly what
-// frag_rows_perm() returns from the plain tile, with one 16-byte read; two
+// two 8-byte reads at k and k + 16 would return from the plain tile, with one 16-byte read; two
 // such tiles contract correctly with each other as well.
 __device__ __forceinline__ int perm_unit(int u) { return 8 * (u >> 3) + 2 * (u & 3) + ((u >> 2) & 1); }
 
@@ -362,27 +286,6 @@ __device__ __forceinline__ float decay_log_cumsum(const DecayArg& d, float raw)
     if (d.kind == 1)
         return (float)(lane + 1) * logf(raw);
     float x = logf(raw);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off)
-            x += y;
-    }
-    return x;
-}
-
-// Inclusive cumulative log-decay of the chunk's tokens, token = lane:
-// lam_i = sum_{r <= i} ln a_r over the chunk starting at token tok0.  Must be
-// called by a full wave.  Log-space and chunk-local, so exp(lam_i - lam_j)
-// and exp(lam_i) never overflow or underflow across long sequences.
-__device__ __forceinline__ float chunk_log_cumsum(const DecayArg& d, int b, int h, int64_t tok0)
-{
-    const int lane = lane_id();
-    if (d.kind == 0)
-        return 0.f;
-    if (d.kind == 1)
-        return (float)(lane + 1) * logf(d.ptr[h * d.sh]);
-    float x = logf(d.ptr[b * d.sb + h * d.sh + (tok0 + lane) * d.st]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -548,7 +451,7 @@ __device__ __forceinline__ floatx4 mma(const Split<float>& a, const Frag<float>&
 }
 
 // Split operand from two 16x16 result tiles in registers (k-slot order of
-// frag_rows_perm / frag_cols_perm).
+// the result tiles).
 template <typename T>
 __device__ __forceinline__ Split<T> split_tiles(const floatx4& a, const floatx4& b)
 {

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void seg_fold_kernel(
 //   O[:, cols] = gamma .* (Q S_{n-1}[:, cols]) + P V[:, cols],
 //   S_n[:, cols] = gamma_C S_{n-1}[:, cols] + K^T (V[:, cols] .* gamma_C/gamma).
 // The state serves as the B operand straight from registers (k-slot order
-// of frag_rows_perm).  The next chunk's rows load while this one computes.
+// of the result tiles).  The next chunk's rows load while this one computes.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             }
             put_split4(Ps[0], Ps[1], (16 * ib_p + t) * PP + 16 * jb, acc);
         }
-        // S_{n-1} as split B fragments (k = f in frag_rows_perm order)
+        // S_{n-1} as split B fragments (k = f in result-tile k-slot order)
         Split<T> sf[DK / 32];
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)

@@ -231,6 +231,95 @@ def _check(rc, where):
         raise LinrecError(rc, where)
 
 
+
+# ----------------------------------------------------------------- validation
+#
+# The C ABI checks what it can see (shapes in the descriptor, alignment,
+# strides, NULL pointers).  It cannot see tensor shapes, dtypes, devices or
+# buffer sizes, so a mismatch there would become an out-of-bounds access on
+# the GPU.  These checks run before any library call; the device check comes
+# last so that every structural mistake is reported as such.
+
+def _need(cond: bool, msg: str, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_act(name, t, shape, dtype=None):
+    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
+    _need(t.dim() == 4, f"{name}: must be [B,H,T,d], got {tuple(t.shape)}")
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name}: dtype {t.dtype} != {dtype}", TypeError)
+    _need(t.stride(-1) == 1, f"{name}: the feature dimension must be contiguous (stride 1)")
+
+
+def _check_state(name, t, shape):
+    if t is None:
+        return
+    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
+    _need(t.dtype == torch.float32, f"{name}: must be float32, got {t.dtype}", TypeError)
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    _need(t.is_contiguous(), f"{name}: must be contiguous")
+
+
+def _check_decay(decay, B, H, T):
+    if decay is None:
+        return
+    _need(isinstance(decay, torch.Tensor), "decay: expected a tensor", TypeError)
+    _need(decay.dtype == torch.float32, "decay must be float32", TypeError)
+    _need(tuple(decay.shape) in ((H,), (B, H, T)), f"decay must be [H] or [B,H,T], got "
+          f"{tuple(decay.shape)} for B={B} H={H} T={T}")
+
+
+def _check_buffer(name, t, nbytes):
+    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
+    _need(t.is_contiguous(), f"{name}: must be contiguous")
+    have = t.numel() * t.element_size()
+    _need(have >= nbytes, f"{name}: {have} bytes, the call needs {nbytes}")
+
+
+def _check_device(q, *others):
+    _need(q.is_cuda, f"tensors must be on a GPU, got {q.device}")
+    for name, t in others:
+        if t is not None:
+            _need(t.device == q.device, f"{name}: on {t.device}, q on {q.device}")
+
+
+def _validate(q, k, v, decay, *, dO=None, outs=(), states_in=(), states_out=(), extra=()):
+    """Check every tensor of a call against q's [B,H,T,d_k] and v's d_v.
+
+    outs: (name, tensor or None, out dtype, d) activation outputs;
+    states_in / states_out: (name, tensor or None) fp32 [B,H,d_k,d_v];
+    extra: (name, tensor or None) other tensors that only need the device check.
+    Returns the (name, tensor) pairs for _check_device, which the caller runs
+    after its buffer-size checks, so that structural errors are reported first."""
+    _need(isinstance(q, torch.Tensor), "q: expected a tensor", TypeError)
+    _need(q.dim() == 4, f"q: must be [B,H,T,d_k], got {tuple(q.shape)}")
+    B, H, T, DK = q.shape
+    _need(q.dtype in (torch.bfloat16, torch.float32), f"unsupported activation dtype {q.dtype}",
+          TypeError)
+    _check_act("q", q, (B, H, T, DK), q.dtype)
+    _check_act("k", k, (B, H, T, DK), q.dtype)
+    _need(isinstance(v, torch.Tensor) and v.dim() == 4, "v: must be [B,H,T,d_v]")
+    DV = v.shape[3]
+    _check_act("v", v, (B, H, T, DV), q.dtype)
+    if dO is not None:
+        _check_act("dO", dO, (B, H, T, DV), q.dtype)
+    _check_decay(decay, B, H, T)
+    odts = set()
+    for name, t, odt, d in outs:
+        if t is not None:
+            _check_act(name, t, (B, H, T, d))
+            odts.add(t.dtype)
+        else:
+            odts.add(odt)
+    _need(len(odts) <= 1, f"outputs must share one dtype, got {sorted(map(str, odts))}", TypeError)
+    for name, t in tuple(states_in) + tuple(states_out):
+        _check_state(name, t, (B, H, DK, DV))
+    return (("k", k), ("v", v), ("dO", dO), ("decay", decay),
+            *((n, t) for n, t, _, _ in outs), *states_in, *states_out, *extra)
+
 # ----------------------------------------------------------------- calls
 
 def _out_dtype(q, out_dtype, given):
@@ -239,14 +328,38 @@ def _out_dtype(q, out_dtype, given):
     return q.dtype if out_dtype is None else out_dtype
 
 
+def _piece_lengths(lengths, T):
+    lengths = [int(x) for x in lengths]
+    _need(len(lengths) >= 1, "lengths: need at least one piece")
+    _need(sum(lengths) == T, f"lengths sum to {sum(lengths)}, the sequence has {T} tokens")
+    return lengths
+
+
+def _outs(q, v, odt, **given):
+    """(name, tensor or None, dtype, width) for the activation outputs."""
+    DK, DV = q.shape[3], v.shape[3]
+    width = {"o": DV, "dq": DK, "dk": DK, "dv": DV}
+    return tuple((n, t, odt, width[n]) for n, t in given.items())
+
+
+def _new_act(q, d, odt, t):
+    B, H, T = q.shape[:3]
+    return torch.empty(B, H, T, d, dtype=odt, device=q.device) if t is None else t
+
+
 def fwd(q, k, v, decay=None, S_in=None, *, o=None, S_out=None, states=None, out_dtype=None):
     """Forward over one piece.  Returns (o, S_out, states)."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, o)
+    devs = _validate(q, k, v, decay, outs=_outs(q, v, odt, o=o), states_in=(("S_in", S_in),),
+              states_out=(("S_out", S_out),), extra=(("states", states),))
+    kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     B, H, T, dk = q.shape
     dv = v.shape[3]
-    o = torch.empty(B, H, T, dv, dtype=odt, device=q.device) if o is None else o
+    if states is not None:
+        _check_buffer("states", states, states_bytes(d))
+    _check_device(q, *devs)
+    o = _new_act(q, dv, odt, o)
     S_out = _state_out(q, B, H, dk, dv, S_out)
     if states is None:
         states = torch.empty(max(states_bytes(d), 16), dtype=torch.uint8, device=q.device)
@@ -260,14 +373,19 @@ def fwd(q, k, v, decay=None, S_in=None, *, o=None, S_out=None, states=None, out_
 def bwd(q, k, v, decay, states, dO, dS_out=None, *, dq=None, dk=None, dv=None,
         dS_in=None, workspace=None, out_dtype=None):
     """Backward over one piece.  Returns (dq, dk, dv, dS_in)."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+              states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+              extra=(("states", states), ("workspace", workspace)))
+    kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    _check_buffer("states", states, states_bytes(d))
+    if workspace is not None:
+        _check_buffer("workspace", workspace, bwd_workspace_bytes(d))
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
     dS_in = _state_out(q, B, H, DK, DV, dS_in)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(d), 16), dtype=torch.uint8, device=q.device)
@@ -286,14 +404,18 @@ def bwd_recompute(q, k, v, decay, S_in, dO, dS_out=None, *, dq=None, dk=None, dv
                   dS_in=None, workspace=None, out_dtype=None):
     """Backward over one piece from its boundary state S_in alone (the
     per-segment states are rebuilt).  Returns (dq, dk, dv, dS_in)."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+              states_in=(("S_in", S_in), ("dS_out", dS_out)), states_out=(("dS_in", dS_in),),
+              extra=(("workspace", workspace),))
+    kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    if workspace is not None:
+        _check_buffer("workspace", workspace, bwd_recompute_workspace_bytes(d))
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
     dS_in = _state_out(q, B, H, DK, DV, dS_in)
     if workspace is None:
         workspace = torch.empty(max(bwd_recompute_workspace_bytes(d), 16), dtype=torch.uint8,
@@ -317,14 +439,28 @@ def bwd_da(q, k, v, decay, states, dO, dS_out=None, da_carry=None, *, dq=None, d
     da_carry: fp32 [B,H], the gradient carried from later pieces (<dS_out,
     S_out>; None = 0).  Returns (dq, dk, dv, dS_in, da, da_carry_out) with
     da fp32 [B,H,T] and da_carry_out the carry for the previous piece."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, dq)
-    d = _desc_of(q, v, kind, odt)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+              states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+              extra=(("states", states), ("workspace", workspace), ("da", da),
+                     ("da_carry", da_carry), ("da_carry_out", da_carry_out)))
+    _need(decay is not None, "bwd_da: needs a decay tensor")
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    if da is not None:
+        _need(da.dtype == torch.float32 and tuple(da.shape) == (B, H, T),
+              f"da: must be float32 [B,H,T] = {(B, H, T)}, got {da.dtype} {tuple(da.shape)}")
+    for name, t in (("da_carry", da_carry), ("da_carry_out", da_carry_out)):
+        if t is not None:
+            _need(t.dtype == torch.float32 and tuple(t.shape) == (B, H) and t.is_contiguous(),
+                  f"{name}: must be contiguous float32 [B,H] = {(B, H)}")
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    _check_buffer("states", states, states_bytes(d))
+    if workspace is not None:
+        _check_buffer("workspace", workspace, bwd_da_workspace_bytes(d))
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
     dS_in = _state_out(q, B, H, DK, DV, dS_in)
     da = torch.empty(B, H, T, dtype=torch.float32, device=q.device) if da is None else da
     if da_carry_out is None:
@@ -347,12 +483,18 @@ def fwd_seq(q, k, v, decay, lengths: Sequence[int], S_in=None, *, o=None, S_out=
     """Sequence accumulation forward over consecutive pieces (native driver).
 
     Returns (o, S_out, states) with states covering the whole sequence."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, o)
+    devs = _validate(q, k, v, decay, outs=_outs(q, v, odt, o=o), states_in=(("S_in", S_in),),
+              states_out=(("S_out", S_out),), extra=(("states", states),))
+    lengths = _piece_lengths(lengths, q.shape[2])
+    kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     B, H, T, dk = q.shape
     dv = v.shape[3]
-    o = torch.empty(B, H, T, dv, dtype=odt, device=q.device) if o is None else o
+    if states is not None:
+        _check_buffer("states", states, seq_states_bytes(d, lengths))
+    _check_device(q, *devs)
+    o = _new_act(q, dv, odt, o)
     S_out = _state_out(q, B, H, dk, dv, S_out)
     if states is None:
         states = torch.empty(max(seq_states_bytes(d, lengths), 16), dtype=torch.uint8,
@@ -368,14 +510,20 @@ def fwd_seq(q, k, v, decay, lengths: Sequence[int], S_in=None, *, o=None, S_out=
 def bwd_seq(q, k, v, decay, lengths: Sequence[int], states, dO, dS_out=None, *, dq=None,
             dk=None, dv=None, dS_in=None, workspace=None, out_dtype=None):
     """Sequence accumulation backward (pieces in reverse, dS carried back)."""
-    kind, dec = _decay(decay)
     odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+              states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+              extra=(("states", states), ("workspace", workspace)))
+    lengths = _piece_lengths(lengths, q.shape[2])
+    kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    dq = torch.empty(q.shape, dtype=odt, device=q.device) if dq is None else dq
-    dk = torch.empty(k.shape, dtype=odt, device=q.device) if dk is None else dk
-    dv = torch.empty(v.shape, dtype=odt, device=q.device) if dv is None else dv
+    _check_buffer("states", states, seq_states_bytes(d, lengths))
+    if workspace is not None:
+        _check_buffer("workspace", workspace, bwd_seq_workspace_bytes(d, lengths))
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
     dS_in = _state_out(q, B, H, DK, DV, dS_in)
     if workspace is None:
         workspace = torch.empty(max(bwd_seq_workspace_bytes(d, lengths), 16), dtype=torch.uint8,

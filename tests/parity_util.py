@@ -1,17 +1,25 @@
 """Helpers shared by the GPU parity tests: oracle runs on sampled heads and
-the error measure.
+the error measures.
 
 err(X) = max |X_gpu - X_oracle| / RMS(X_oracle), per returned tensor; the
 bar is 2e-2 for bf16 activations and 1e-4 for fp32 ones.  The oracle eats
 the GPU's inputs exactly as stored (bf16 values upcast to fp64), so input
 quantisation is not counted as error.
 
-An output stored as bf16 cannot hold the exact result: rounding it costs up
-to half a unit in the last place, 2^-8 |x|, which alone exceeds 2e-2 RMS on
-the large elements of these workloads.  For bf16 outputs the error is
-therefore measured beyond that representation limit:
-    err_bf16(X) = max( |X_gpu - X_oracle| - 2^-8 |X_oracle| ) / RMS(X_oracle),
-and fp32 outputs (same kernels, no final rounding) are held to the plain bar.
+bf16 outputs.  An output stored as bf16 cannot hold the exact result:
+rounding the oracle's own fp64 values to bf16 (round to nearest even) already
+gives max|err|/RMS of 2.2e-2 to 3.4e-2 on the bf16 workloads, because their
+largest elements are 10 to 13 times the RMS and half an ulp is 2^-8 |x|.  No
+bf16-output result can meet the plain bar, so three figures are reported for
+bf16 outputs:
+    plain  = max |X_gpu - X_oracle| / RMS                      (printed)
+    floor  = max |rne_bf16(X_oracle) - X_oracle| / RMS         (printed: the
+             plain error of a perfect bf16 result)
+    excess = max( |X_gpu - X_oracle| - 2^-8 |X_oracle| ) / RMS (asserted <= bar)
+and fp32 outputs of the same kernels (no final rounding) are held to the
+plain bar.  That the bf16 store itself rounds to nearest even is checked
+separately (rne_mismatch): bf16 outputs must equal the fp32 outputs of the
+same kernels cast with round to nearest even.
 """
 from __future__ import annotations
 
@@ -30,14 +38,50 @@ def np64(t: torch.Tensor) -> np.ndarray:
 BF16_HALF_ULP = 2.0 ** -8
 
 
+def _rms(ref: np.ndarray) -> float:
+    return float(np.sqrt(np.mean(ref * ref)))
+
+
 def rel_err(got: torch.Tensor, ref: np.ndarray) -> float:
+    """The asserted measure: plain for fp32 outputs, excess beyond half a
+    bf16 ulp for bf16 outputs."""
     g = np64(got)
     allow = BF16_HALF_ULP * np.abs(ref) if got.dtype == torch.bfloat16 else 0.0
     excess = np.maximum(np.abs(g - ref) - allow, 0.0)
-    rms = float(np.sqrt(np.mean(ref * ref)))
+    rms = _rms(ref)
     if rms == 0.0:
         return float(np.max(excess))
     return float(np.max(excess) / rms)
+
+
+def plain_err(got: torch.Tensor, ref: np.ndarray) -> float:
+    rms = _rms(ref)
+    e = float(np.max(np.abs(np64(got) - ref)))
+    return e / rms if rms else e
+
+
+def bf16_floor(ref: np.ndarray) -> float:
+    """max|rne_bf16(ref) - ref| / RMS: what a correctly rounded bf16 result scores."""
+    r = torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy()
+    rms = _rms(ref)
+    e = float(np.max(np.abs(r - ref)))
+    return e / rms if rms else e
+
+
+def rne_mismatch(out_bf16: torch.Tensor, out_f32: torch.Tensor):
+    """Compare a bf16 output with the fp32 output of the same kernels cast to
+    bf16 (round to nearest even).  Returns (fraction of elements that differ,
+    largest difference in bf16 ulps of the fp32 value)."""
+    want = out_f32.to(torch.bfloat16)
+    diff = out_bf16.view(torch.int16).to(torch.int32) - want.view(torch.int16).to(torch.int32)
+    same_sign = (out_bf16.float() * want.float()) >= 0
+    nz = diff != 0
+    frac = float(nz.float().mean())
+    # bit patterns of same-sign finite bf16 values differ by the ulp count
+    ulps = int(diff.abs()[same_sign].max()) if bool(same_sign.any()) else 0
+    if bool((nz & ~same_sign).any()):
+        ulps = max(ulps, 1 << 16)
+    return frac, ulps
 
 
 def select_heads(x: torch.Tensor | None, heads):
@@ -73,10 +117,19 @@ def oracle_run(inp, heads=None, want_bwd=True, nthreads=None):
 
 
 def compare(got: dict, ref: dict, heads, tol: float):
-    """Per-tensor errors of GPU outputs (full [B,H,...] tensors) vs oracle."""
-    errs = {}
+    """Per-tensor errors of GPU outputs (full [B,H,...] tensors) vs oracle.
+
+    Returns (errs, bad, report): errs holds the asserted measure per tensor
+    (rel_err), bad those over tol, report a printable line that also gives
+    the plain error and, for bf16 outputs, the bf16 floor."""
+    errs, parts = {}, []
     for name, r in ref.items():
         g = select_heads(got[name], heads)
         errs[name] = rel_err(g, r)
+        if g.dtype == torch.bfloat16:
+            parts.append(f"{name}: plain={plain_err(g, r):.2e} floor={bf16_floor(r):.2e} "
+                         f"excess={errs[name]:.2e}")
+        else:
+            parts.append(f"{name}={errs[name]:.2e}")
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
-    return errs, bad
+    return errs, bad, " ".join(parts)

@@ -13,14 +13,16 @@ unsplit fp64 oracle on sampled heads over the whole sequence.
 
 Outputs are checked twice: fp32 outputs against the plain 2e-2 bar, and the
 bf16 outputs the benchmark produces beyond their half-ulp representation
-limit (see parity_util)."""
+limit, with the plain error and the error of a perfectly rounded bf16 result
+printed beside it (see parity_util); the bf16 outputs must also equal the
+fp32 outputs of the same kernels rounded to nearest even, on every head."""
 import os
 
 import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare, oracle_run
+from parity_util import TOL, compare, oracle_run, rne_mismatch
 from state_passing_amd import linrec
 from state_passing_amd.workloads import WORKLOADS, make_inputs
 
@@ -62,11 +64,22 @@ def test_fullsize_sequence_accumulation(idx):
     if wl.dtype != "bf16" or idx == 3:
         # the whole sequence as one piece (for sa-256k: 1024 segments a head)
         runs.append(([wl.T], torch.float32))
+    kept = {}
     for lens, odt in runs:
         got = run_sa(inp, lens, odt)
-        errs, bad = compare(got, ref, heads, tol)
-        print(f"[{wl.name} {len(lens)} pieces {odt}] "
-              + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        errs, bad, report = compare(got, ref, heads, tol)
+        print(f"[{wl.name} {len(lens)} pieces {odt}] {report}", flush=True)
         assert not bad, f"{wl.name} {len(lens)} pieces, outputs {odt}: over {tol}: {bad}"
-        del got
+        if lens is lengths:
+            kept[odt] = got
+        else:
+            del got
+    if torch.bfloat16 in kept:
+        # every head: the bf16 store is the fp32 result rounded to nearest even
+        for name in ("o", "dq", "dk", "dv"):
+            frac, ulps = rne_mismatch(kept[torch.bfloat16][name], kept[torch.float32][name])
+            print(f"  {name}: bf16 store vs rne(fp32 store), all heads: {frac:.2e} differ, "
+                  f"max {ulps} ulp", flush=True)
+            assert frac <= 1e-4 and ulps <= 1, (name, frac, ulps)
+    del kept
     torch.cuda.empty_cache()

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare, oracle_run
+from parity_util import TOL, compare, oracle_run, rne_mismatch
 from state_passing_amd import linrec
 from state_passing_amd.workloads import Workload, make_inputs
 
@@ -73,9 +73,19 @@ def run_loop(inp, lengths, out_dtype=None):
 
 def check(got, ref, heads, wl, label):
     tol = TOL[wl.torch_dtype]
-    errs, bad = compare(got, ref, heads, tol)
-    print(f"[{label}] {wl.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    errs, bad, report = compare(got, ref, heads, tol)
+    print(f"[{label}] {wl.name}: {report}", flush=True)
     assert not bad, f"{label} {wl.name}: over tolerance {tol}: {bad}"
+
+
+def check_rne(got16, got32, label):
+    """bf16 outputs are the fp32 results of the same kernels rounded to
+    nearest even."""
+    for name in ("o", "dq", "dk", "dv"):
+        frac, ulps = rne_mismatch(got16[name], got32[name])
+        print(f"  [{label}] {name}: bf16 store vs rne(fp32 store): {frac:.2e} differ, "
+              f"max {ulps} ulp", flush=True)
+        assert frac <= 1e-4 and ulps <= 1, (label, name, frac, ulps)
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
@@ -86,9 +96,12 @@ def test_small_unsplit(wl):
     inp = gpu_inputs(wl)
     ref = oracle_run(inp)
     heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
-    check(run_unsplit(inp, torch.float32), ref, heads, wl, "unsplit/f32-out")
+    got32 = run_unsplit(inp, torch.float32)
+    check(got32, ref, heads, wl, "unsplit/f32-out")
     if wl.dtype == "bf16":
-        check(run_unsplit(inp), ref, heads, wl, "unsplit/bf16-out")
+        got16 = run_unsplit(inp)
+        check(got16, ref, heads, wl, "unsplit/bf16-out")
+        check_rne(got16, got32, "unsplit")
 
 
 SPLIT_CASES = SMALL[:2] + SMALL[6:8] + SMALL[9:10]

@@ -198,6 +198,44 @@ def test_decay_gradient_identity():
                                    rtol=1e-10, atol=1e-10)
 
 
+@pytest.mark.parametrize("decay", ["token", "head"])
+def test_decay_gradient_across_checkpoint_blocks(decay):
+    """The oracle's da rebuilds S_{t-1} from a checkpoint every 256 tokens.
+    At T = 700 (two full blocks and a partial third) it is pinned two ways
+    that do not use that code:
+      * the suffix-sum identity a_r da_r = sum_{t >= r} g_t + <dS_out, S_out>,
+        g_t = q_t.dq_t - k_t.dk_t (dq, dk come from the plain sweeps);
+      * central differences of L in single a_t at the block edges.  L is
+        affine in each single a_t (every path through the recurrence meets
+        a_t once), so the central difference is exact up to rounding."""
+    rng = np.random.default_rng(31)
+    B, H, T, dk, dv = 1, 2, 700, 3, 4
+    q, k, v, a, S_in = rand_case(rng, B, H, T, dk, dv, decay=decay, lo=0.985)
+    dO = rng.standard_normal((B, H, T, dv))
+    dS_out = rng.standard_normal((B, H, dk, dv))
+    dq, dk_, dv_, dS_in, da = oracle.bwd(q, k, v, a, S_in, dO, dS_out, want_da=True)
+    _, S_out = oracle.fwd(q, k, v, a, S_in)
+    g = np.sum(q * dq, -1) - np.sum(k * dk_, -1)
+    carry = np.sum(dS_out * S_out, axis=(-2, -1))
+    suffix = np.cumsum(g[..., ::-1], -1)[..., ::-1] + carry[..., None]
+    af = decay_full(a, B, H, T)
+    scale = np.max(np.abs(suffix))
+    np.testing.assert_allclose(af * da, suffix, rtol=1e-11, atol=1e-11 * scale)
+    if decay != "token":
+        return
+    eps = 1e-5
+    for t in (0, 255, 256, 257, 511, 512, 699):
+        for h in range(H):
+            old = a[0, h, t]
+            a[0, h, t] = old + eps
+            lp = loss(q, k, v, a, S_in, dO, dS_out)
+            a[0, h, t] = old - eps
+            lm = loss(q, k, v, a, S_in, dO, dS_out)
+            a[0, h, t] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - da[0, h, t]) <= 1e-7 * max(1.0, abs(fd)), (t, h, fd, da[0, h, t])
+
+
 # ------------------------------------------------------ torch autograd
 
 

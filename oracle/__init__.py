@@ -24,18 +24,18 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "linrec_oracle.c")
+_SRCS = [os.path.join(_HERE, "linrec_oracle.c"), os.path.join(_HERE, "deltarule_oracle.c")]
 _LIB = os.path.join(_HERE, "liblinrec_oracle.so")
 
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc (-O2, OpenMP).  Returns the .so path."""
+    """Compile the C oracles with gcc (-O2, OpenMP).  Returns the .so path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, _SRC]
+               "-Wall", "-Wextra", "-o", tmp, *_SRCS]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -45,7 +45,7 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(map(os.path.getmtime, _SRCS)):
         build(force=True)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
@@ -67,6 +67,20 @@ def _load():
                                + [P]
                                + [P, I64, I64, I64]
                                + [I])
+    lib.delta_fwd.restype = I
+    lib.delta_fwd.argtypes = ([I, I, I64, I, I]
+                              + [P, I64, I64, I64] * 5
+                              + [P, P, I64, I64, I64, P, I])
+    lib.delta_bwd.restype = I
+    lib.delta_bwd.argtypes = ([I, I, I64, I, I]
+                              + [P, I64, I64, I64] * 5
+                              + [P]
+                              + [P, I64, I64, I64]
+                              + [P]
+                              + [P, I64, I64, I64] * 3
+                              + [P]
+                              + [P, I64, I64, I64] * 2
+                              + [I])
     lib.oracle_max_threads.restype = I
     lib.oracle_max_threads.argtypes = []
     _lib = lib
@@ -173,3 +187,78 @@ def bwd(q, k, v, a, S_in, dO, dS_out=None, want_da: bool = False,
     if want_da:
         return dq, dkk, dvv, dS_in, da
     return dq, dkk, dvv, dS_in
+
+
+# ------------------------------------------------------------ delta rule
+#
+# Gated delta rule (deltarule_oracle.c): S_t = a_t (I - beta_t k_t^T k_t)
+# S_{t-1} + beta_t k_t^T v_t, o_t = q_t S_t -- the recurrence of the Gated
+# DeltaNet models StateFlow trains (the gptget summary, "Experimental
+# design"), in the layer's d_k x d_v state orientation.
+
+
+def _beta(x, B, H, T):
+    if x.dtype != np.float64 or x.shape != (B, H, T):
+        raise ValueError(f"beta: need float64 [B,H,T], got {x.dtype} {x.shape}")
+    return x.ctypes.data, x.strides[0] // 8, x.strides[1] // 8, x.strides[2] // 8
+
+
+def delta_fwd(q, k, v, beta, a=None, S_in=None, nthreads: int | None = None,
+              want_o: bool = True):
+    """Delta-rule forward over one (sub-)sequence.  beta: [B,H,T].
+
+    Returns (o [B,H,T,dv] or None, S_out [B,H,dk,dv]), float64."""
+    lib = _load()
+    B, H, T, dk = k.shape
+    dv = v.shape[3]
+    S_in = None if S_in is None else np.ascontiguousarray(S_in, dtype=np.float64)
+    o = np.empty((B, H, T, dv), np.float64) if want_o else None
+    S_out = np.empty((B, H, dk, dv), np.float64)
+    qa = _act(q, "q", B, H, T, dk) if want_o else (None, 0, 0, 0)
+    oa = _act(o, "o", B, H, T, dv) if want_o else (None, 0, 0, 0)
+    nt = nthreads or min(B * H, max_threads()) or 1
+    rc = lib.delta_fwd(B, H, T, dk, dv, *qa, *_act(k, "k", B, H, T, dk),
+                       *_act(v, "v", B, H, T, dv), *_beta(beta, B, H, T), *_decay(a, B, H, T),
+                       _state(S_in, "S_in", B, H, dk, dv), *oa, S_out.ctypes.data, nt)
+    if rc != 0:
+        raise RuntimeError("delta_fwd: bad arguments")
+    return o, S_out
+
+
+def delta_bwd(q, k, v, beta, a, S_in, dO, dS_out=None, want_da: bool = False,
+              nthreads: int | None = None):
+    """Backward of L = <dO, o> + <dS_out, S_out> through the delta rule.
+
+    Returns (dq, dk, dv, dbeta, dS_in) -- plus da [B,H,T] when want_da."""
+    lib = _load()
+    B, H, T, dk = k.shape
+    dv = v.shape[3]
+    S_in = None if S_in is None else np.ascontiguousarray(S_in, dtype=np.float64)
+    dS_out = None if dS_out is None else np.ascontiguousarray(dS_out, dtype=np.float64)
+    dq = np.empty((B, H, T, dk), np.float64)
+    dkk = np.empty((B, H, T, dk), np.float64)
+    dvv = np.empty((B, H, T, dv), np.float64)
+    dbeta = np.empty((B, H, T), np.float64)
+    dS_in = np.empty((B, H, dk, dv), np.float64)
+    da = None
+    daa = (None, 0, 0, 0)
+    if want_da:
+        if a is None:
+            raise ValueError("da needs a decay tensor")
+        da = np.empty((B, H, T), np.float64)
+        daa = (da.ctypes.data, T * H, T, 1)
+    nt = nthreads or min(B * H, max_threads()) or 1
+    rc = lib.delta_bwd(B, H, T, dk, dv,
+                       *_act(q, "q", B, H, T, dk), *_act(k, "k", B, H, T, dk),
+                       *_act(v, "v", B, H, T, dv), *_beta(beta, B, H, T), *_decay(a, B, H, T),
+                       _state(S_in, "S_in", B, H, dk, dv),
+                       *(_act(dO, "dO", B, H, T, dv) if dO is not None else (None, 0, 0, 0)),
+                       _state(dS_out, "dS_out", B, H, dk, dv),
+                       *_act(dq, "dq", B, H, T, dk), *_act(dkk, "dk", B, H, T, dk),
+                       *_act(dvv, "dv", B, H, T, dv), dS_in.ctypes.data,
+                       dbeta.ctypes.data, T * H, T, 1, *daa, nt)
+    if rc != 0:
+        raise RuntimeError("delta_bwd: bad arguments")
+    if want_da:
+        return dq, dkk, dvv, dbeta, dS_in, da
+    return dq, dkk, dvv, dbeta, dS_in

@@ -99,7 +99,9 @@ typedef enum {
     LINREC_E_ALIGN = 5,     /* a pointer or stride breaks 16-byte row alignment */
     LINREC_E_WORKSPACE = 6, /* states/workspace pointer missing or misaligned */
     LINREC_E_DEVICE = 7,    /* HIP runtime error outside a launch             */
-    LINREC_E_LAUNCH = 8     /* a kernel launch failed                         */
+    LINREC_E_LAUNCH = 8,    /* a kernel launch failed                         */
+    LINREC_E_SCRATCH = 9    /* the call needs more than the fixed scratch of
+                               linrec_bwd_noalloc                             */
 } linrec_status;
 
 typedef enum { LINREC_BF16 = 0, LINREC_F32 = 1 } linrec_dtype;
@@ -178,6 +180,31 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d,
                          linrec_tensor dO, const float* dS_out,
                          linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
                          float* dS_in, void* workspace, void* stream);
+
+/* Size of the fixed device scratch linrec_bwd_noalloc works in. */
+#define LINREC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* linrec_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The gradient records linrec_bwd keeps
+ * in its workspace live instead in a static device array of
+ * LINREC_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU
+ * it runs on until the process ends; nothing is allocated or freed by the
+ * call.  Arguments, results and rules are those of linrec_bwd (results equal
+ * linrec_bwd's bit for bit).  A piece whose workspace
+ * (linrec_bwd_workspace_bytes(d)) exceeds the scratch is rejected with
+ * LINREC_E_SCRATCH before anything is enqueued; e.g. B*H = 16 heads of
+ * d_k = d_v = 128 fit pieces of up to 7936 tokens.  Every call on one GPU
+ * shares that GPU's scratch: calls that may run concurrently on one GPU
+ * (different streams, different threads) race and must be serialised by the
+ * caller.  The scratch is written before it is read within each call, so it
+ * needs no clearing between calls. */
+linrec_status linrec_bwd_noalloc(linrec_ctx* ctx, const linrec_desc* d,
+                                 linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                                 linrec_tensor decay, const void* states,
+                                 linrec_tensor dO, const float* dS_out,
+                                 linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                 float* dS_in, void* stream);
 
 /* Bytes of workspace linrec_bwd_recompute needs (0 if `d` is invalid): the
  * piece's rebuilt state records, its gradient records and one fp32 state

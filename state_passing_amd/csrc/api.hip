@@ -26,6 +26,8 @@ struct TimedLaunch {
 
 struct linrec_ctx {
     int device;
+    void* scratch;          // this device's address of the no-allocation scratch
+    hipError_t scratch_err; // result of looking that address up
     hipStream_t aux;        // state transitions
     hipEvent_t ev_start;    // inputs ready on the caller's stream
     hipEvent_t ev_scan;     // a piece's scan finished (aux)
@@ -36,6 +38,13 @@ struct linrec_ctx {
     double ms[LINREC_KERNEL_KINDS];
     int64_t count[LINREC_KERNEL_KINDS];
 };
+
+// Scratch of linrec_bwd_noalloc: the gradient records of one piece.  Each
+// GPU the library runs on holds its own copy for the life of the process.
+// In host code this name is only a stand-in for the symbol: kernels and
+// runtime calls get the device address that linrec_ctx_create looks up with
+// hipGetSymbolAddress (ctx->scratch).
+static __device__ __align__(256) unsigned char scratch[LINREC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -411,6 +420,13 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device)
         e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&c->ev_scan, hipEventDisableTiming);
+    // the no-allocation scratch's address on this device (the device is
+    // current); a failure here only disables linrec_bwd_noalloc
+    if (e == hipSuccess) {
+        c->scratch_err = hipGetSymbolAddress(&c->scratch, HIP_SYMBOL(scratch));
+        if (c->scratch_err != hipSuccess)
+            c->scratch = nullptr;
+    }
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         linrec_ctx_destroy(c);
@@ -559,6 +575,35 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
     const BwdIntraLaunch in =
         bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0, ns, workspace);
+    LAUNCH_SCAN(ctx, sc, s);
+    LAUNCH_BWD_INTRA(ctx, in, s);
+    return LINREC_OK;
+}
+
+linrec_status linrec_bwd_noalloc(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                                 linrec_tensor k, linrec_tensor v, linrec_tensor decay,
+                                 const void* states, linrec_tensor dO, const float* dS_out,
+                                 linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                 float* dS_in, void* stream)
+{
+    // the workspace check is done against the scratch below; any aligned
+    // non-NULL pointer stands in for it in the common argument checks
+    linrec_status st = check_bwd_args(d, q, k, v, decay, states, dO, dS_out, dq, dk, dv,
+                                      dS_in, states);
+    if (st != LINREC_OK)
+        return st;
+    if (linrec_bwd_workspace_bytes(d) > LINREC_NOALLOC_SCRATCH_BYTES)
+        return LINREC_E_SCRATCH;
+    if ((st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    if (!ctx->scratch)
+        return hip_fail(ctx->scratch_err != hipSuccess ? ctx->scratch_err : hipErrorInvalidSymbol,
+                        LINREC_E_DEVICE);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t ns = nseg_of(d->T);
+    const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, ctx->scratch);
+    const BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, 0, d->T, states, 0,
+                                           ns, ctx->scratch);
     LAUNCH_SCAN(ctx, sc, s);
     LAUNCH_BWD_INTRA(ctx, in, s);
     return LINREC_OK;
@@ -714,6 +759,7 @@ const char* linrec_status_str(linrec_status s)
     case LINREC_E_WORKSPACE: return "states/workspace missing or misaligned";
     case LINREC_E_DEVICE: return "HIP runtime error";
     case LINREC_E_LAUNCH: return "kernel launch failed";
+    case LINREC_E_SCRATCH: return "the piece needs more than the fixed no-allocation scratch";
     }
     return "unknown status";
 }

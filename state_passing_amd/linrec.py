@@ -29,8 +29,11 @@ DECAY_NONE, DECAY_HEAD, DECAY_TOKEN = 0, 1, 2
 STATUS = {
     0: "LINREC_OK", 1: "LINREC_E_NULL", 2: "LINREC_E_SHAPE", 3: "LINREC_E_DTYPE",
     4: "LINREC_E_LAYOUT", 5: "LINREC_E_ALIGN", 6: "LINREC_E_WORKSPACE",
-    7: "LINREC_E_DEVICE", 8: "LINREC_E_LAUNCH",
+    7: "LINREC_E_DEVICE", 8: "LINREC_E_LAUNCH", 9: "LINREC_E_SCRATCH",
 }
+
+# Fixed device scratch of linrec_bwd_noalloc (LINREC_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every function include/linrec.h declares.
 EXPORTS = (
@@ -39,7 +42,7 @@ EXPORTS = (
     "linrec_bwd_seq_workspace_bytes", "linrec_bwd_seq", "linrec_status_str",
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
     "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
-    "linrec_bwd_da_workspace_bytes", "linrec_bwd_da",
+    "linrec_bwd_da_workspace_bytes", "linrec_bwd_da", "linrec_bwd_noalloc",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
@@ -91,6 +94,7 @@ def _lib():
         "linrec_bwd_recompute_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_recompute": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_bwd_da_workspace_bytes": ([D], ctypes.c_size_t),
+        "linrec_bwd_noalloc": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P], ctypes.c_int),
         "linrec_bwd_da": ([P, D, T, T, T, T, P, T, P, T, T, T, P, T, P, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
@@ -393,6 +397,31 @@ def bwd(q, k, v, decay, states, dO, dS_out=None, *, dq=None, dk=None, dv=None,
                            dec, _ptr(states), _act(dO), _ptr(dS_out), _act(dq), _act(dk),
                            _act(dv), _ptr(dS_in), _ptr(workspace), _stream(q.device))
     _check(rc, "linrec_bwd")
+    return dq, dk, dv, dS_in
+
+
+def bwd_noalloc(q, k, v, decay, states, dO, dS_out=None, *, dq=None, dk=None, dv=None,
+                dS_in=None, out_dtype=None):
+    """linrec_bwd_noalloc: the backward of one piece in the library's fixed
+    device scratch (no workspace).  The library call allocates nothing; pass
+    dq, dk, dv and dS_in to keep this wrapper from allocating them.  Returns
+    (dq, dk, dv, dS_in)."""
+    odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+                     states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+                     extra=(("states", states),))
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    _check_buffer("states", states, states_bytes(d))
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
+    dS_in = _state_out(q, B, H, DK, DV, dS_in)
+    rc = _lib().linrec_bwd_noalloc(context(q.device.index), ctypes.byref(d), _act(q), _act(k),
+                                   _act(v), dec, _ptr(states), _act(dO), _ptr(dS_out), _act(dq),
+                                   _act(dk), _act(dv), _ptr(dS_in), _stream(q.device))
+    _check(rc, "linrec_bwd_noalloc")
     return dq, dk, dv, dS_in
 
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_status_strings():
     lib = linrec._lib()
     assert lib.linrec_version() >= 100
-    for code in range(9):
+    for code in range(10):
         assert lib.linrec_status_str(code)
     assert lib.linrec_status_str(99) == b"unknown status"
 
@@ -212,3 +212,22 @@ def test_null_desc_and_ctx_destroy_null():
                           act(), FAKE, FAKE, None) == E["LINREC_E_NULL"]
     assert lib.linrec_ctx_destroy(None) == 0
     assert lib.linrec_ctx_create(None, 0) == E["LINREC_E_NULL"]
+
+
+def test_noalloc_arguments():
+    """The no-allocation backward checks its arguments like linrec_bwd and
+    rejects a piece whose gradient records exceed the fixed scratch before
+    looking at the context."""
+    lib = linrec._lib()
+
+    def call(desc, states=FAKE, dS_in=FAKE):
+        return lib.linrec_bwd_noalloc(None, ctypes.byref(desc), act(), act(), act(),
+                                      linrec.Tensor(FAKE, 0, 1, 0), states, act(), None, act(),
+                                      act(), act(), dS_in, None)
+    assert call(d()) == E["LINREC_E_NULL"]                 # checks pass, no context
+    assert call(d(T=7936)) == E["LINREC_E_NULL"]           # 31 segments: fits 32 MiB
+    assert linrec.bwd_workspace_bytes(d(T=7936)) <= linrec.NOALLOC_SCRATCH_BYTES
+    assert call(d(T=8192)) == E["LINREC_E_SCRATCH"]        # 32 segments: does not
+    assert call(d(T=100)) == E["LINREC_E_SHAPE"]
+    assert call(d(), states=None) == E["LINREC_E_WORKSPACE"]
+    assert call(d(), dS_in=None) == E["LINREC_E_NULL"]

@@ -117,35 +117,41 @@ def traffic_from_profile(kernel: str, launch_units: int):
     return float(m.group(1)) if m else None
 
 
-def mfma_busy_from_profile():
-    """The dominant kernel's MFMA busy percentage from the committed shader
-    counter summary; None if missing or taken on other kernel code."""
+def mfma_busy_from_profile(kernel: str):
+    """A kernel's MFMA busy percentage from the committed shader counter
+    summary; None if missing or taken on other kernel code."""
     if not os.path.exists(SQ_FILE):
         return None
     txt = open(SQ_FILE).read()
     m = re.search(r"kernel_source_sha256_16:\s*(\w+)", txt)
     if not m or m.group(1) != kernel_source_hash():
         return None
-    m = re.search(r"mfma_busy_pct_bwd_seg:\s*([0-9.eE+]+)", txt)
+    m = re.search(r"mfma_busy_pct_%s:\s*([0-9.eE+]+)" % kernel, txt)
     return float(m.group(1)) if m else None
 
 
-def copy_probe(nbytes: int) -> None:
+def copy_probe(nbytes: int) -> float:
+    """Read + write GB/s of a plain device copy of `nbytes` (torch's copy
+    kernel), timed with events over 10 copies after 3 untimed ones: the HBM
+    rate a streaming kernel can reach on this GPU, beside the 8 TB/s spec."""
     import torch
     n = nbytes // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     reps = 10
+    a.record()
     for _ in range(reps):
         dst.copy_(src)
+    b.record()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    print(json.dumps({"copy_probe_bytes": nbytes, "read_plus_write_GBs": 2 * nbytes / dt / 1e9}))
+    dt = a.elapsed_time(b) * 1e-3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
 
 
 def cpu_baseline(inp, wl, sample_tokens: int):
@@ -158,14 +164,15 @@ def cpu_baseline(inp, wl, sample_tokens: int):
     f64 = lambda t: np.ascontiguousarray(t[:, :, sl].to("cpu", torch.float64).numpy())  # noqa: E731
     q, k, v, dO = f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.dO)
     a = inp.decay.to("cpu", torch.float64).numpy()
-    threads = min(wl.B * wl.H, len(os.sched_getaffinity(0)))
+    available = len(os.sched_getaffinity(0))
+    threads = min(wl.B * wl.H, available)
     t0 = time.perf_counter()
     oracle.fwd(q, k, v, a, None, nthreads=threads)
     t1 = time.perf_counter()
     oracle.bwd(q, k, v, a, None, dO, None, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": wl.B * sample_tokens / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "cores_available": available, "cpu_count": os.cpu_count(), "kind": "oracle",
             "sample": f"fwd+bwd, unsplit, all {wl.B * wl.H} heads, first {sample_tokens} of "
                       f"{wl.T} tokens ({dt:.1f} s)",
             "fwd_tokens_per_s": wl.B * sample_tokens / (t1 - t0)}
@@ -179,7 +186,8 @@ def main():
         sys.exit(2)
     import torch
     if args.copy_probe:
-        copy_probe(args.copy_probe)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe,
+                          "read_plus_write_GBs": copy_probe(args.copy_probe)}))
         return
 
     from state_passing_amd import linrec
@@ -292,6 +300,9 @@ def main():
                 "algorithmic_bytes_per_launch": KERNEL_BYTES[dominant] * token_heads_piece,
                 "design_bytes_per_launch": KERNEL_DESIGN_BYTES[dominant] * token_heads_piece,
                 "avg_launch_us": dom["avg_us"]}
+    if not args.profile:
+        # what a plain streaming copy reaches on this GPU, beside the spec peak
+        roofline["copy_probe_GBs"] = copy_probe(1 << 30)
     if args.profile:
         print(json.dumps({"ms_per_step_serialized": ms_serial, "kernels": kernels,
                           "roofline": roofline}))
@@ -365,7 +376,7 @@ def main():
         "fwd_tokens_per_s": tokens / (fwd_only_ms * 1e-3),
         "fwd_ms": fwd_only_ms,
         "mfma_util_pct": 100.0 * flops_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "bwd_seg_mfma_busy_pct_counters": mfma_busy_from_profile(),
+        "mfma_busy_pct_counters": {k: mfma_busy_from_profile(k) for k in ("fwd_seg", "bwd_seg")},
         "hbm_roof_pct_minimal_bytes": 100.0 * (FWD_BYTES + BWD_BYTES) * B * H * T
                                       / (ms_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "fwd_mfma_util_pct": 100.0 * FWD_FLOPS * B * H * T / (fwd_only_ms * 1e-3)

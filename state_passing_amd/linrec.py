@@ -244,50 +244,65 @@ def _check(rc, where):
 # the GPU.  These checks run before any library call; the device check comes
 # last so that every structural mistake is reported as such.
 
-def _need(cond: bool, msg: str, exc=ValueError):
-    if not cond:
-        raise exc(msg)
+def _fail(msg: str, exc=ValueError):
+    raise exc(msg)
 
 
 def _check_act(name, t, shape, dtype=None):
-    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
-    _need(t.dim() == 4, f"{name}: must be [B,H,T,d], got {tuple(t.shape)}")
-    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
-    if dtype is not None:
-        _need(t.dtype == dtype, f"{name}: dtype {t.dtype} != {dtype}", TypeError)
-    _need(t.stride(-1) == 1, f"{name}: the feature dimension must be contiguous (stride 1)")
+    # conditions first, messages only on failure (this runs on every call)
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name}: expected a tensor", TypeError)
+    if t.dim() != 4:
+        _fail(f"{name}: must be [B,H,T,d], got {tuple(t.shape)}")
+    if t.shape != shape:
+        _fail(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        _fail(f"{name}: dtype {t.dtype} != {dtype}", TypeError)
+    if t.stride(-1) != 1:
+        _fail(f"{name}: the feature dimension must be contiguous (stride 1)")
 
 
 def _check_state(name, t, shape):
     if t is None:
         return
-    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
-    _need(t.dtype == torch.float32, f"{name}: must be float32, got {t.dtype}", TypeError)
-    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
-    _need(t.is_contiguous(), f"{name}: must be contiguous")
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name}: expected a tensor", TypeError)
+    if t.dtype != torch.float32:
+        _fail(f"{name}: must be float32, got {t.dtype}", TypeError)
+    if t.shape != shape:
+        _fail(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if not t.is_contiguous():
+        _fail(f"{name}: must be contiguous")
 
 
 def _check_decay(decay, B, H, T):
     if decay is None:
         return
-    _need(isinstance(decay, torch.Tensor), "decay: expected a tensor", TypeError)
-    _need(decay.dtype == torch.float32, "decay must be float32", TypeError)
-    _need(tuple(decay.shape) in ((H,), (B, H, T)), f"decay must be [H] or [B,H,T], got "
-          f"{tuple(decay.shape)} for B={B} H={H} T={T}")
+    if not isinstance(decay, torch.Tensor):
+        _fail("decay: expected a tensor", TypeError)
+    if decay.dtype != torch.float32:
+        _fail("decay must be float32", TypeError)
+    if decay.shape != (H,) and decay.shape != (B, H, T):
+        _fail(f"decay must be [H] or [B,H,T], got {tuple(decay.shape)} for B={B} H={H} T={T}")
 
 
 def _check_buffer(name, t, nbytes):
-    _need(isinstance(t, torch.Tensor), f"{name}: expected a tensor", TypeError)
-    _need(t.is_contiguous(), f"{name}: must be contiguous")
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name}: expected a tensor", TypeError)
+    if not t.is_contiguous():
+        _fail(f"{name}: must be contiguous")
     have = t.numel() * t.element_size()
-    _need(have >= nbytes, f"{name}: {have} bytes, the call needs {nbytes}")
+    if have < nbytes:
+        _fail(f"{name}: {have} bytes, the call needs {nbytes}")
 
 
 def _check_device(q, *others):
-    _need(q.is_cuda, f"tensors must be on a GPU, got {q.device}")
+    if not q.is_cuda:
+        _fail(f"tensors must be on a GPU, got {q.device}")
+    dev = q.device
     for name, t in others:
-        if t is not None:
-            _need(t.device == q.device, f"{name}: on {t.device}, q on {q.device}")
+        if t is not None and t.device != dev:
+            _fail(f"{name}: on {t.device}, q on {dev}")
 
 
 def _validate(q, k, v, decay, *, dO=None, outs=(), states_in=(), states_out=(), extra=()):
@@ -298,29 +313,38 @@ def _validate(q, k, v, decay, *, dO=None, outs=(), states_in=(), states_out=(), 
     extra: (name, tensor or None) other tensors that only need the device check.
     Returns the (name, tensor) pairs for _check_device, which the caller runs
     after its buffer-size checks, so that structural errors are reported first."""
-    _need(isinstance(q, torch.Tensor), "q: expected a tensor", TypeError)
-    _need(q.dim() == 4, f"q: must be [B,H,T,d_k], got {tuple(q.shape)}")
+    if not isinstance(q, torch.Tensor):
+        _fail("q: expected a tensor", TypeError)
+    if q.dim() != 4:
+        _fail(f"q: must be [B,H,T,d_k], got {tuple(q.shape)}")
     B, H, T, DK = q.shape
-    _need(q.dtype in (torch.bfloat16, torch.float32), f"unsupported activation dtype {q.dtype}",
-          TypeError)
-    _check_act("q", q, (B, H, T, DK), q.dtype)
-    _check_act("k", k, (B, H, T, DK), q.dtype)
-    _need(isinstance(v, torch.Tensor) and v.dim() == 4, "v: must be [B,H,T,d_v]")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        _fail(f"unsupported activation dtype {q.dtype}", TypeError)
+    qs = q.shape
+    _check_act("q", q, qs, q.dtype)
+    _check_act("k", k, qs, q.dtype)
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        _fail("v: must be [B,H,T,d_v]")
     DV = v.shape[3]
-    _check_act("v", v, (B, H, T, DV), q.dtype)
+    vs = torch.Size((B, H, T, DV))
+    _check_act("v", v, vs, q.dtype)
     if dO is not None:
-        _check_act("dO", dO, (B, H, T, DV), q.dtype)
+        _check_act("dO", dO, vs, q.dtype)
     _check_decay(decay, B, H, T)
     odts = set()
     for name, t, odt, d in outs:
         if t is not None:
-            _check_act(name, t, (B, H, T, d))
+            _check_act(name, t, torch.Size((B, H, T, d)))
             odts.add(t.dtype)
         else:
             odts.add(odt)
-    _need(len(odts) <= 1, f"outputs must share one dtype, got {sorted(map(str, odts))}", TypeError)
-    for name, t in tuple(states_in) + tuple(states_out):
-        _check_state(name, t, (B, H, DK, DV))
+    if len(odts) > 1:
+        _fail(f"outputs must share one dtype, got {sorted(map(str, odts))}", TypeError)
+    ss = torch.Size((B, H, DK, DV))
+    for name, t in states_in:
+        _check_state(name, t, ss)
+    for name, t in states_out:
+        _check_state(name, t, ss)
     return (("k", k), ("v", v), ("dO", dO), ("decay", decay),
             *((n, t) for n, t, _, _ in outs), *states_in, *states_out, *extra)
 
@@ -334,8 +358,10 @@ def _out_dtype(q, out_dtype, given):
 
 def _piece_lengths(lengths, T):
     lengths = [int(x) for x in lengths]
-    _need(len(lengths) >= 1, "lengths: need at least one piece")
-    _need(sum(lengths) == T, f"lengths sum to {sum(lengths)}, the sequence has {T} tokens")
+    if not lengths:
+        _fail("lengths: need at least one piece")
+    if sum(lengths) != T:
+        _fail(f"lengths sum to {sum(lengths)}, the sequence has {T} tokens")
     return lengths
 
 
@@ -473,16 +499,16 @@ def bwd_da(q, k, v, decay, states, dO, dS_out=None, da_carry=None, *, dq=None, d
               states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
               extra=(("states", states), ("workspace", workspace), ("da", da),
                      ("da_carry", da_carry), ("da_carry_out", da_carry_out)))
-    _need(decay is not None, "bwd_da: needs a decay tensor")
+    if decay is None:
+        _fail("bwd_da: needs a decay tensor")
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    if da is not None:
-        _need(da.dtype == torch.float32 and tuple(da.shape) == (B, H, T),
-              f"da: must be float32 [B,H,T] = {(B, H, T)}, got {da.dtype} {tuple(da.shape)}")
+    if da is not None and (da.dtype != torch.float32 or da.shape != (B, H, T)):
+        _fail(f"da: must be float32 [B,H,T] = {(B, H, T)}, got {da.dtype} {tuple(da.shape)}")
     for name, t in (("da_carry", da_carry), ("da_carry_out", da_carry_out)):
-        if t is not None:
-            _need(t.dtype == torch.float32 and tuple(t.shape) == (B, H) and t.is_contiguous(),
-                  f"{name}: must be contiguous float32 [B,H] = {(B, H)}")
+        if t is not None and (t.dtype != torch.float32 or t.shape != (B, H) or
+                              not t.is_contiguous()):
+            _fail(f"{name}: must be contiguous float32 [B,H] = {(B, H)}")
     kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     _check_buffer("states", states, states_bytes(d))

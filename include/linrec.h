@@ -279,7 +279,8 @@ linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              linrec_tensor o, float* S_out, void* states,
                              void* stream);
 
-/* Bytes of workspace linrec_bwd_seq needs for these pieces (0 if invalid). */
+/* Bytes of workspace linrec_bwd_seq needs for these pieces (0 if invalid):
+ * two slots, each holding the gradient records of the longest piece. */
 size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
                                       const int32_t* lengths);
 
@@ -289,9 +290,11 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
  * Accumulation and Beyond, "Approach"; boundary gradients carried from piece
  * to piece: StateFlow, Abstract).  Every launch goes to `stream` (the
  * backward segment kernel occupies a whole CU, so a concurrent transition
- * kernel would only delay it).  The workspace holds the gradient records of
- * one piece, reused piece after piece.  Same arguments and rules as
- * linrec_bwd otherwise; `states` as written by linrec_fwd_seq. */
+ * kernel would only delay it).  Piece i - 1's reverse fold, which needs
+ * piece i's dS_in, travels inside piece i's segment-kernel launch; the
+ * gradient records of consecutive pieces alternate between the workspace's
+ * two slots.  Same arguments and rules as linrec_bwd otherwise; `states` as
+ * written by linrec_fwd_seq. */
 linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              int32_t npieces, const int32_t* lengths,
                              linrec_tensor q, linrec_tensor k, linrec_tensor v,
@@ -300,6 +303,45 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              linrec_tensor dq, linrec_tensor dk,
                              linrec_tensor dv, float* dS_in, void* workspace,
                              void* stream);
+
+/* ------------------------------------------------------------ delta rule
+ * The gated delta rule, per batch b and head h (one sub-sequence):
+ *
+ *   S_0 = S_in,  S_t = a_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t,
+ *   o_t = q_t S_t,  S_out = S_T
+ *
+ * the recurrence of the Gated DeltaNet models StateFlow trains (the gptget
+ * summary, "Experimental design"), with the layer's d_k x d_v state.  The
+ * erase term acts on the key dimension: with |k_t| = 1 and beta_t = 1 the
+ * state read at k_t after the update is exactly v_t.  Pieces chain through
+ * S_out -> S_in as for the linear recurrence.
+ *
+ * Chunkwise (64 tokens): per chunk, the new values U solve the unit
+ * lower-triangular system (I + A) U = diag(beta) (V - diag(gamma) K S_0)
+ * with A_ij = beta_i (gamma_i / gamma_j) k_i . k_j for j < i; a first kernel
+ * forms T = (I + A)^{-1}, W_v = T diag(beta) V and W_k = T diag(beta gamma) K
+ * for every chunk in parallel, a second carries S across the chunks (the
+ * transition is S <- gamma_C S + K~^T (W_v - W_k S)), 16 state columns per
+ * workgroup, and writes O = diag(gamma) Q S_0 + [(Q K^T) .* D] U.  Products
+ * of two computed operands use bf16 hi + lo pairs on both sides; the state
+ * is carried in fp32.
+ */
+
+/* Bytes of workspace linrec_delta_fwd needs (0 if `d` is invalid or
+ * d_k != d_v): W_k and W_v of every token, fp32, B*H*T*(d_k + d_v)*4. */
+size_t linrec_delta_workspace_bytes(const linrec_desc* d);
+
+/* Delta-rule forward over one piece.
+ *   q, k: [B,H,T,d_k]; v, o: [B,H,T,d_v]; d_k == d_v (64 or 128; fp32 inputs
+ *   only at 64).  beta: fp32 [B,H,T] with strides (sb, sh, st), values in
+ *   [0, 1].  decay per d->decay (as linrec_fwd; the gate a_t).  S_in: fp32
+ *   [B,H,d_k,d_v] or NULL (zeros).  S_out: fp32, required, may alias S_in.
+ *   workspace: linrec_delta_workspace_bytes(d) bytes, 16-byte aligned.
+ * Errors and ownership as linrec_fwd. */
+linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d,
+                               linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                               linrec_tensor beta, linrec_tensor decay, const float* S_in,
+                               linrec_tensor o, float* S_out, void* workspace, void* stream);
 
 /* Kernel kinds for linrec_ctx_kernel_times(). */
 enum {
@@ -310,7 +352,8 @@ enum {
     LINREC_KERNEL_BWD_FOLD = 4,   /* reverse fold across segments (dS carried) */
     LINREC_KERNEL_BWD_SEG = 5,    /* backward segment kernel: dQ, dK, dV       */
     LINREC_KERNEL_DA_FINISH = 6,  /* decay gradient, last step                 */
-    LINREC_KERNEL_KINDS = 7
+    LINREC_KERNEL_DELTA_FWD = 7,  /* delta rule forward (both of its kernels)  */
+    LINREC_KERNEL_KINDS = 8
 };
 
 /* Per-kernel timing (instrumentation, off by default).  While enabled, every

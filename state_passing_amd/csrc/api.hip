@@ -536,11 +536,18 @@ size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int3
     return (size_t)d->B * (size_t)d->H * (size_t)total_nseg(npieces, lengths) * per_seg_bytes(d);
 }
 
+// Two slots of gradient records, each sized for the longest piece: piece
+// i - 1's are summed and folded while piece i's are read.
+size_t bwd_seq_slot_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
+{
+    return (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
+}
+
 size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
         return 0;
-    return (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
+    return 2 * bwd_seq_slot_bytes(d, npieces, lengths);
 }
 
 linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
@@ -727,23 +734,79 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         return st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t nseg_total = total_nseg(npieces, lengths);
-    // Every launch goes to the caller's stream, one piece after another.
-    // The backward segment kernel fills a CU's LDS, so transition kernels
-    // on a second stream cannot share a CU with it; running them
-    // concurrently only delays its workgroups.
-    int64_t tok_end = d->T, seg_end = nseg_total;
-    for (int32_t i = npieces - 1; i >= 0; --i) {
-        const int64_t tok0 = tok_end - lengths[i];
-        const int64_t seg0 = seg_end - nseg_of(lengths[i]);
-        const float* cin = i == npieces - 1 ? dS_out : dS_in;
-        const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, tok0, lengths[i], cin, dS_in, workspace);
-        const BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0, lengths[i],
-                                               states, seg0, nseg_total, workspace);
-        LAUNCH_SCAN(ctx, sc, s);
-        LAUNCH_BWD_INTRA(ctx, in, s);
-        tok_end = tok0;
-        seg_end = seg0;
+    // Every launch goes to the caller's stream, one piece after another (the
+    // backward segment kernel fills each CU's LDS, so transition kernels on a
+    // second stream would only delay its workgroups).  Piece i - 1's segment
+    // sums run before piece i's segment kernel, and piece i - 1's fold (which
+    // needs piece i's dS_in) travels inside that launch; only the last
+    // piece's fold has a launch of its own.  The gradient records of
+    // consecutive pieces alternate between the workspace's two slots.
+    const size_t slot_bytes = bwd_seq_slot_bytes(d, npieces, lengths);
+    auto slot_ptr = [&](int32_t i) { return (void*)((char*)workspace + (i & 1) * slot_bytes); };
+    std::vector<int64_t> tok0s(npieces), seg0s(npieces);
+    for (int32_t i = 0, t0 = 0, g0 = 0; i < npieces; ++i) {
+        tok0s[i] = t0;
+        seg0s[i] = g0;
+        t0 += lengths[i];
+        g0 += (int32_t)nseg_of(lengths[i]);
     }
+    auto scan_of = [&](int32_t i, const float* cin) {
+        return bwd_scan_of(d, q, dO, decay, tok0s[i], lengths[i], cin, dS_in, slot_ptr(i));
+    };
+    const ScanLaunch last = scan_of(npieces - 1, dS_out);
+    LAUNCH_SCAN(ctx, last, s);
+    for (int32_t i = npieces - 1; i >= 0; --i) {
+        BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0s[i], lengths[i],
+                                         states, seg0s[i], nseg_total, slot_ptr(i));
+        if (i > 0) {
+            const ScanLaunch prev = scan_of(i - 1, dS_in);
+            LAUNCH(timed_launch(ctx, LINREC_KERNEL_BWD_SUM, s,
+                                [&] { return linrec::launch_seg_sum(prev, s); }));
+            in.fold = linrec::FoldArg{dS_in, dS_in, (float*)prev.store, prev.store_nseg,
+                                      (int32_t)nseg_of(lengths[i - 1])};
+        }
+        LAUNCH_BWD_INTRA(ctx, in, s);
+    }
+    return LINREC_OK;
+}
+
+size_t linrec_delta_workspace_bytes(const linrec_desc* d)
+{
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+        return 0;
+    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv) * sizeof(float);
+}
+
+linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                               linrec_tensor k, linrec_tensor v, linrec_tensor beta,
+                               linrec_tensor decay, const float* S_in, linrec_tensor o,
+                               float* S_out, void* workspace, void* stream)
+{
+    linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
+    if (st != LINREC_OK)
+        return st;
+    if (d->dk != d->dv)
+        return LINREC_E_SHAPE;
+    if (!beta.ptr)
+        return LINREC_E_NULL;
+    if (!aligned(beta.ptr, 4))
+        return LINREC_E_ALIGN;
+    if (beta.sb < 0 || beta.sh < 0 || beta.st < 0)
+        return LINREC_E_LAYOUT;
+    if ((st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    linrec::DeltaFwdLaunch s{};
+    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
+    s.B = d->B; s.H = d->H; s.T = d->T;
+    s.q = targ(q); s.k = targ(k); s.v = targ(v); s.beta = targ(beta); s.o = targ(o);
+    s.decay = targ(decay);
+    s.decay_kind = d->decay;
+    s.S_in = S_in;
+    s.S_out = S_out;
+    s.wk = (float*)workspace;
+    s.wv = (float*)workspace + (size_t)d->B * d->H * (size_t)d->T * d->dk;
+    LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_FWD, (hipStream_t)stream,
+                        [&] { return linrec::launch_delta_fwd(s, (hipStream_t)stream); }));
     return LINREC_OK;
 }
 

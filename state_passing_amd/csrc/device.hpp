@@ -471,6 +471,41 @@ __device__ __forceinline__ Split<T> split_scaled(const Frag<T>& f, const float (
 }
 
 
+// Product of two computed operands, each a hi + lo pair: hi.hi + hi.lo +
+// lo.hi (the lo.lo term lies below fp32 rounding).
+__device__ __forceinline__ floatx4 mma(const Split<bf16>& a, const Split<bf16>& b, floatx4 c)
+{
+    return mma(a.lo, b.hi, mma(a.hi, b.lo, mma(a.hi, b.hi, c)));
+}
+__device__ __forceinline__ floatx4 mma(const Split<float>& a, const Split<float>& b, floatx4 c)
+{
+    return mma(a.hi, b.hi, c);
+}
+
+// Split operands read from an fp32 LDS tile: frag_rows() / frag_cols()
+// patterns (k contiguous in a row, or k running down the rows).
+template <typename T>
+__device__ __forceinline__ Split<T> split_rows_f32(const float* tile, int pitch, int rbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const float* p = tile + (rbase + t) * pitch + kbase + 8 * g;
+    const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return split8<T>(x);
+}
+
+template <typename T>
+__device__ __forceinline__ Split<T> split_cols_f32(const float* tile, int pitch, int cbase, int kbase)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        x[r] = tile[(kbase + 8 * g + r) * pitch + cbase + t];
+    return split8<T>(x);
+}
+
 // Split fragments read from LDS plane pairs.
 template <typename T>
 __device__ __forceinline__ Split<T> frag_rows_split(const T* hi, const T* lo, int pitch, int rbase, int kbase)

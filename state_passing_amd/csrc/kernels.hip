@@ -199,22 +199,18 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
         rec[DK * DV] = seg_log;
 }
 
-template <int DK, int DV, bool REVERSE>
-__global__ __launch_bounds__(256) void seg_fold_kernel(
-    const float* __restrict__ carry_in, float* __restrict__ carry_out, float* __restrict__ store,
-    int64_t store_nseg, int H, int nseg)
+// Fold of four consecutive state elements [e, e + 4) of head bh across the
+// nseg records at base (in order, or from the last record back when
+// REVERSE): each record's state is replaced by the carried value, then
+// c <- exp(log Gamma_s) c + U_s.  Loads of a batch of records are issued
+// before any of the batch's stores (each store goes to a slot just read).
+template <int DK, int DV, bool REVERSE, int BATCH>
+__device__ __forceinline__ void fold_elems(const float* carry_in, float* carry_out, float* base,
+                                           int nseg, int64_t bh, int e)
 {
     constexpr int64_t REC = seg_record_floats(DK, DV);
-    // four consecutive elements [f][c] of a record per thread
-    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int64_t bh = (int64_t)b * H + h;
     const int64_t io = bh * (DK * DV) + e;                   // S_in / S_out: same layout
     floatx4 carry = carry_in ? *reinterpret_cast<const floatx4*>(carry_in + io) : floatx4{0.f, 0.f, 0.f, 0.f};
-    float* base = store + bh * store_nseg * REC;
-    // loads of a batch of records are issued before any of the batch's
-    // stores (each store goes to a slot that was just read)
-    constexpr int BATCH = 16;
     for (int k0 = 0; k0 < nseg; k0 += BATCH) {
         floatx4 u[BATCH];
         float lg[BATCH];
@@ -241,6 +237,35 @@ __global__ __launch_bounds__(256) void seg_fold_kernel(
         }
     }
     *reinterpret_cast<floatx4*>(carry_out + io) = carry;
+}
+
+template <int DK, int DV, bool REVERSE>
+__global__ __launch_bounds__(256) void seg_fold_kernel(
+    const float* __restrict__ carry_in, float* __restrict__ carry_out, float* __restrict__ store,
+    int64_t store_nseg, int H, int nseg)
+{
+    // four consecutive elements [f][c] of a record per thread
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * H + h;
+    fold_elems<DK, DV, REVERSE, 16>(carry_in, carry_out, store + bh * store_nseg * seg_record_floats(DK, DV),
+                                    nseg, bh, e);
+}
+
+// A fold carried by a segment-kernel launch (see FoldArg): workgroup
+// (s, h, b) of the launch's nsegs_here takes a contiguous share of head
+// (b, h)'s state elements, four per thread at a time.  Nothing in the launch
+// reads or writes what the fold touches, so no workgroup waits on another.
+template <int DK, int DV, bool REVERSE, int NT>
+__device__ __forceinline__ void fold_share(const FoldArg& f, int b, int h, int H, int s, int nsegs_here)
+{
+    constexpr int UNITS = DK * DV / 4;
+    const int per = (UNITS + nsegs_here - 1) / nsegs_here;
+    const int u1 = min((s + 1) * per, UNITS);
+    const int64_t bh = (int64_t)b * H + h;
+    float* base = f.store + bh * f.store_nseg * seg_record_floats(DK, DV);
+    for (int u = s * per + (int)threadIdx.x; u < u1; u += NT)
+        fold_elems<DK, DV, REVERSE, 8>(f.carry_in, f.carry_out, base, f.nseg, bh, 4 * u);
 }
 
 // ---------------------------------------------------------------------------
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, Act<const T> dO, DecayArg dec,
     const float* __restrict__ bstates, int64_t bs_nseg, const float* __restrict__ gstates,
     int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, Act<float> da, float* __restrict__ da_tot,
-    int H, int N, int m)
+    int H, int N, int m, FoldArg fold)
 {
     constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
@@ -434,6 +459,9 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st);
     load_state<DK, DV, 1>(C, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
     float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
+    // the previous piece's fold, while the first chunk's loads are in flight
+    if (fold.store)
+        fold_share<DK, DV, true, NT>(fold, b, h, H, s, gridDim.x);
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         chunk_store(rk, Ks, QP);
@@ -781,14 +809,14 @@ hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
                            cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
                            decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
                            (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                           mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m);
+                           mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold);
     else
         hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, 0, stream,
                            cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
                            decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
                            (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
                            mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
-                           s.m);
+                           s.m, s.fold);
     return hipGetLastError();
 }
 

@@ -36,6 +36,19 @@ struct ScanLaunch {
     int64_t store_nseg;
 };
 
+// The previous piece's reverse fold carried along by a backward
+// segment-kernel launch of the sequence driver (store == NULL: none).  Same meaning as the fold of a
+// ScanLaunch: that piece's records (store, store_nseg per (b, h), nseg of
+// them) and its carry.  Each workgroup of the launch folds an equal share of
+// every head's state elements.
+struct FoldArg {
+    const float* carry_in;   // may be NULL (zeros); may alias carry_out
+    float* carry_out;
+    float* store;
+    int64_t store_nseg;
+    int nseg;
+};
+
 struct FwdIntraLaunch {
     int dtype, out_dtype, dk, dv, B, H, N, m;
     TensorArg q, k, v, decay, o;
@@ -57,6 +70,7 @@ struct BwdIntraLaunch {
     int64_t g_nseg;
     TensorArg da;
     float* da_tot;
+    FoldArg fold;            // the previous piece's reverse fold, or none
 };
 
 // Finishes the decay gradient of one piece: adds the totals of later
@@ -71,6 +85,18 @@ struct DaFinishLaunch {
     float* carry_out;
 };
 
+// Gated delta rule, forward over one piece: per-chunk W_k, W_v into the
+// workspace (fp32 [B][H][T][d_k], then [B][H][T][d_v]), then the serial walk.
+struct DeltaFwdLaunch {
+    int dtype, out_dtype, dk, dv, B, H, T;
+    TensorArg q, k, v, beta, decay, o;
+    int decay_kind;
+    const float* S_in;       // may be NULL (zeros)
+    float* S_out;
+    float* wk;
+    float* wv;
+};
+
 // The state transition is two launches: the parallel segment sum, then the
 // serial fold (both from the same description).
 hipError_t launch_seg_sum(const ScanLaunch& s, hipStream_t stream);
@@ -78,5 +104,6 @@ hipError_t launch_seg_fold(const ScanLaunch& s, hipStream_t stream);
 hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream);
+hipError_t launch_delta_fwd(const DeltaFwdLaunch& s, hipStream_t stream);
 
 }  // namespace linrec

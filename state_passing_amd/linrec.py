@@ -43,10 +43,11 @@ EXPORTS = (
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
     "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
     "linrec_bwd_da_workspace_bytes", "linrec_bwd_da", "linrec_bwd_noalloc",
+    "linrec_delta_workspace_bytes", "linrec_delta_fwd",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
-                5: "bwd_seg", 6: "da_finish"}
+                5: "bwd_seg", 6: "da_finish", 7: "delta_fwd"}
 
 
 class LinrecError(RuntimeError):
@@ -95,6 +96,8 @@ def _lib():
         "linrec_bwd_recompute": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
         "linrec_bwd_da_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_noalloc": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P], ctypes.c_int),
+        "linrec_delta_workspace_bytes": ([D], ctypes.c_size_t),
+        "linrec_delta_fwd": ([P, D, T, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_da": ([P, D, T, T, T, T, P, T, P, T, T, T, P, T, P, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
@@ -590,6 +593,41 @@ def bwd_seq(q, k, v, decay, lengths: Sequence[int], states, dO, dS_out=None, *, 
                                _ptr(workspace), _stream(q.device))
     _check(rc, "linrec_bwd_seq")
     return dq, dk, dv, dS_in
+
+
+# ----------------------------------------------------------------- delta rule
+
+def delta_workspace_bytes(d: Desc) -> int:
+    return int(_lib().linrec_delta_workspace_bytes(ctypes.byref(d)))
+
+
+def delta_fwd(q, k, v, beta, decay=None, S_in=None, *, o=None, S_out=None, workspace=None,
+              out_dtype=None):
+    """Gated delta rule, forward over one piece (linrec_delta_fwd):
+    S_t = a_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t, o_t = q_t S_t.
+    beta: fp32 [B,H,T].  Returns (o, S_out)."""
+    odt = _out_dtype(q, out_dtype, o)
+    devs = _validate(q, k, v, decay, outs=_outs(q, v, odt, o=o), states_in=(("S_in", S_in),),
+                     states_out=(("S_out", S_out),), extra=(("beta", beta), ("workspace", workspace)))
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    if not isinstance(beta, torch.Tensor) or beta.dtype != torch.float32 or beta.shape != (B, H, T):
+        _fail(f"beta: must be float32 [B,H,T] = {(B, H, T)}")
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, delta_workspace_bytes(d))
+    _check_device(q, *devs)
+    o = _new_act(q, DV, odt, o)
+    S_out = _state_out(q, B, H, DK, DV, S_out)
+    if workspace is None:
+        workspace = torch.empty(max(delta_workspace_bytes(d), 16), dtype=torch.uint8, device=q.device)
+    bs = beta.stride()
+    rc = _lib().linrec_delta_fwd(context(q.device.index), ctypes.byref(d), _act(q), _act(k), _act(v),
+                                 Tensor(beta.data_ptr(), bs[0], bs[1], bs[2]), dec, _ptr(S_in),
+                                 _act(o), _ptr(S_out), _ptr(workspace), _stream(q.device))
+    _check(rc, "linrec_delta_fwd")
+    return o, S_out
 
 
 def piece_loop(q, k, v, decay, lengths: Sequence[int], S_in=None, dO=None, dS_out=None,

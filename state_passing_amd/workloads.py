@@ -15,13 +15,15 @@ Workloads (sizes from the five configurations this layer is measured on):
                    seeded random piece lengths (multiples of 64 in [2048, 32768])
   5 gated-batch    B=8 H=32 T=32768  d=128 bf16, per-token gate, 8 x 4096
 
-Recipe (all draws seeded, in this order: q, k, v, dO, S_in, gate logits):
+Recipe (all draws seeded, in this order: q, k, v, dO, S_in, gate logits,
+dS_out when asked for, beta logits for the delta rule):
   q, k  ~ N(0, I) per token in fp32, divided by their L2 norm, then cast to
         the workload dtype (round to nearest even);
   v, dO ~ N(0, 1), cast the same way;
   S_in  ~ N(0, s^2) fp32 with s = 0.1 for workload 4, else zeros;
   per-head decay a_h = 1 - 2^-(5 + 8h/H), h = 0..H-1, stored as fp32;
-  per-token gate a = 0.9 + 0.1 * sigmoid(x), x ~ N(2, 1), fp32.
+  per-token gate a = 0.9 + 0.1 * sigmoid(x), x ~ N(2, 1), fp32;
+  delta rule: beta = sigmoid(y), y ~ N(0, 1), fp32 [B,H,T].
 """
 from __future__ import annotations
 
@@ -48,6 +50,7 @@ class Workload:
     s_in_std: float = 0.0
     piece: int = 4096     # uniform piece length (ignored when random_split)
     random_split: bool = False
+    delta: bool = False   # gated delta rule: also draw the write strengths beta
 
     @property
     def seed(self) -> int:
@@ -77,6 +80,14 @@ WORKLOADS = {
     4: Workload(4, "nonuniform-256k", 1, 32, 262144, 128, 128, "bf16", "head",
                 s_in_std=0.1, random_split=True),
     5: Workload(5, "gated-batch", 8, 32, 32768, 128, 128, "bf16", "token", piece=4096),
+}
+
+# Gated delta rule (the Gated DeltaNet recurrence StateFlow trains): the
+# gated-batch recipe per head at the 16-head, 16K-token shape, plus write
+# strengths beta = sigmoid(y), y ~ N(0, 1), drawn last.
+DELTA_WORKLOADS = {
+    6: Workload(6, "delta-gated-16k", 1, 16, 16384, 128, 128, "bf16", "token", piece=4096,
+                delta=True),
 }
 
 
@@ -119,6 +130,7 @@ class Inputs:
     S_in: Optional[torch.Tensor]          # fp32 [B,H,dk,dv] or None (zeros)
     decay: Optional[torch.Tensor]         # fp32 [H] or [B,H,T], None for a_t = 1
     dS_out: Optional[torch.Tensor] = None  # fp32 [B,H,dk,dv] or None (zeros)
+    beta: Optional[torch.Tensor] = None    # fp32 [B,H,T] (delta rule) or None
     extra: dict = field(default_factory=dict)
 
 
@@ -152,4 +164,5 @@ def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None,
         x = randn(B, H, T) + 2.0
         decay = 0.9 + 0.1 * torch.sigmoid(x)
     dS_out = randn(B, H, dk, dv) if with_dS_out else None
-    return Inputs(wl, q, k, v, dO, S_in, decay, dS_out)
+    beta = torch.sigmoid(randn(B, H, T)) if wl.delta else None
+    return Inputs(wl, q, k, v, dO, S_in, decay, dS_out, beta)

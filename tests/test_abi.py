@@ -63,10 +63,10 @@ def test_sizes():
     assert linrec.seq_states_bytes(d(T=8192), [2048, 4096, 2048]) == linrec.states_bytes(d(T=8192))
     assert linrec.seq_states_bytes(d(T=384), [64, 320]) == 16 * 3 * rec
     assert linrec.seq_states_bytes(d(T=384), [64, 300]) == 0
-    # one piece's records, sized for the longest piece
+    # two slots of one piece's records, sized for the longest piece
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \
-        linrec.states_bytes(d(T=4096))
-    assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == linrec.states_bytes(d())
+        2 * linrec.states_bytes(d(T=4096))
+    assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == 2 * linrec.states_bytes(d())
     for bad in (d(T=100), d(T=0), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
         assert linrec.states_bytes(bad) == 0
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [4096, 4000]) == 0
@@ -231,3 +231,20 @@ def test_noalloc_arguments():
     assert call(d(T=100)) == E["LINREC_E_SHAPE"]
     assert call(d(), states=None) == E["LINREC_E_WORKSPACE"]
     assert call(d(), dS_in=None) == E["LINREC_E_NULL"]
+
+
+def test_delta_arguments():
+    lib = linrec._lib()
+    assert linrec.delta_workspace_bytes(d()) == 16 * 4096 * 256 * 4
+    assert linrec.delta_workspace_bytes(d(dk=64)) == 0        # d_k != d_v
+    assert linrec.delta_workspace_bytes(d(T=100)) == 0
+
+    def call(desc, beta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), ws=FAKE):
+        return lib.linrec_delta_fwd(None, ctypes.byref(desc), act(), act(), act(), beta,
+                                    linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, ws, None)
+    assert call(d()) == E["LINREC_E_NULL"]                   # checks pass, no context
+    assert call(d(dk=64)) == E["LINREC_E_SHAPE"]
+    assert call(d(), beta=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
+    assert call(d(), beta=linrec.Tensor(FAKE + 2, 0, 0, 1)) == E["LINREC_E_ALIGN"]
+    assert call(d(), beta=linrec.Tensor(FAKE, -1, 0, 1)) == E["LINREC_E_LAYOUT"]
+    assert call(d(), ws=None) == E["LINREC_E_WORKSPACE"]

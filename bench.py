@@ -68,8 +68,9 @@ KERNEL_DESIGN_BYTES = {
     "bwd_sum": 512 + 256,          # q, dO; writes the gradient records
     "bwd_fold": 256 + 256,
     # k, v, dO for dQ; q, and k, v, dO again except on the chunk both walks
-    # share (one of four); dq, dk, dv; the S and G segment states
-    "bwd_seg": 768 + 256 + 576 + 768 + 512,
+    # share (one of four); dq, dk, dv; the S and G segment states; and the
+    # previous piece's fold it carries (63 launches of 64 in a step)
+    "bwd_seg": 768 + 256 + 576 + 768 + 512 + 512 * 63 / 64,
 }
 KERNEL_SYMBOL = {
     "fwd_sum": "seg_sum_kernel<bf16,128,128,false>",
@@ -77,7 +78,7 @@ KERNEL_SYMBOL = {
     "fwd_seg": "fwd_seg_kernel<bf16,bf16,128,128>",
     "bwd_sum": "seg_sum_kernel<bf16,128,128,true>",
     "bwd_fold": "seg_fold_kernel<128,128,true>",
-    "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128>",
+    "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128,false>",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_seg_sa256k_traffic.txt")
 SQ_FILE = os.path.join(ROOT, "profiles", "linrec_kernels_sa256k_sq_counters.txt")
@@ -178,6 +179,68 @@ def cpu_baseline(inp, wl, sample_tokens: int):
             "fwd_tokens_per_s": wl.B * sample_tokens / (t1 - t0)}
 
 
+def delta_bench(linrec, dev, args):
+    """Gated delta rule on its 16-head, 16K-token workload (4 pieces of 4096,
+    per-token gate, d = 128, bf16): forward over the pieces (keeping what the
+    backward needs), then the backward in reverse, carrying dS."""
+    import torch
+    from state_passing_amd.workloads import DELTA_WORKLOADS, make_inputs
+    wl = DELTA_WORKLOADS[6]
+    inp = make_inputs(wl, device=dev)
+    lengths = wl.pieces()
+    B, H, T, D = wl.B, wl.H, wl.T, wl.dk
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    dq, dk, dv = (torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    db = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    pd = linrec.desc(B, H, lengths[0], D, D, linrec.BF16, linrec.DECAY_TOKEN)
+    saved = [torch.empty(linrec.delta_saved_bytes(pd), dtype=torch.uint8, device=dev) for _ in lengths]
+    wsf = torch.empty(linrec.delta_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(linrec.delta_bwd_workspace_bytes(pd), dtype=torch.uint8, device=dev)
+    S = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    dS = torch.empty_like(S)
+    bounds = [0]
+    for L in lengths:
+        bounds.append(bounds[-1] + L)
+
+    def fwd():
+        for i in range(len(lengths)):
+            sl = slice(bounds[i], bounds[i + 1])
+            linrec.delta_fwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.beta[:, :, sl],
+                             inp.decay[:, :, sl], None if i == 0 else S, o=o[:, :, sl], S_out=S,
+                             saved=saved[i], workspace=wsf)
+
+    def bwd():
+        for i in reversed(range(len(lengths))):
+            sl = slice(bounds[i], bounds[i + 1])
+            linrec.delta_bwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.beta[:, :, sl],
+                             inp.decay[:, :, sl], saved[i], inp.dO[:, :, sl],
+                             None if i == len(lengths) - 1 else dS, dq=dq[:, :, sl],
+                             dk=dk[:, :, sl], dv=dv[:, :, sl], dbeta=db[:, :, sl], dS_in=dS,
+                             workspace=wsb)
+
+    def timed(fn, steps):
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b_.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b_) / steps
+
+    for _ in range(max(args.warmup, 1)):
+        fwd()
+        bwd()
+    steps = max(1, min(args.steps, 5))
+    ms_fwd = timed(fwd, steps)
+    ms_bwd = timed(bwd, steps)
+    tokens = B * T
+    return {"workload": wl.name, "B": B, "H": H, "T": T, "d": D,
+            "pieces": f"{len(lengths)} x {lengths[0]}", "decay": "per-token gate",
+            "fwd_ms": ms_fwd, "bwd_ms": ms_bwd, "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
+            "fwd_plus_bwd_tokens_per_s": tokens / ((ms_fwd + ms_bwd) * 1e-3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -226,26 +289,6 @@ def main():
             ev[2].record()
             record.append(ev)
 
-    # serialized pass: the same pieces through the per-piece calls on one stream
-    pd = linrec.desc(B, H, lengths[0], DK, DV, linrec.BF16, linrec.DECAY_HEAD)
-    piece_states = [torch.empty(linrec.states_bytes(pd), dtype=torch.uint8, device=dev)
-                    for _ in lengths]
-    piece_ws = torch.empty(linrec.bwd_workspace_bytes(pd), dtype=torch.uint8, device=dev)
-
-    def step_serial():
-        S = inp.S_in
-        for i in range(len(lengths)):
-            sl = slice(bounds[i], bounds[i + 1])
-            _, S, _ = linrec.fwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.decay, S,
-                                 o=o[:, :, sl], S_out=S_out, states=piece_states[i])
-        dS = None
-        for i in reversed(range(len(lengths))):
-            sl = slice(bounds[i], bounds[i + 1])
-            _, _, _, dS = linrec.bwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl], inp.decay,
-                                     piece_states[i], inp.dO[:, :, sl], dS, dq=dq[:, :, sl],
-                                     dk=dk[:, :, sl], dv=dv[:, :, sl], dS_in=dS_in,
-                                     workspace=piece_ws)
-
     def timed(fn, steps):
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -256,32 +299,36 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b_) / steps
 
-    result = {}
-    tokens = B * T
-    if not args.profile:
-        for _ in range(args.warmup):
+    for _ in range(args.warmup):
+        step_seq()
+    torch.cuda.synchronize()
+    if args.profile:
+        # only the timed region's dispatches, for a profiler
+        for _ in range(args.steps):
             step_seq()
         torch.cuda.synchronize()
-        # timed region: K whole steps, bracketed by synchronisation
-        fwd_ev = []
-        t0 = time.perf_counter()
-        ms_step = timed(lambda: step_seq(fwd_ev), args.steps)
-        wall = time.perf_counter() - t0
-        fwd_only_ms = sum(e[0].elapsed_time(e[1]) for e in fwd_ev) / len(fwd_ev)
-        per_step = sorted(e[0].elapsed_time(e[2]) for e in fwd_ev)
+        print(json.dumps({"profile": "sequence drivers", "steps": args.steps}))
+        return
 
-    # serialized pass with per-kernel events on each kernel's own stream
-    for _ in range(args.warmup):
-        step_serial()
+    # timed region: K whole steps, bracketed by synchronisation
+    fwd_ev = []
+    t0 = time.perf_counter()
+    ms_step = timed(lambda: step_seq(fwd_ev), args.steps)
+    wall = time.perf_counter() - t0
+    fwd_only_ms = sum(e[0].elapsed_time(e[1]) for e in fwd_ev) / len(fwd_ev)
+    per_step = sorted(e[0].elapsed_time(e[2]) for e in fwd_ev)
+
+    # the same steps again with per-kernel events on each kernel's own stream
     linrec.set_kernel_timing(True)
-    ms_serial = timed(step_serial, args.steps)
+    ms_events = timed(step_seq, args.steps)
     ktimes = linrec.kernel_times()
     linrec.set_kernel_timing(False)
 
+    tokens = B * T
     token_heads_piece = B * H * lengths[0]
     kernels = {}
     for name, (n, ms) in ktimes.items():
-        if n == 0:
+        if n == 0 or name not in KERNEL_BYTES:
             continue
         avg_ms = ms / n
         kernels[name] = {
@@ -299,18 +346,18 @@ def main():
                 "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": KERNEL_BYTES[dominant] * token_heads_piece,
                 "design_bytes_per_launch": KERNEL_DESIGN_BYTES[dominant] * token_heads_piece,
-                "avg_launch_us": dom["avg_us"]}
-    if not args.profile:
-        # what a plain streaming copy reaches on this GPU, beside the spec peak
-        roofline["copy_probe_GBs"] = copy_probe(1 << 30)
-    if args.profile:
-        print(json.dumps({"ms_per_step_serialized": ms_serial, "kernels": kernels,
-                          "roofline": roofline}))
-        return
+                "avg_launch_us": dom["avg_us"],
+                # what a plain streaming copy reaches on this GPU, beside the spec peak
+                "copy_probe_GBs": copy_probe(1 << 30)}
 
     # The backward variants, each over the 64 pieces in reverse with dS
-    # carried, against the plain per-piece backward of the serialized pass
-    # (whose forward left piece_states and o in place).
+    # carried through the per-piece calls, against the plain per-piece
+    # backward; the per-piece forward below leaves the piece states, the
+    # boundary states and o in place.
+    pd = linrec.desc(B, H, lengths[0], DK, DV, linrec.BF16, linrec.DECAY_HEAD)
+    piece_states = [torch.empty(linrec.states_bytes(pd), dtype=torch.uint8, device=dev)
+                    for _ in lengths]
+    piece_ws = torch.empty(linrec.bwd_workspace_bytes(pd), dtype=torch.uint8, device=dev)
     bnd = torch.zeros(len(lengths) + 1, B, H, DK, DV, dtype=torch.float32, device=dev)
     if inp.S_in is not None:
         bnd[0].copy_(inp.S_in)
@@ -384,9 +431,10 @@ def main():
         "fwd_hbm_roof_pct_minimal_bytes": 100.0 * FWD_BYTES * B * H * T / (fwd_only_ms * 1e-3)
                                           / (PEAK_HBM_GBS * 1e9),
         "roofline": roofline,
-        "ms_per_step_serialized": ms_serial,
+        "ms_per_step_with_kernel_events": ms_events,
         "kernels": kernels,
         "backward_variants": next_rows,
+        "delta_rule": delta_bench(linrec, dev, args),
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

@@ -331,17 +331,48 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
  * d_k != d_v): W_k and W_v of every token, fp32, B*H*T*(d_k + d_v)*4. */
 size_t linrec_delta_workspace_bytes(const linrec_desc* d);
 
+/* Bytes linrec_delta_fwd writes to `saved` for the backward (0 if `d` is
+ * invalid or d_k != d_v): the state entering every chunk, fp32
+ * [B,H,T/64,d_k,d_v], then U of every token, fp32 [B,H,T,d_v]. */
+size_t linrec_delta_saved_bytes(const linrec_desc* d);
+
 /* Delta-rule forward over one piece.
  *   q, k: [B,H,T,d_k]; v, o: [B,H,T,d_v]; d_k == d_v (64 or 128; fp32 inputs
  *   only at 64).  beta: fp32 [B,H,T] with strides (sb, sh, st), values in
  *   [0, 1].  decay per d->decay (as linrec_fwd; the gate a_t).  S_in: fp32
  *   [B,H,d_k,d_v] or NULL (zeros).  S_out: fp32, required, may alias S_in.
+ *   saved: NULL, or linrec_delta_saved_bytes(d) bytes (16-byte aligned) that
+ *   the backward of this piece reads.
  *   workspace: linrec_delta_workspace_bytes(d) bytes, 16-byte aligned.
  * Errors and ownership as linrec_fwd. */
 linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d,
                                linrec_tensor q, linrec_tensor k, linrec_tensor v,
                                linrec_tensor beta, linrec_tensor decay, const float* S_in,
-                               linrec_tensor o, float* S_out, void* workspace, void* stream);
+                               linrec_tensor o, float* S_out, void* saved, void* workspace,
+                               void* stream);
+
+/* Bytes of workspace linrec_delta_bwd needs (0 if `d` is invalid or
+ * d_k != d_v): W_k, W_v, per-chunk T (then the masked gradient of A),
+ * dU (then T^T dU) and the gradient leaving every chunk, all fp32. */
+size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d);
+
+/* Delta-rule backward over one piece, for L = <dO, o> + <dS_out, S_out>:
+ *   dU   = P^T dO + (K .* gamma_C/gamma) dS_C  and
+ *   dS_0 = (Q .* gamma)^T dO + gamma_C dS_C - W_k^T dU  (carried across chunks,
+ *   serially, 16 gradient columns per workgroup), then per chunk in parallel
+ *   dV = beta .* (T^T dU), dbeta, dQ and dK through W = T R, T = (I + A)^-1,
+ *   P = (Q K^T) .* D and the state update.  The gate is not differentiated.
+ *   saved: as written by linrec_delta_fwd for this piece.  dO: [B,H,T,d_v];
+ *   dS_out: fp32 [B,H,d_k,d_v] or NULL (zeros).  dq, dk, dv as linrec_bwd;
+ *   dbeta: fp32 [B,H,T] (strides like beta); dS_in: fp32, required, may
+ *   alias dS_out.  workspace: linrec_delta_bwd_workspace_bytes(d) bytes.
+ * Errors and ownership as linrec_bwd. */
+linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d,
+                               linrec_tensor q, linrec_tensor k, linrec_tensor v,
+                               linrec_tensor beta, linrec_tensor decay, const void* saved,
+                               linrec_tensor dO, const float* dS_out, linrec_tensor dq,
+                               linrec_tensor dk, linrec_tensor dv, linrec_tensor dbeta,
+                               float* dS_in, void* workspace, void* stream);
 
 /* Kernel kinds for linrec_ctx_kernel_times(). */
 enum {
@@ -353,7 +384,8 @@ enum {
     LINREC_KERNEL_BWD_SEG = 5,    /* backward segment kernel: dQ, dK, dV       */
     LINREC_KERNEL_DA_FINISH = 6,  /* decay gradient, last step                 */
     LINREC_KERNEL_DELTA_FWD = 7,  /* delta rule forward (both of its kernels)  */
-    LINREC_KERNEL_KINDS = 8
+    LINREC_KERNEL_DELTA_BWD = 8,  /* delta rule backward (its four kernels)    */
+    LINREC_KERNEL_KINDS = 9
 };
 
 /* Per-kernel timing (instrumentation, off by default).  While enabled, every

@@ -339,10 +339,13 @@ hipError_t pool_event(linrec_ctx* ctx, hipEvent_t* ev)
         ctx->pool.pop_back();
         return hipSuccess;
     }
-    return hipEventCreate(ev);
+    // no system-scope release at the event: it would write back L2 after
+    // the bracketed kernel and bill that to the kernel's duration
+    return hipEventCreateWithFlags(ev, hipEventDisableSystemFence);
 }
 
-// Launch `fn` on `stream`; with timing on, bracket it by events on that stream.
+// Launch `fn` on `stream`; with timing on, the kernels it launches carry a pair
+// of events as their own start and end stamps (launch_kernel).
 template <typename F>
 hipError_t timed_launch(linrec_ctx* ctx, int kind, hipStream_t stream, F fn)
 {
@@ -352,12 +355,12 @@ hipError_t timed_launch(linrec_ctx* ctx, int kind, hipStream_t stream, F fn)
     hipError_t e = pool_event(ctx, &t.begin);
     if (e == hipSuccess)
         e = pool_event(ctx, &t.end);
-    if (e == hipSuccess)
-        e = hipEventRecord(t.begin, stream);
-    if (e == hipSuccess)
+    if (e == hipSuccess) {
+        // the events become the launched kernels' own start and end stamps
+        linrec::launch_stamps() = linrec::LaunchStamps{t.begin, t.end};
         e = fn();
-    if (e == hipSuccess)
-        e = hipEventRecord(t.end, stream);
+        linrec::launch_stamps() = linrec::LaunchStamps{};
+    }
     if (e != hipSuccess) {
         if (t.begin)
             ctx->pool.push_back(t.begin);
@@ -777,22 +780,52 @@ size_t linrec_delta_workspace_bytes(const linrec_desc* d)
     return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv) * sizeof(float);
 }
 
-linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
-                               linrec_tensor k, linrec_tensor v, linrec_tensor beta,
-                               linrec_tensor decay, const float* S_in, linrec_tensor o,
-                               float* S_out, void* workspace, void* stream)
+size_t linrec_delta_saved_bytes(const linrec_desc* d)
 {
-    linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
-    if (st != LINREC_OK)
-        return st;
-    if (d->dk != d->dv)
-        return LINREC_E_SHAPE;
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+        return 0;
+    const size_t bh = (size_t)d->B * d->H;
+    return bh * ((size_t)(d->T / kChunk) * d->dk * d->dv + (size_t)d->T * d->dv) * sizeof(float);
+}
+
+size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
+{
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+        return 0;
+    const size_t bh = (size_t)d->B * d->H, N = (size_t)(d->T / kChunk);
+    return bh * ((size_t)d->T * (d->dk + 2 * d->dv) + N * kChunk * kChunk + N * d->dk * d->dv) *
+           sizeof(float);
+}
+
+namespace {
+
+linrec_status check_beta(const linrec_tensor& beta)
+{
     if (!beta.ptr)
         return LINREC_E_NULL;
     if (!aligned(beta.ptr, 4))
         return LINREC_E_ALIGN;
     if (beta.sb < 0 || beta.sh < 0 || beta.st < 0)
         return LINREC_E_LAYOUT;
+    return LINREC_OK;
+}
+
+}  // namespace
+
+linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                               linrec_tensor k, linrec_tensor v, linrec_tensor beta,
+                               linrec_tensor decay, const float* S_in, linrec_tensor o,
+                               float* S_out, void* saved, void* workspace, void* stream)
+{
+    linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
+    if (st != LINREC_OK)
+        return st;
+    if (d->dk != d->dv)
+        return LINREC_E_SHAPE;
+    if ((st = check_beta(beta)) != LINREC_OK)
+        return st;
+    if (saved && !aligned(saved, 16))
+        return LINREC_E_WORKSPACE;
     if ((st = check_ctx(ctx)) != LINREC_OK)
         return st;
     linrec::DeltaFwdLaunch s{};
@@ -805,8 +838,51 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.S_out = S_out;
     s.wk = (float*)workspace;
     s.wv = (float*)workspace + (size_t)d->B * d->H * (size_t)d->T * d->dk;
+    if (saved) {
+        s.s0 = (float*)saved;
+        s.u = (float*)saved + (size_t)d->B * d->H * (size_t)(d->T / kChunk) * d->dk * d->dv;
+    }
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_FWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_fwd(s, (hipStream_t)stream); }));
+    return LINREC_OK;
+}
+
+linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
+                               linrec_tensor k, linrec_tensor v, linrec_tensor beta,
+                               linrec_tensor decay, const void* saved, linrec_tensor dO,
+                               const float* dS_out, linrec_tensor dq, linrec_tensor dk,
+                               linrec_tensor dv, linrec_tensor dbeta, float* dS_in,
+                               void* workspace, void* stream)
+{
+    linrec_status st = check_bwd_args(d, q, k, v, decay, saved, dO, dS_out, dq, dk, dv, dS_in,
+                                      workspace);
+    if (st != LINREC_OK)
+        return st;
+    if (d->dk != d->dv)
+        return LINREC_E_SHAPE;
+    if ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK)
+        return st;
+    if ((st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    const size_t bh = (size_t)d->B * d->H, T = (size_t)d->T, N = T / kChunk;
+    linrec::DeltaBwdLaunch s{};
+    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
+    s.B = d->B; s.H = d->H; s.T = d->T;
+    s.q = targ(q); s.k = targ(k); s.v = targ(v); s.beta = targ(beta); s.decay = targ(decay);
+    s.dO = targ(dO); s.dq = targ(dq); s.dk_ = targ(dk); s.dv_ = targ(dv); s.dbeta = targ(dbeta);
+    s.decay_kind = d->decay;
+    s.s0 = (const float*)saved;
+    s.u = (const float*)saved + bh * N * d->dk * d->dv;
+    s.dS_out = dS_out;
+    s.dS_in = dS_in;
+    float* ws = (float*)workspace;
+    s.wk = ws;
+    s.wv = s.wk + bh * T * d->dk;
+    s.tm = s.wv + bh * T * d->dv;
+    s.duy = s.tm + bh * N * kChunk * kChunk;
+    s.dsc = s.duy + bh * T * d->dv;
+    LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, (hipStream_t)stream,
+                        [&] { return linrec::launch_delta_bwd(s, (hipStream_t)stream); }));
     return LINREC_OK;
 }
 

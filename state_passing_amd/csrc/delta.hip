@@ -43,7 +43,8 @@ namespace linrec {
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<const T> V,
                                                          Act<const float> beta, DecayArg dec,
-                                                         Act<float> Wk, Act<float> Wv, int H)
+                                                         Act<float> Wk, Act<float> Wv,
+                                                         float* __restrict__ Tout, int H)
 {
     constexpr int NT = 256, NW = 4;
     constexpr int PAD = Pad<T>::value;
@@ -106,6 +107,12 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<con
 #pragma unroll
         for (int i = 0; i < CHUNK; ++i)
             Ts[i * AP + l] = x[i];
+        if (Tout) {   // the backward's copy: [B][H][N][64][64]
+            float* dst = Tout + (((int64_t)b * H + h) * gridDim.x + n) * CHUNK * CHUNK;
+#pragma unroll
+            for (int i = 0; i < CHUNK; ++i)
+                dst[i * CHUNK + l] = x[i];
+        }
     }
     __syncthreads();
 
@@ -147,8 +154,9 @@ template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
                                                          Act<const float> Wk, Act<const float> Wv,
                                                          DecayArg dec, const float* S_in,
-                                                         float* S_out, Act<OT> O, int H,
-                                                         int N)
+                                                         float* S_out, Act<OT> O,
+                                                         float* __restrict__ s0_out,
+                                                         float* __restrict__ u_out, int H, int N)
 {
     constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
     static_assert(FPW >= 1 && FPW * NW == NFB, "d_k must be 64 or 128");
@@ -205,8 +213,12 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 #pragma unroll
         for (int q = 0; q < FPW; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Ss[(16 * (FPW * w + q) + 4 * g + r) * CP + t] = S[q][r];
+            for (int r = 0; r < 4; ++r) {
+                const int f = 16 * (FPW * w + q) + 4 * g + r;
+                Ss[f * CP + t] = S[q][r];
+                if (s0_out)   // the state entering chunk n, for the backward
+                    s0_out[((bh * N + n) * DK + f) * DV + cbase + t] = S[q][r];
+            }
         __syncthreads();
 
         // P = (Q K^T) .* D, causal, fp32
@@ -234,7 +246,10 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r;
-                Us[i * CP + t] = Wvs[i * CP + t] - acc[r];
+                const float u = Wvs[i * CP + t] - acc[r];
+                Us[i * CP + t] = u;
+                if (u_out)    // U for the backward, [B][H][T][DV]
+                    u_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u;
             }
         }
         __syncthreads();
@@ -276,6 +291,414 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 }
 
 // ---------------------------------------------------------------------------
+// Backward.  With dO the chunk's output gradient and dS_C the gradient of
+// the state leaving it (G, carried from later chunks):
+//
+//   dU   = P^T dO + K~ dS_C                         (K~ = K .* gamma_C/gamma)
+//   dS_0 = (Q .* gamma)^T dO + gamma_C dS_C - W_k^T dU          (serial)
+//   Y    = T^T dU,   dV = beta .* Y
+//   dA   = -Y U^T,   M = dA .* (gamma_i / gamma_j) for j < i, else 0
+//   dbeta_i = < V_i - gamma_i (K S_0)_i, Y_i > + sum_j M_ij k_i . k_j
+//   dQ   = gamma .* (dO S_0^T) + [(dO U^T) .* D] K
+//   dK   = [(dO U^T) .* D]^T Q + gamma_C/gamma .* (U dS_C^T)
+//          - beta gamma .* (Y S_0^T) + beta .* (M K) + M^T (beta .* K)
+//
+// (through W = T R with T = (I + A)^{-1}: dT = dU ((I + A) U)^T, so
+// dA = -T^T dT T^T = -Y U^T.)  The gate is not differentiated.
+// ---------------------------------------------------------------------------
+
+// Serial reverse walk over a piece's chunks for one (b, h) and gradient
+// columns [16 cb, 16 cb + 16), 4 waves as in delta_scan_kernel.  Writes dU
+// ([B][H][T][DV] fp32), the gradient leaving every chunk (dS_C, per chunk
+// [B][H][N][DK][DV]) and dS_in.
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
+                                                          Act<const T> dO, Act<const float> Wk,
+                                                          DecayArg dec, const float* dS_out,
+                                                          float* dS_in, float* __restrict__ dU_out,
+                                                          float* __restrict__ dsc_out, int H, int N)
+{
+    constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
+    constexpr int PAD = Pad<T>::value;
+    constexpr int QP = DK + PAD, OP = 16 + PAD;
+    constexpr int WP = DK + 4, CP = 16 + 4, PP = CHUNK + 4;
+    __shared__ __align__(16) T Qs[CHUNK * QP];
+    __shared__ __align__(16) T Ks[CHUNK * QP];
+    __shared__ __align__(16) T dOs[CHUNK * OP];
+    __shared__ __align__(16) float Wks[CHUNK * WP];
+    __shared__ __align__(16) float Ps[CHUNK * PP];
+    __shared__ __align__(16) float Gs[DK * CP];
+    __shared__ __align__(16) float dUs[CHUNK * CP];
+    __shared__ __align__(16) float tab[TAB_SIZE];
+
+    const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
+    const int64_t bh = (int64_t)b * H + h;
+    const int cbase = 16 * cb;
+
+    floatx4 G[FPW];   // dS[16 fb + 4g + r][cbase + t], fb = FPW w + q
+#pragma unroll
+    for (int q = 0; q < FPW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            G[q][r] = dS_out ? dS_out[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t]
+                             : 0.f;
+
+    const T* qh = Q.head(b, h);
+    const T* kh = K.head(b, h);
+    const T* doh = dO.head(b, h);
+    const float* wkh = Wk.head(b, h);
+    for (int n = N - 1; n >= 0; --n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        {
+            ChunkRegs<T, DK, NT> rq, rk;
+            chunk_load(rq, qh + tok0 * Q.st, Q.st);
+            chunk_load(rk, kh + tok0 * K.st, K.st);
+            chunk_store(rq, Qs, QP);
+            chunk_store(rk, Ks, QP);
+        }
+        constexpr int VEC = 16 / sizeof(T), PER = 16 / VEC;   // 16-byte vectors per slice row
+        if (threadIdx.x < CHUNK * PER) {
+            const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
+            *reinterpret_cast<u32x4*>(dOs + row * OP + col) =
+                *reinterpret_cast<const u32x4*>(doh + (tok0 + row) * dO.st + cbase + col);
+        }
+        for (int idx = threadIdx.x; idx < CHUNK * DK / 4; idx += NT) {
+            const int row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
+            *reinterpret_cast<floatx4*>(Wks + row * WP + col) =
+                *reinterpret_cast<const floatx4*>(wkh + (tok0 + row) * Wk.st + col);
+        }
+        if (w == 0)
+            decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
+#pragma unroll
+        for (int q = 0; q < FPW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int f = 16 * (FPW * w + q) + 4 * g + r;
+                Gs[f * CP + t] = G[q][r];
+                dsc_out[((bh * N + n) * DK + f) * DV + cbase + t] = G[q][r];
+            }
+        __syncthreads();
+
+        const bool fac = decay_factored(tab);
+        for (int tile = w; tile < 16; tile += NW) {
+            const int ib = tile >> 2, jb = tile & 3;
+            floatx4 acc = zero4();
+            if (jb <= ib) {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    acc = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
+                acc = decay_mask<true>(acc, tab, 16 * ib, 16 * jb, fac);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Ps[(16 * ib + 4 * g + r) * PP + 16 * jb + t] = acc[r];
+        }
+        __syncthreads();
+
+        // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
+        {
+            floatx4 acc = zero4(), acc2 = zero4();
+#pragma unroll
+            for (int js = w / 2; js < 2; ++js)
+                acc = mma(split_cols_f32<T>(Ps, PP, 16 * w, 32 * js), frag_cols(dOs, OP, 0, 32 * js), acc);
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                acc2 = mma(frag_rows(Ks, QP, 16 * w, 32 * ks), split_cols_f32<T>(Gs, CP, 0, 32 * ks), acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * g + r;
+                const float u = acc[r] + tab[TAB_F + i] * acc2[r];
+                dUs[i * CP + t] = u;
+                dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u;
+            }
+        }
+        __syncthreads();
+
+        // dS <- gamma_C dS + (Q .* gamma)^T dO - W_k^T dU, this wave's row blocks
+        {
+            const float gC = tab[TAB_G + CHUNK - 1];
+            float qf[2][8];
+            slot_factors(tab + TAB_G, qf);
+#pragma unroll
+            for (int q = 0; q < FPW; ++q) {
+                const int fb = FPW * w + q;
+                floatx4 acc = zero4(), acc2 = zero4();
+#pragma unroll
+                for (int ks = 0; ks < CHUNK / 32; ++ks) {
+                    acc = mma(split_scaled<T>(frag_cols(Qs, QP, 16 * fb, 32 * ks), qf[ks]),
+                              frag_cols(dOs, OP, 0, 32 * ks), acc);
+                    acc2 = mma(split_cols_f32<T>(Wks, WP, 16 * fb, 32 * ks), split_cols_f32<T>(dUs, CP, 0, 32 * ks),
+                               acc2);
+                }
+                G[q] = gC * G[q] + acc - acc2;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < FPW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dS_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t] = G[q][r];
+}
+
+// Per chunk, first part: Y = T^T dU (written over dU), dV, M (written over
+// T) and dbeta.  Workgroup = (chunk, h, b), 4 waves; wave w owns token rows
+// [16 w, 16 w + 16) of Y, dV, M and dbeta (no reduction crosses waves).
+template <typename T, typename OT, int DK, int DV>
+__global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<const T> V,
+                                                           Act<const float> beta, DecayArg dec,
+                                                           const float* __restrict__ s0,
+                                                           const float* __restrict__ u,
+                                                           float* __restrict__ Tm, float* __restrict__ dUY,
+                                                           Act<OT> dVo, Act<float> dbeta, int H)
+{
+    constexpr int NT = 256;
+    constexpr int PAD = Pad<T>::value;
+    constexpr int KP = DK + PAD;
+    constexpr int UP = DV + 4, AP = CHUNK + 4;
+    __shared__ __align__(16) T Ks[CHUNK * KP];
+    __shared__ __align__(16) float Ts[CHUNK * AP];
+    __shared__ __align__(16) float Us[CHUNK * UP];
+    __shared__ __align__(16) float Ys[CHUNK * UP];   // dU, then Y
+    __shared__ __align__(16) float tab[TAB_SIZE];
+    __shared__ float bet[CHUNK];
+
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z, N = gridDim.x;
+    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
+    const int64_t bh = (int64_t)b * H + h;
+    const int64_t tok0 = (int64_t)n * CHUNK;
+    float* Tc = Tm + (bh * N + n) * CHUNK * CHUNK;
+    const float* S0 = s0 + (bh * N + n) * DK * DV;
+    const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
+    float* yc = dUY + (bh * (int64_t)N * CHUNK + tok0) * DV;
+    {
+        ChunkRegs<T, DK, NT> rk;
+        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
+        chunk_store(rk, Ks, KP);
+    }
+    for (int idx = threadIdx.x; idx < CHUNK * CHUNK / 4; idx += NT) {
+        const int row = idx / (CHUNK / 4), col = 4 * (idx % (CHUNK / 4));
+        *reinterpret_cast<floatx4*>(Ts + row * AP + col) = *reinterpret_cast<const floatx4*>(Tc + row * CHUNK + col);
+    }
+    for (int idx = threadIdx.x; idx < CHUNK * DV / 4; idx += NT) {
+        const int row = idx / (DV / 4), col = 4 * (idx % (DV / 4));
+        *reinterpret_cast<floatx4*>(Us + row * UP + col) = *reinterpret_cast<const floatx4*>(uc + row * DV + col);
+        *reinterpret_cast<floatx4*>(Ys + row * UP + col) = *reinterpret_cast<const floatx4*>(yc + row * DV + col);
+    }
+    if (w == 0) {
+        decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
+        bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+    }
+    __syncthreads();
+
+    // Y rows [16 w, 16 w + 16): Y[i][c] = sum_{m >= i} T[m][i] dU[m][c]
+    floatx4 Y[DV / 16];
+#pragma unroll
+    for (int cb = 0; cb < DV / 16; ++cb) {
+        Y[cb] = zero4();
+#pragma unroll
+        for (int ms = w / 2; ms < 2; ++ms)
+            Y[cb] = mma(split_cols_f32<T>(Ts, AP, 16 * w, 32 * ms), split_cols_f32<T>(Ys, UP, 16 * cb, 32 * ms),
+                        Y[cb]);
+    }
+    __syncthreads();   // every wave has read dU
+    float db[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta of rows 16 w + 4g + r, this lane's columns
+    {
+        OT* dvh = dVo.head(b, h) + tok0 * dVo.st;
+        const T* vh = V.head(b, h) + tok0 * V.st;
+        // ROCm 7.2's hipcc merged two of the Y stores below into one
+        // ds_write2_b32 whose first offset was wrong (one Y element per row
+        // 4g + 3 stayed dU); volatile keeps the stores apart.
+        auto* ysv = (volatile __attribute__((address_space(3))) float*)Ys;
+#pragma unroll
+        for (int cb = 0; cb < DV / 16; ++cb) {
+            // (K S_0) tile of rows 16 w, columns 16 cb
+            floatx4 ks0 = zero4();
+#pragma unroll
+            for (int fs = 0; fs < DK / 32; ++fs)
+                ks0 = mma(frag_rows(Ks, KP, 16 * w, 32 * fs), split_cols_glob<T>(S0, DV, 16 * cb, 32 * fs), ks0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * g + r, c = 16 * cb + t;
+                const float y = Y[cb][r];
+                ysv[i * UP + c] = y;
+                yc[i * DV + c] = y;
+                dvh[i * dVo.st + c] = (OT)(bet[i] * y);
+                const float z = (float)vh[i * V.st + c] - tab[TAB_G + i] * ks0[r];
+                db[r] += z * y;
+            }
+        }
+    }
+    __syncthreads();   // Y rows in LDS
+    // dA = -Y U^T (j < i), M = dA .* gamma_i / gamma_j; sum_j M_ij k_i . k_j into dbeta
+    for (int jb = 0; jb <= w; ++jb) {
+        floatx4 dA = zero4(), gk = zero4();
+#pragma unroll
+        for (int cs = 0; cs < DV / 32; ++cs)
+            dA = mma(split_rows_f32<T>(Ys, UP, 16 * w, 32 * cs), split_rows_f32<T>(Us, UP, 16 * jb, 32 * cs), dA);
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+            gk = mma(frag_rows(Ks, KP, 16 * w, 32 * ks), frag_rows(Ks, KP, 16 * jb, 32 * ks), gk);
+        const int j = 16 * jb + t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * g + r;
+            const float m = j < i ? -dA[r] * __expf(tab[TAB_LAM + i] - tab[TAB_LAM + j]) : 0.f;
+            Tc[i * CHUNK + j] = m;
+            db[r] += m * gk[r];
+        }
+    }
+    for (int jb = w + 1; jb < 4; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Tc[(16 * w + 4 * g + r) * CHUNK + 16 * jb + t] = 0.f;
+    // row sums over the 16 lanes of a group
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float x = db[r];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if (t == 0)
+            dbeta.ptr[b * dbeta.sb + h * dbeta.sh + (tok0 + 16 * w + 4 * g + r) * dbeta.st] = x;
+    }
+}
+
+// Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), 4 waves;
+// output tiles are spread over the waves.
+template <typename T, typename OT, int DK, int DV>
+__global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
+                                                           Act<const float> beta, DecayArg dec,
+                                                           const float* __restrict__ s0,
+                                                           const float* __restrict__ dsc,
+                                                           const float* __restrict__ u,
+                                                           const float* __restrict__ Y,
+                                                           const float* __restrict__ Mg, Act<OT> dQo,
+                                                           Act<OT> dKo, int H)
+{
+    constexpr int NT = 256, NW = 4;
+    constexpr int PAD = Pad<T>::value;
+    constexpr int QP = DK + PAD, OP = DV + PAD;
+    constexpr int UP = DV + 4, AP = CHUNK + 4;
+    __shared__ __align__(16) T Qs[CHUNK * QP];
+    __shared__ __align__(16) T Ks[CHUNK * QP];
+    __shared__ __align__(16) T dOs[CHUNK * OP];
+    __shared__ __align__(16) float Us[CHUNK * UP];
+    __shared__ __align__(16) float Ms[CHUNK * AP];
+    __shared__ __align__(16) float dPs[CHUNK * AP];
+    __shared__ __align__(16) float tab[TAB_SIZE];
+    __shared__ float bet[CHUNK];
+
+    const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z, N = gridDim.x;
+    const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
+    const int64_t bh = (int64_t)b * H + h;
+    const int64_t tok0 = (int64_t)n * CHUNK;
+    const float* S0 = s0 + (bh * N + n) * DK * DV;
+    const float* dSC = dsc + (bh * N + n) * DK * DV;
+    const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
+    const float* yc = Y + (bh * (int64_t)N * CHUNK + tok0) * DV;
+    const float* Mc = Mg + (bh * N + n) * CHUNK * CHUNK;
+    {
+        ChunkRegs<T, DK, NT> rq, rk;
+        ChunkRegs<T, DV, NT> ro;
+        chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
+        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
+        chunk_load(ro, dO.head(b, h) + tok0 * dO.st, dO.st);
+        chunk_store(rq, Qs, QP);
+        chunk_store(rk, Ks, QP);
+        chunk_store(ro, dOs, OP);
+    }
+    for (int idx = threadIdx.x; idx < CHUNK * DV / 4; idx += NT) {
+        const int row = idx / (DV / 4), col = 4 * (idx % (DV / 4));
+        *reinterpret_cast<floatx4*>(Us + row * UP + col) = *reinterpret_cast<const floatx4*>(uc + row * DV + col);
+    }
+    for (int idx = threadIdx.x; idx < CHUNK * CHUNK / 4; idx += NT) {
+        const int row = idx / (CHUNK / 4), col = 4 * (idx % (CHUNK / 4));
+        *reinterpret_cast<floatx4*>(Ms + row * AP + col) = *reinterpret_cast<const floatx4*>(Mc + row * CHUNK + col);
+    }
+    if (w == 0) {
+        decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
+        bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+    }
+    __syncthreads();
+
+    // dP .* D = (dO U^T) .* D, causal (incl. the diagonal)
+    const bool fac = decay_factored(tab);
+    for (int tile = w; tile < 16; tile += NW) {
+        const int ib = tile >> 2, jb = tile & 3;
+        floatx4 acc = zero4();
+        if (jb <= ib) {
+#pragma unroll
+            for (int cs = 0; cs < DV / 32; ++cs)
+                acc = mma(frag_rows(dOs, OP, 16 * ib, 32 * cs), split_rows_f32<T>(Us, UP, 16 * jb, 32 * cs), acc);
+            acc = decay_mask<true>(acc, tab, 16 * ib, 16 * jb, fac);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            dPs[(16 * ib + 4 * g + r) * AP + 16 * jb + t] = acc[r];
+    }
+    __syncthreads();
+
+    constexpr int NFB = DK / 16;
+    for (int job = w; job < 8 * NFB; job += NW) {
+        const bool isk = job >= 4 * NFB;
+        const int jj = isk ? job - 4 * NFB : job, rb = jj & 3, fb = jj >> 2;
+        floatx4 acc = zero4();
+        if (!isk) {
+            // dQ[i][f] = gamma_i (dO S_0^T)[i][f] + (dP .* D) K
+#pragma unroll
+            for (int cs = 0; cs < DV / 32; ++cs)
+                acc = mma(frag_rows(dOs, OP, 16 * rb, 32 * cs), split_rows_glob<T>(S0, DV, 16 * fb, 32 * cs), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= tab[TAB_G + 16 * rb + 4 * g + r];
+#pragma unroll
+            for (int js = 0; js <= rb / 2; ++js)
+                acc = mma(split_rows_f32<T>(dPs, AP, 16 * rb, 32 * js), frag_cols(Ks, QP, 16 * fb, 32 * js), acc);
+            OT* out = dQo.head(b, h) + tok0 * dQo.st;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                out[(16 * rb + 4 * g + r) * dQo.st + 16 * fb + t] = (OT)acc[r];
+        } else {
+            // dK[j][f]: five terms with different row factors
+            floatx4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4();
+#pragma unroll
+            for (int is = rb / 2; is < 2; ++is) {
+                // (dP .* D)^T Q  and  M^T (beta .* K)    (i >= j)
+                acc = mma(split_cols_f32<T>(dPs, AP, 16 * rb, 32 * is), frag_cols(Qs, QP, 16 * fb, 32 * is), acc);
+                float bf[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    bf[r] = bet[32 * is + 8 * g + r];
+                acc = mma(split_cols_f32<T>(Ms, AP, 16 * rb, 32 * is),
+                          split_scaled<T>(frag_cols(Ks, QP, 16 * fb, 32 * is), bf), acc);
+            }
+#pragma unroll
+            for (int is = 0; is <= rb / 2; ++is)   // M K  (i < j)
+                a3 = mma(split_rows_f32<T>(Ms, AP, 16 * rb, 32 * is), frag_cols(Ks, QP, 16 * fb, 32 * is), a3);
+#pragma unroll
+            for (int cs = 0; cs < DV / 32; ++cs) {
+                a1 = mma(split_rows_f32<T>(Us, UP, 16 * rb, 32 * cs), split_rows_glob<T>(dSC, DV, 16 * fb, 32 * cs), a1);
+                a2 = mma(split_rows_glob<T>(yc, DV, 16 * rb, 32 * cs), split_rows_glob<T>(S0, DV, 16 * fb, 32 * cs), a2);
+            }
+            (void)a4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * rb + 4 * g + r;
+                acc[r] += tab[TAB_F + j] * a1[r] - bet[j] * tab[TAB_G + j] * a2[r] + bet[j] * a3[r];
+            }
+            OT* out = dKo.head(b, h) + tok0 * dKo.st;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                out[(16 * rb + 4 * g + r) * dKo.st + 16 * fb + t] = (OT)acc[r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 namespace {
@@ -290,19 +713,64 @@ hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
     const Act<float> wk{s.wk, (int64_t)s.H * s.T * DK, (int64_t)s.T * DK, DK};
     const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
     const int N = s.T / CHUNK;
-    hipLaunchKernelGGL((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), 0, stream,
-                       dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.H);
+    launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
+                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, nullptr, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((delta_scan_kernel<T, OT, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256), 0,
-                       stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
-                       Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, dec, s.S_in, s.S_out,
-                       Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.H, N);
+    launch_kernel((delta_scan_kernel<T, OT, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256),
+                  stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
+                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, dec, s.S_in, s.S_out,
+                  Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N);
+    return hipGetLastError();
+}
+
+template <typename T, typename OT, int DK, int DV>
+hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
+{
+    const DecayArg dec{(const float*)s.decay.ptr, s.decay.sb, s.decay.sh, s.decay.st, s.decay_kind};
+    const int N = s.T / CHUNK;
+    const Act<float> wk{s.wk, (int64_t)s.H * s.T * DK, (int64_t)s.T * DK, DK};
+    const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
+    launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
+                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.tm, s.H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    launch_kernel((delta_bscan_kernel<T, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
+                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
+                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, dec, s.dS_out, s.dS_in, s.duy,
+                  s.dsc, s.H, N);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
+                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, (const float*)s.s0,
+                  (const float*)s.u, s.tm, s.duy, Act<OT>{(OT*)s.dv_.ptr, s.dv_.sb, s.dv_.sh, s.dv_.st},
+                  Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
+                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), dec,
+                  (const float*)s.s0, (const float*)s.dsc, (const float*)s.u, (const float*)s.duy,
+                  (const float*)s.tm, Act<OT>{(OT*)s.dq.ptr, s.dq.sb, s.dq.sh, s.dq.st},
+                  Act<OT>{(OT*)s.dk_.ptr, s.dk_.sb, s.dk_.sh, s.dk_.st}, s.H);
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_delta_bwd(const DeltaBwdLaunch& s, hipStream_t stream)
+{
+    if (s.dtype == 0 && s.dk == 128 && s.dv == 128)
+        return s.out_dtype == 0 ? delta_bwd_impl<bf16, bf16, 128, 128>(s, stream)
+                                : delta_bwd_impl<bf16, float, 128, 128>(s, stream);
+    if (s.dtype == 0 && s.dk == 64 && s.dv == 64)
+        return s.out_dtype == 0 ? delta_bwd_impl<bf16, bf16, 64, 64>(s, stream)
+                                : delta_bwd_impl<bf16, float, 64, 64>(s, stream);
+    if (s.dtype == 1 && s.dk == 64 && s.dv == 64 && s.out_dtype == 1)
+        return delta_bwd_impl<float, float, 64, 64>(s, stream);
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_delta_fwd(const DeltaFwdLaunch& s, hipStream_t stream)
 {

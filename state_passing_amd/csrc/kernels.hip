@@ -764,13 +764,13 @@ hipError_t sum_impl(const ScanLaunch& s, hipStream_t stream)
 {
     const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
     if (s.reverse)
-        hipLaunchKernelGGL((seg_sum_kernel<T, DK, DV, true>), grid, block, 0, stream, cact<T>(s.x),
-                           cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
-                           s.store_nseg, s.H, s.N, s.m);
+        launch_kernel((seg_sum_kernel<T, DK, DV, true>), grid, block, stream, cact<T>(s.x),
+                      cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                      s.store_nseg, s.H, s.N, s.m);
     else
-        hipLaunchKernelGGL((seg_sum_kernel<T, DK, DV, false>), grid, block, 0, stream, cact<T>(s.x),
-                           cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
-                           s.store_nseg, s.H, s.N, s.m);
+        launch_kernel((seg_sum_kernel<T, DK, DV, false>), grid, block, stream, cact<T>(s.x),
+                      cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                      s.store_nseg, s.H, s.N, s.m);
     return hipGetLastError();
 }
 
@@ -780,11 +780,11 @@ hipError_t fold_impl(const ScanLaunch& s, hipStream_t stream)
     const int nseg = (s.N + s.m - 1) / s.m;
     const dim3 grid(DK * DV / 1024, s.H, s.B), block(256);
     if (s.reverse)
-        hipLaunchKernelGGL((seg_fold_kernel<DK, DV, true>), grid, block, 0, stream, s.carry_in,
-                           s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
+        launch_kernel((seg_fold_kernel<DK, DV, true>), grid, block, stream, s.carry_in,
+                      s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
     else
-        hipLaunchKernelGGL((seg_fold_kernel<DK, DV, false>), grid, block, 0, stream, s.carry_in,
-                           s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
+        launch_kernel((seg_fold_kernel<DK, DV, false>), grid, block, stream, s.carry_in,
+                      s.carry_out, (float*)s.store, s.store_nseg, s.H, nseg);
     return hipGetLastError();
 }
 
@@ -792,9 +792,9 @@ template <typename T, typename OT, int DK, int DV>
 hipError_t fwd_seg_impl(const FwdIntraLaunch& s, hipStream_t stream)
 {
     const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
-    hipLaunchKernelGGL((fwd_seg_kernel<T, OT, DK, DV>), grid, block, 0, stream,
-                       cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), decay_arg(s.decay, s.decay_kind),
-                       (const float*)s.states, s.st_nseg, mact<OT>(s.o), s.H, s.N, s.m);
+    launch_kernel((fwd_seg_kernel<T, OT, DK, DV>), grid, block, stream,
+                  cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), decay_arg(s.decay, s.decay_kind),
+                  (const float*)s.states, s.st_nseg, mact<OT>(s.o), s.H, s.N, s.m);
     return hipGetLastError();
 }
 
@@ -805,18 +805,18 @@ hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
     if (s.m > 4)
         return hipErrorInvalidValue;
     if (s.da.ptr)
-        hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV, true>), grid, block, 0, stream,
-                           cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                           decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
-                           (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                           mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold);
+        launch_kernel((bwd_seg_kernel<T, OT, DK, DV, true>), grid, block, stream,
+                      cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                      decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                      (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                      mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold);
     else
-        hipLaunchKernelGGL((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, 0, stream,
-                           cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                           decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
-                           (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                           mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
-                           s.m, s.fold);
+        launch_kernel((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, stream,
+                      cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                      decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                      (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                      mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
+                      s.m, s.fold);
     return hipGetLastError();
 }
 
@@ -872,9 +872,9 @@ hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream)
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream)
 {
     const int seg_len = s.m * CHUNK, nseg = (s.N + s.m - 1) / s.m;
-    hipLaunchKernelGGL(da_finish_kernel, dim3(s.H, s.B), dim3(1024), 0, stream, mact<float>(s.da),
-                       decay_arg(s.decay, s.decay_kind), s.tot, s.carry_in, s.carry_out, s.H,
-                       s.N * CHUNK, seg_len, nseg);
+    launch_kernel(da_finish_kernel, dim3(s.H, s.B), dim3(1024), stream, mact<float>(s.da),
+                  decay_arg(s.decay, s.decay_kind), s.tot, s.carry_in, s.carry_out, s.H,
+                  s.N * CHUNK, seg_len, nseg);
     return hipGetLastError();
 }
 

@@ -2,10 +2,41 @@
 // kernel launchers (plain data; pointers are device addresses).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace linrec {
+
+// Per-kernel timing.  When `stop` is set, the kernels launched on this thread
+// carry the two events as their dispatch's own start and end stamps (so the
+// measured time is the kernels' execution, as a kernel trace reports it, not
+// queueing or the dispatch latency before them).  The first launch takes
+// `start`; every launch takes `stop`, so a call that launches several kernels
+// spans from the first one's start to the last one's end.
+struct LaunchStamps {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+inline LaunchStamps& launch_stamps()
+{
+    static thread_local LaunchStamps s;
+    return s;
+}
+
+// Every kernel of the library is launched through here (no dynamic LDS).
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                          Args... args)
+{
+    LaunchStamps& st = launch_stamps();
+    if (st.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, st.start, st.stop, 0, args...);
+        st.start = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    }
+}
 
 // Floats per stored segment record: a d_k x d_v state, then the segment's
 // total log-decay, padded so records stay 256-byte aligned.
@@ -95,6 +126,26 @@ struct DeltaFwdLaunch {
     float* S_out;
     float* wk;
     float* wv;
+    float* s0;               // optional: the state entering every chunk, [B][H][N][d_k][d_v]
+    float* u;                // optional: U of every token, [B][H][T][d_v]
+};
+
+// Gated delta rule, backward over one piece, from the forward's saved s0 and
+// u.  Workspace: W_k, W_v (as the forward), T then M per chunk
+// ([B][H][N][64][64]), dU then Y ([B][H][T][d_v]), dS_C per chunk.
+struct DeltaBwdLaunch {
+    int dtype, out_dtype, dk, dv, B, H, T;
+    TensorArg q, k, v, beta, decay, dO, dq, dk_, dv_, dbeta;
+    int decay_kind;
+    const float* s0;
+    const float* u;
+    const float* dS_out;     // may be NULL (zeros)
+    float* dS_in;
+    float* wk;
+    float* wv;
+    float* tm;
+    float* duy;
+    float* dsc;
 };
 
 // The state transition is two launches: the parallel segment sum, then the
@@ -105,5 +156,6 @@ hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream);
 hipError_t launch_delta_fwd(const DeltaFwdLaunch& s, hipStream_t stream);
+hipError_t launch_delta_bwd(const DeltaBwdLaunch& s, hipStream_t stream);
 
 }  // namespace linrec

@@ -43,11 +43,12 @@ EXPORTS = (
     "linrec_last_hip_error", "linrec_version", "linrec_ctx_set_timing",
     "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
     "linrec_bwd_da_workspace_bytes", "linrec_bwd_da", "linrec_bwd_noalloc",
-    "linrec_delta_workspace_bytes", "linrec_delta_fwd",
+    "linrec_delta_workspace_bytes", "linrec_delta_fwd", "linrec_delta_saved_bytes",
+    "linrec_delta_bwd_workspace_bytes", "linrec_delta_bwd",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
-                5: "bwd_seg", 6: "da_finish", 7: "delta_fwd"}
+                5: "bwd_seg", 6: "da_finish", 7: "delta_fwd", 8: "delta_bwd"}
 
 
 class LinrecError(RuntimeError):
@@ -97,7 +98,10 @@ def _lib():
         "linrec_bwd_da_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_bwd_noalloc": ([P, D, T, T, T, T, P, T, P, T, T, T, P, P], ctypes.c_int),
         "linrec_delta_workspace_bytes": ([D], ctypes.c_size_t),
-        "linrec_delta_fwd": ([P, D, T, T, T, T, T, P, T, P, P, P], ctypes.c_int),
+        "linrec_delta_fwd": ([P, D, T, T, T, T, T, P, T, P, P, P, P], ctypes.c_int),
+        "linrec_delta_saved_bytes": ([D], ctypes.c_size_t),
+        "linrec_delta_bwd_workspace_bytes": ([D], ctypes.c_size_t),
+        "linrec_delta_bwd": ([P, D, T, T, T, T, T, P, T, P, T, T, T, T, P, P, P], ctypes.c_int),
         "linrec_bwd_da": ([P, D, T, T, T, T, P, T, P, T, T, T, P, T, P, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
@@ -601,33 +605,87 @@ def delta_workspace_bytes(d: Desc) -> int:
     return int(_lib().linrec_delta_workspace_bytes(ctypes.byref(d)))
 
 
-def delta_fwd(q, k, v, beta, decay=None, S_in=None, *, o=None, S_out=None, workspace=None,
-              out_dtype=None):
+def delta_saved_bytes(d: Desc) -> int:
+    return int(_lib().linrec_delta_saved_bytes(ctypes.byref(d)))
+
+
+def delta_bwd_workspace_bytes(d: Desc) -> int:
+    return int(_lib().linrec_delta_bwd_workspace_bytes(ctypes.byref(d)))
+
+
+def _beta_arg(name, x, B, H, T):
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.shape != (B, H, T):
+        _fail(f"{name}: must be float32 [B,H,T] = {(B, H, T)}")
+    st = x.stride()
+    return Tensor(x.data_ptr(), st[0], st[1], st[2])
+
+
+def delta_fwd(q, k, v, beta, decay=None, S_in=None, *, o=None, S_out=None, saved=None,
+              save=False, workspace=None, out_dtype=None):
     """Gated delta rule, forward over one piece (linrec_delta_fwd):
     S_t = a_t (I - beta_t k_t^T k_t) S_{t-1} + beta_t k_t^T v_t, o_t = q_t S_t.
-    beta: fp32 [B,H,T].  Returns (o, S_out)."""
+    beta: fp32 [B,H,T].  With save=True (or a `saved` buffer) the states and
+    values the backward needs are kept.  Returns (o, S_out, saved or None)."""
     odt = _out_dtype(q, out_dtype, o)
     devs = _validate(q, k, v, decay, outs=_outs(q, v, odt, o=o), states_in=(("S_in", S_in),),
-                     states_out=(("S_out", S_out),), extra=(("beta", beta), ("workspace", workspace)))
+                     states_out=(("S_out", S_out),),
+                     extra=(("beta", beta), ("workspace", workspace), ("saved", saved)))
     B, H, T, DK = q.shape
     DV = v.shape[3]
-    if not isinstance(beta, torch.Tensor) or beta.dtype != torch.float32 or beta.shape != (B, H, T):
-        _fail(f"beta: must be float32 [B,H,T] = {(B, H, T)}")
+    barg = _beta_arg("beta", beta, B, H, T)
     kind, dec = _decay(decay)
     d = _desc_of(q, v, kind, odt)
     if workspace is not None:
         _check_buffer("workspace", workspace, delta_workspace_bytes(d))
+    if saved is not None:
+        _check_buffer("saved", saved, delta_saved_bytes(d))
     _check_device(q, *devs)
     o = _new_act(q, DV, odt, o)
     S_out = _state_out(q, B, H, DK, DV, S_out)
     if workspace is None:
         workspace = torch.empty(max(delta_workspace_bytes(d), 16), dtype=torch.uint8, device=q.device)
-    bs = beta.stride()
+    if saved is None and save:
+        saved = torch.empty(max(delta_saved_bytes(d), 16), dtype=torch.uint8, device=q.device)
     rc = _lib().linrec_delta_fwd(context(q.device.index), ctypes.byref(d), _act(q), _act(k), _act(v),
-                                 Tensor(beta.data_ptr(), bs[0], bs[1], bs[2]), dec, _ptr(S_in),
-                                 _act(o), _ptr(S_out), _ptr(workspace), _stream(q.device))
+                                 barg, dec, _ptr(S_in), _act(o), _ptr(S_out), _ptr(saved),
+                                 _ptr(workspace), _stream(q.device))
     _check(rc, "linrec_delta_fwd")
-    return o, S_out
+    return o, S_out, saved
+
+
+def delta_bwd(q, k, v, beta, decay, saved, dO, dS_out=None, *, dq=None, dk=None, dv=None,
+              dbeta=None, dS_in=None, workspace=None, out_dtype=None):
+    """Gated delta rule, backward over one piece (linrec_delta_bwd) from the
+    forward's `saved` buffer.  Returns (dq, dk, dv, dbeta, dS_in)."""
+    odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+                     states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+                     extra=(("beta", beta), ("saved", saved), ("workspace", workspace),
+                            ("dbeta", dbeta)))
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    barg = _beta_arg("beta", beta, B, H, T)
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    _check_buffer("saved", saved, delta_saved_bytes(d))
+    if workspace is not None:
+        _check_buffer("workspace", workspace, delta_bwd_workspace_bytes(d))
+    if dbeta is not None:
+        _beta_arg("dbeta", dbeta, B, H, T)
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
+    dS_in = _state_out(q, B, H, DK, DV, dS_in)
+    if dbeta is None:
+        dbeta = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(delta_bwd_workspace_bytes(d), 16), dtype=torch.uint8,
+                                device=q.device)
+    rc = _lib().linrec_delta_bwd(context(q.device.index), ctypes.byref(d), _act(q), _act(k), _act(v),
+                                 barg, dec, _ptr(saved), _act(dO), _ptr(dS_out), _act(dq), _act(dk),
+                                 _act(dv), _beta_arg("dbeta", dbeta, B, H, T), _ptr(dS_in),
+                                 _ptr(workspace), _stream(q.device))
+    _check(rc, "linrec_delta_bwd")
+    return dq, dk, dv, dbeta, dS_in
 
 
 def piece_loop(q, k, v, decay, lengths: Sequence[int], S_in=None, dO=None, dS_out=None,

@@ -239,12 +239,30 @@ def test_delta_arguments():
     assert linrec.delta_workspace_bytes(d(dk=64)) == 0        # d_k != d_v
     assert linrec.delta_workspace_bytes(d(T=100)) == 0
 
-    def call(desc, beta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), ws=FAKE):
+    def call(desc, beta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), ws=FAKE, saved=None):
         return lib.linrec_delta_fwd(None, ctypes.byref(desc), act(), act(), act(), beta,
-                                    linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, ws, None)
+                                    linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, saved, ws, None)
     assert call(d()) == E["LINREC_E_NULL"]                   # checks pass, no context
     assert call(d(dk=64)) == E["LINREC_E_SHAPE"]
     assert call(d(), beta=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
     assert call(d(), beta=linrec.Tensor(FAKE + 2, 0, 0, 1)) == E["LINREC_E_ALIGN"]
     assert call(d(), beta=linrec.Tensor(FAKE, -1, 0, 1)) == E["LINREC_E_LAYOUT"]
     assert call(d(), ws=None) == E["LINREC_E_WORKSPACE"]
+    assert call(d(), saved=FAKE + 8) == E["LINREC_E_WORKSPACE"]
+    assert call(d(), saved=FAKE) == E["LINREC_E_NULL"]
+    # saved: one state per chunk and U per token; backward workspace: W_k, W_v,
+    # T per chunk, dU per token and one gradient state per chunk
+    N = 4096 // 64
+    assert linrec.delta_saved_bytes(d()) == 16 * (N * 128 * 128 + 4096 * 128) * 4
+    assert linrec.delta_bwd_workspace_bytes(d()) == \
+        16 * (4096 * 384 + N * 64 * 64 + N * 128 * 128) * 4
+
+    def bcall(desc, dbeta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), saved=FAKE):
+        return lib.linrec_delta_bwd(None, ctypes.byref(desc), act(), act(), act(),
+                                    linrec.Tensor(FAKE, 16 * 4096, 4096, 1),
+                                    linrec.Tensor(FAKE, 0, 1, 0), saved, act(), None, act(), act(),
+                                    act(), dbeta, FAKE, FAKE, None)
+    assert bcall(d()) == E["LINREC_E_NULL"]
+    assert bcall(d(), dbeta=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
+    assert bcall(d(), saved=None) == E["LINREC_E_WORKSPACE"]
+    assert bcall(d(dk=64)) == E["LINREC_E_SHAPE"]

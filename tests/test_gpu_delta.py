@@ -1,7 +1,8 @@
-"""GPU parity of the gated delta-rule forward (linrec_delta_fwd, through the
-C ABI) against the fp64 delta-rule oracle: small cases over every decay kind,
-d = 64 and 128, fp32 and bf16 inputs, a nonzero S_in, pieces chained through
-S_out -> S_in, and the 16-head, 16K-token gated workload on sampled heads.
+"""GPU parity of the gated delta rule (linrec_delta_fwd / linrec_delta_bwd,
+through the C ABI) against the fp64 delta-rule oracle: small cases over every
+decay kind, d = 64 and 128, fp32 and bf16 inputs, a nonzero S_in and dS_out,
+pieces chained through S_out -> S_in and dS_in -> dS_out, and the 16-head,
+16K-token gated workload on sampled heads.
 
 Error measure as for the linear recurrence: max|X_gpu - X_oracle| / RMS(X_oracle)
 per tensor, fp32 outputs, bar 2e-2 for bf16 inputs and 1e-4 for fp32."""
@@ -37,14 +38,14 @@ SMALL = [
 
 
 def to_dev(inp):
-    for name in ("q", "k", "v", "S_in", "decay", "beta"):
+    for name in ("q", "k", "v", "dO", "S_in", "dS_out", "decay", "beta"):
         x = getattr(inp, name)
         if x is not None:
             setattr(inp, name, x.to(DEV))
     return inp
 
 
-def oracle_delta(inp, heads=None):
+def oracle_delta(inp, heads=None, backward=False):
     wl = inp.wl
     if heads is None:
         heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
@@ -55,7 +56,13 @@ def oracle_delta(inp, heads=None):
              else pick(inp.decay))
     o, S_out = oracle.delta_fwd(pick(inp.q), pick(inp.k), pick(inp.v), pick(inp.beta), a,
                                 pick(inp.S_in))
-    return {"o": o, "S_out": S_out}
+    out = {"o": o, "S_out": S_out}
+    if backward:
+        dq, dk, dv, db, dS_in = oracle.delta_bwd(pick(inp.q), pick(inp.k), pick(inp.v),
+                                                 pick(inp.beta), a, pick(inp.S_in), pick(inp.dO),
+                                                 pick(inp.dS_out))
+        out.update(dq=dq, dk=dk, dv=dv, dbeta=db, dS_in=dS_in)
+    return out
 
 
 def errors(got, ref, heads):
@@ -67,19 +74,51 @@ def errors(got, ref, heads):
     return out
 
 
-def run_pieces(inp, lengths):
-    """The pieces one after another, S carried through S_out -> S_in."""
+def run_pieces(inp, lengths, backward=False):
+    """The pieces one after another, S carried through S_out -> S_in, then
+    (backward) in reverse with dS carried through dS_in -> dS_out."""
     S = inp.S_in
     o = torch.empty(inp.v.shape, dtype=torch.float32, device=DEV)
-    t0 = 0
+    bounds, saved = [0], []
     for L in lengths:
-        sl = slice(t0, t0 + L)
-        dec = inp.decay if inp.decay is None or inp.decay.dim() == 1 else inp.decay[:, :, sl]
-        _, S = linrec.delta_fwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl],
-                                inp.beta[:, :, sl], dec, S, o=o[:, :, sl])
-        t0 += L
+        bounds.append(bounds[-1] + L)
+    dsl = lambda x, sl: x if x is None or x.dim() == 1 else x[:, :, sl]  # noqa: E731
+    for i in range(len(lengths)):
+        sl = slice(bounds[i], bounds[i + 1])
+        _, S, sv = linrec.delta_fwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl],
+                                    inp.beta[:, :, sl], dsl(inp.decay, sl), S, o=o[:, :, sl],
+                                    save=backward)
+        saved.append(sv)
+    out = {"o": o, "S_out": S}
+    if backward:
+        dq, dk, dv = (torch.empty(x.shape, dtype=torch.float32, device=DEV) for x in (inp.q, inp.k, inp.v))
+        db = torch.empty(inp.beta.shape, dtype=torch.float32, device=DEV)
+        dS = inp.dS_out
+        for i in reversed(range(len(lengths))):
+            sl = slice(bounds[i], bounds[i + 1])
+            _, _, _, _, dS = linrec.delta_bwd(inp.q[:, :, sl], inp.k[:, :, sl], inp.v[:, :, sl],
+                                              inp.beta[:, :, sl], dsl(inp.decay, sl), saved[i],
+                                              inp.dO[:, :, sl], dS, dq=dq[:, :, sl], dk=dk[:, :, sl],
+                                              dv=dv[:, :, sl], dbeta=db[:, :, sl], out_dtype=torch.float32)
+        out.update(dq=dq, dk=dk, dv=dv, dbeta=db, dS_in=dS)
     torch.cuda.synchronize()
-    return {"o": o, "S_out": S}
+    return out
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_delta_backward_small(wl):
+    """Forward with the saved states, backward against the oracle's gradients
+    (q, k, v, beta, S_in) with a nonzero dS_out; whole piece and chained."""
+    print(f"case {wl}", flush=True)
+    inp = to_dev(make_inputs(wl, device="cpu", seed=11, with_dS_out=True))
+    ref = oracle_delta(inp, backward=True)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    splits = [[wl.T]] + ([[64, wl.T - 192, 128]] if wl.T >= 256 else [])
+    for lens in splits:
+        errs = errors(run_pieces(inp, lens, backward=True), ref, heads)
+        print(f"[{wl.name} pieces {lens}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+              flush=True)
+        assert all(v <= TOL[wl.dtype] for v in errs.values()), errs
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
@@ -120,11 +159,13 @@ def test_delta_unit_key_overwrite_exact():
 
 
 def test_delta_gated_16k_sampled_heads():
+    """Forward and backward over the 4 pieces of the 16-head, 16K-token gated
+    workload; the oracle runs unsplit on three heads."""
     wl = DELTA_WORKLOADS[6]
     heads = [(0, 0), (0, 7), (0, 15)]
     inp = make_inputs(wl, device=DEV)
-    ref = oracle_delta(inp, heads)
-    got = run_pieces(inp, wl.pieces())
+    ref = oracle_delta(inp, heads, backward=True)
+    got = run_pieces(inp, wl.pieces(), backward=True)
     errs = errors(got, ref, heads)
     print(f"[{wl.name} {len(wl.pieces())} pieces] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
           flush=True)

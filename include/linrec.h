@@ -43,8 +43,8 @@
  *           LINREC_DECAY_TOKEN -> fp32 [B, H, T] with strides (sb, sh, st).
  *           Values must lie in (0, 1].
  *   S_in, S_out, dS_out, dS_in: contiguous fp32 [B, H, d_k, d_v].
- *   states: opaque, linrec_states_bytes() bytes, 256-byte aligned.
- *   workspace: opaque, linrec_bwd_workspace_bytes() bytes, 256-byte aligned.
+ *   states: opaque, linrec_states_bytes() bytes, 16-byte aligned.
+ *   workspace: opaque, linrec_bwd_workspace_bytes() bytes, 16-byte aligned.
  *
  * ---------------------------------------------------------------- dtypes
  *   dtype (inputs q, k, v, dO):

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -888,7 +889,11 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
 
 const char* linrec_status_str(linrec_status s)
 {
-    switch (s) {
+    // a C caller may pass any int; read it as one (an out-of-range value
+    // loaded as the enum type is undefined in C++)
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case LINREC_OK: return "ok";
     case LINREC_E_NULL: return "required pointer is NULL";
     case LINREC_E_SHAPE: return "unsupported shape";

@@ -57,7 +57,10 @@ KERNEL_BYTES = {
     "fwd_seg": 1024,       # reads q, k, v, writes o
     "bwd_sum": 512,        # reads q, dO
     "bwd_fold": 0,
-    "bwd_seg": 1792,       # reads q, k, v, dO, writes dq, dk, dv
+    # reads q, k, v, dO, writes dq, dk, dv; in the sequence backward the
+    # launch also computes another piece's segment sums (q, dO: 62 launches
+    # of 64 in a step)
+    "bwd_seg": 1792 + 512 * 62 / 64,
 }
 # per-launch bytes of each kernel as designed, per token-head: one fp32
 # d_k x d_v record or state per 256-token segment is 256 B per token-head
@@ -68,9 +71,10 @@ KERNEL_DESIGN_BYTES = {
     "bwd_sum": 512 + 256,          # q, dO; writes the gradient records
     "bwd_fold": 256 + 256,
     # k, v, dO for dQ; q, and k, v, dO again except on the chunk both walks
-    # share (one of four); dq, dk, dv; the S and G segment states; and the
-    # previous piece's fold it carries (63 launches of 64 in a step)
-    "bwd_seg": 768 + 256 + 576 + 768 + 512 + 512 * 63 / 64,
+    # share (one of four); dq, dk, dv; the S and G segment states; the fold
+    # it carries (63 launches of 64 in a step) and the segment sums it
+    # carries (62 of 64)
+    "bwd_seg": 768 + 256 + 576 + 768 + 512 + 512 * 63 / 64 + 768 * 62 / 64,
 }
 KERNEL_SYMBOL = {
     "fwd_sum": "seg_sum_kernel<bf16,128,128,false>",

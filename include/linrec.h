@@ -280,7 +280,7 @@ linrec_status linrec_fwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              void* stream);
 
 /* Bytes of workspace linrec_bwd_seq needs for these pieces (0 if invalid):
- * two slots, each holding the gradient records of the longest piece. */
+ * three slots, each holding the gradient records of the longest piece. */
 size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
                                       const int32_t* lengths);
 
@@ -288,12 +288,14 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
  * from dS_out to dS_in, each piece's backward running over the states its
  * forward stored (the backward pass over stored states of Sequence
  * Accumulation and Beyond, "Approach"; boundary gradients carried from piece
- * to piece: StateFlow, Abstract).  Every launch goes to `stream` (the
- * backward segment kernel occupies a whole CU, so a concurrent transition
- * kernel would only delay it).  Piece i - 1's reverse fold, which needs
- * piece i's dS_in, travels inside piece i's segment-kernel launch; the
- * gradient records of consecutive pieces alternate between the workspace's
- * two slots.  Same arguments and rules as linrec_bwd otherwise; `states` as
+ * to piece: StateFlow, Abstract; state transitions overlapped with the
+ * surrounding computation: StateFlow, Abstract).  Every launch goes to
+ * `stream`, one per piece: piece i's segment-kernel launch also carries
+ * piece i - 1's reverse fold (which needs piece i's dS_in) and piece
+ * i - 2's segment sums, as extra work of the same grid (a transition kernel
+ * on a second stream could not share a CU with the segment kernel, whose
+ * LDS fills it).  The gradient records of piece j live in workspace slot
+ * j % 3.  Same arguments and rules as linrec_bwd otherwise; `states` as
  * written by linrec_fwd_seq. */
 linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
                              int32_t npieces, const int32_t* lengths,

@@ -551,7 +551,7 @@ size_t linrec_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces, con
 {
     if (check_desc(d) != LINREC_OK || check_pieces(d, npieces, lengths) != LINREC_OK)
         return 0;
-    return 2 * bwd_seq_slot_bytes(d, npieces, lengths);
+    return 3 * bwd_seq_slot_bytes(d, npieces, lengths);
 }
 
 linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
@@ -738,15 +738,18 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         return st;
     hipStream_t s = (hipStream_t)stream;
     const int64_t nseg_total = total_nseg(npieces, lengths);
-    // Every launch goes to the caller's stream, one piece after another (the
-    // backward segment kernel fills each CU's LDS, so transition kernels on a
-    // second stream would only delay its workgroups).  Piece i - 1's segment
-    // sums run before piece i's segment kernel, and piece i - 1's fold (which
-    // needs piece i's dS_in) travels inside that launch; only the last
-    // piece's fold has a launch of its own.  The gradient records of
-    // consecutive pieces alternate between the workspace's two slots.
+    // Every launch goes to the caller's stream, one per piece: the segment
+    // kernel of piece i carries, as extra work in the same launch, the fold
+    // of piece i - 1 (which needs piece i's dS_in, left by the previous
+    // launch) and the segment sums of piece i - 2 (which need nothing
+    // carried).  The state transition thus runs beside the intra-chunk work
+    // on the CUs the segment kernel leaves free, without a launch of its own.
+    // A prologue does the last piece's sums and fold and the next piece's
+    // sums.  The gradient records of piece j live in workspace slot j % 3:
+    // one launch reads slot i % 3, folds slot (i - 1) % 3 and writes
+    // slot (i - 2) % 3.
     const size_t slot_bytes = bwd_seq_slot_bytes(d, npieces, lengths);
-    auto slot_ptr = [&](int32_t i) { return (void*)((char*)workspace + (i & 1) * slot_bytes); };
+    auto slot_ptr = [&](int32_t i) { return (void*)((char*)workspace + (i % 3) * slot_bytes); };
     std::vector<int64_t> tok0s(npieces), seg0s(npieces);
     for (int32_t i = 0, t0 = 0, g0 = 0; i < npieces; ++i) {
         tok0s[i] = t0;
@@ -759,15 +762,23 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
     };
     const ScanLaunch last = scan_of(npieces - 1, dS_out);
     LAUNCH_SCAN(ctx, last, s);
+    if (npieces > 1) {
+        const ScanLaunch next = scan_of(npieces - 2, dS_in);
+        LAUNCH(timed_launch(ctx, LINREC_KERNEL_BWD_SUM, s,
+                            [&] { return linrec::launch_seg_sum(next, s); }));
+    }
     for (int32_t i = npieces - 1; i >= 0; --i) {
         BwdIntraLaunch in = bwd_intra_of(d, q, k, v, decay, dO, dq, dk, dv, tok0s[i], lengths[i],
                                          states, seg0s[i], nseg_total, slot_ptr(i));
         if (i > 0) {
             const ScanLaunch prev = scan_of(i - 1, dS_in);
-            LAUNCH(timed_launch(ctx, LINREC_KERNEL_BWD_SUM, s,
-                                [&] { return linrec::launch_seg_sum(prev, s); }));
             in.fold = linrec::FoldArg{dS_in, dS_in, (float*)prev.store, prev.store_nseg,
                                       (int32_t)nseg_of(lengths[i - 1])};
+        }
+        if (i > 1) {
+            const ScanLaunch sums = scan_of(i - 2, dS_in);
+            in.sum = linrec::SumArg{sums.x, sums.y, sums.decay, sums.decay_kind, sums.store,
+                                    sums.store_nseg, sums.N, sums.m, (int)nseg_of(lengths[i - 2])};
         }
         LAUNCH_BWD_INTRA(ctx, in, s);
     }

@@ -41,6 +41,16 @@
 
 namespace linrec {
 
+// Device side of SumArg.
+template <typename T>
+struct SumDev {
+    Act<const T> X, Y;
+    DecayArg dec;
+    float* store;
+    int64_t store_nseg;
+    int N, m, nseg;
+};
+
 // ---------------------------------------------------------------------------
 // Shared pieces of the segment kernels.
 // ---------------------------------------------------------------------------
@@ -134,22 +144,20 @@ __device__ __forceinline__ void put_state(T* hi, T* lo, int pitch, const floatx4
 // ends with S_out (dS_in).  In the forward direction record s then holds the
 // state entering segment s; in the reverse direction the gradient leaving it.
 // ---------------------------------------------------------------------------
+// The segment sum of segment s of head (b, h), in LDS the caller provides:
+// two chunk buffers for X and for Y (pitches DK + PAD and DV + PAD) and two
+// decay tables.
 template <typename T, int DK, int DV, bool REVERSE>
-__global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
-    Act<const T> X, Act<const T> Y, DecayArg dec, float* __restrict__ store, int64_t store_nseg,
-    int H, int N, int m)
+__device__ __forceinline__ void seg_sum_body(Act<const T> X, Act<const T> Y, DecayArg dec,
+                                             float* __restrict__ store, int64_t store_nseg, int H,
+                                             int N, int m, int s, int h, int b, T* xs0, T* xs1,
+                                             T* ys0, T* ys1, float* tb0, float* tb1)
 {
     constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
     constexpr int XP = DK + PAD, YP = DV + PAD;
     constexpr int64_t REC = seg_record_floats(DK, DV);
-    // two buffers: chunk it + 1 is staged while chunk it may still be read,
-    // so one barrier per chunk suffices
-    __shared__ __align__(16) T Xs[2][CHUNK * XP];
-    __shared__ __align__(16) T Ys[2][CHUNK * YP];
-    __shared__ __align__(16) float tab[2][TAB_SIZE];
 
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id();
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
@@ -172,9 +180,9 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     for (int it = 0; it < cnt; ++it) {
         // buffer it % 2 was last read in chunk it - 2, before every wave
         // passed the previous chunk's barrier
-        T* xs = Xs[it & 1];
-        T* ys = Ys[it & 1];
-        float* tb = tab[it & 1];
+        T* xs = (it & 1) ? xs1 : xs0;
+        T* ys = (it & 1) ? ys1 : ys0;
+        float* tb = (it & 1) ? tb1 : tb0;
         chunk_store(rx, xs, XP);
         chunk_store(ry, ys, YP);
         if (w == 0)
@@ -197,6 +205,22 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     store_state<DK, DV, 1>(rec, U, cbase);
     if (threadIdx.x == 0)
         rec[DK * DV] = seg_log;
+}
+
+template <typename T, int DK, int DV, bool REVERSE>
+__global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
+    Act<const T> X, Act<const T> Y, DecayArg dec, float* __restrict__ store, int64_t store_nseg,
+    int H, int N, int m)
+{
+    constexpr int PAD = Pad<T>::value;
+    constexpr int XP = DK + PAD, YP = DV + PAD;
+    // two buffers: chunk it + 1 is staged while chunk it may still be read,
+    // so one barrier per chunk suffices
+    __shared__ __align__(16) T Xs[2][CHUNK * XP];
+    __shared__ __align__(16) T Ys[2][CHUNK * YP];
+    __shared__ __align__(16) float tab[2][TAB_SIZE];
+    seg_sum_body<T, DK, DV, REVERSE>(X, Y, dec, store, store_nseg, H, N, m, blockIdx.x, blockIdx.y,
+                                     blockIdx.z, Xs[0], Xs[1], Ys[0], Ys[1], tab[0], tab[1]);
 }
 
 // Fold of four consecutive state elements [e, e + 4) of head bh across the
@@ -418,7 +442,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, Act<const T> dO, DecayArg dec,
     const float* __restrict__ bstates, int64_t bs_nseg, const float* __restrict__ gstates,
     int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, Act<float> da, float* __restrict__ da_tot,
-    int H, int N, int m, FoldArg fold)
+    int H, int N, int m, FoldArg fold, SumDev<T> sum)
 {
     constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
@@ -435,7 +459,23 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     __shared__ float qdq_s[DA ? NH * MAXM * CHUNK : 1];
     __shared__ float g_s[DA ? CHUNK : 1];
 
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, h = blockIdx.y;
+    const int nseg_here = (N + m - 1) / m;
+    // With carried segment sums the grid has twice the batch rows: the
+    // launch's own segments are z < B, the sums z >= B, so that every
+    // segment workgroup is dispatched before any sum workgroup and the sums
+    // fill CUs as segment workgroups finish.  The sums use this kernel's LDS.
+    const int B = sum.nseg ? (int)gridDim.z / 2 : (int)gridDim.z;
+    if ((int)blockIdx.z >= B) {
+        if (s < sum.nseg)
+            seg_sum_body<T, DK, DV, true>(sum.X, sum.Y, sum.dec, sum.store, sum.store_nseg, H, sum.N,
+                                          sum.m, s, h, blockIdx.z - B, Qs, Ks, Vs, dOs, tab,
+                                          reinterpret_cast<float*>(Ms[0]));
+        return;
+    }
+    if (s >= nseg_here)
+        return;
+    const int b = blockIdx.z;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * w;
@@ -461,7 +501,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
     // the previous piece's fold, while the first chunk's loads are in flight
     if (fold.store)
-        fold_share<DK, DV, true, NT>(fold, b, h, H, s, gridDim.x);
+        fold_share<DK, DV, true, NT>(fold, b, h, H, s, nseg_here);
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         chunk_store(rk, Ks, QP);
@@ -671,7 +711,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     }
     if constexpr (DA) {
         if (w == 0 && l == 0)
-            da_tot[bh * gridDim.x + s] = dcarry;
+            da_tot[bh * nseg_here + s] = dcarry;
     }
 }
 
@@ -801,22 +841,26 @@ hipError_t fwd_seg_impl(const FwdIntraLaunch& s, hipStream_t stream)
 template <typename T, typename OT, int DK, int DV>
 hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
 {
-    const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
-    if (s.m > 4)
+    if (s.m > 4 || s.sum.m > 4)
         return hipErrorInvalidValue;
+    const SumDev<T> sum{cact<T>(s.sum.x), cact<T>(s.sum.y), decay_arg(s.sum.decay, s.sum.decay_kind),
+                        (float*)s.sum.store, s.sum.store_nseg, s.sum.N, s.sum.m, s.sum.nseg};
+    const int nseg = (s.N + s.m - 1) / s.m;
+    const dim3 grid(s.sum.nseg ? max(nseg, s.sum.nseg) : nseg, s.H, s.sum.nseg ? 2 * s.B : s.B),
+        block(DV / 16 * 64);
     if (s.da.ptr)
         launch_kernel((bwd_seg_kernel<T, OT, DK, DV, true>), grid, block, stream,
                       cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
                       decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
                       (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                      mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold);
+                      mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold, sum);
     else
         launch_kernel((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, stream,
                       cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
                       decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
                       (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
                       mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
-                      s.m, s.fold);
+                      s.m, s.fold, sum);
     return hipGetLastError();
 }
 

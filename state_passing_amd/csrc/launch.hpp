@@ -80,6 +80,18 @@ struct FoldArg {
     int nseg;
 };
 
+// Segment sums carried by a backward segment-kernel launch (the sequence
+// backward): the reverse sums of another piece, whose q and dO views, decay
+// view and records are given here, run as nseg extra workgroups of the
+// launch, dispatched after the segment kernel's own.  nseg = 0: none.
+struct SumArg {
+    TensorArg x, y, decay;   // q, dO and decay of that piece
+    int decay_kind;
+    void* store;
+    int64_t store_nseg;
+    int N, m, nseg;
+};
+
 struct FwdIntraLaunch {
     int dtype, out_dtype, dk, dv, B, H, N, m;
     TensorArg q, k, v, decay, o;
@@ -102,6 +114,7 @@ struct BwdIntraLaunch {
     TensorArg da;
     float* da_tot;
     FoldArg fold;            // the previous piece's reverse fold, or none
+    SumArg sum;              // the segment sums of the piece before that, or none
 };
 
 // Finishes the decay gradient of one piece: adds the totals of later

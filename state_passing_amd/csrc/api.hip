@@ -789,7 +789,8 @@ size_t linrec_delta_workspace_bytes(const linrec_desc* d)
 {
     if (check_desc(d) != LINREC_OK || d->dk != d->dv)
         return 0;
-    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv) * sizeof(float);
+    // W_k, W_v, then P per chunk (64 x 64 per 64 tokens)
+    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv + kChunk) * sizeof(float);
 }
 
 size_t linrec_delta_saved_bytes(const linrec_desc* d)
@@ -805,7 +806,7 @@ size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
     if (check_desc(d) != LINREC_OK || d->dk != d->dv)
         return 0;
     const size_t bh = (size_t)d->B * d->H, N = (size_t)(d->T / kChunk);
-    return bh * ((size_t)d->T * (d->dk + 2 * d->dv) + N * kChunk * kChunk + N * d->dk * d->dv) *
+    return bh * ((size_t)d->T * (d->dk + 2 * d->dv + kChunk) + N * kChunk * kChunk + N * d->dk * d->dv) *
            sizeof(float);
 }
 
@@ -850,6 +851,7 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.S_out = S_out;
     s.wk = (float*)workspace;
     s.wv = (float*)workspace + (size_t)d->B * d->H * (size_t)d->T * d->dk;
+    s.pm = s.wv + (size_t)d->B * d->H * (size_t)d->T * d->dv;
     if (saved) {
         s.s0 = (float*)saved;
         s.u = (float*)saved + (size_t)d->B * d->H * (size_t)(d->T / kChunk) * d->dk * d->dv;
@@ -893,6 +895,7 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.tm = s.wv + bh * T * d->dv;
     s.duy = s.tm + bh * N * kChunk * kChunk;
     s.dsc = s.duy + bh * T * d->dv;
+    s.pm = s.dsc + bh * N * d->dk * d->dv;
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_bwd(s, (hipStream_t)stream); }));
     return LINREC_OK;

@@ -41,15 +41,17 @@ namespace linrec {
 // Workgroup = (chunk, h, b), 4 waves.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<const T> V,
+__global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<const T> K, Act<const T> V,
                                                          Act<const float> beta, DecayArg dec,
                                                          Act<float> Wk, Act<float> Wv,
+                                                         float* __restrict__ Pout,
                                                          float* __restrict__ Tout, int H)
 {
     constexpr int NT = 256, NW = 4;
     constexpr int PAD = Pad<T>::value;
     constexpr int KP = DK + PAD, VP = DV + PAD;
     constexpr int AP = CHUNK + 4;            // fp32 pitch of A and T
+    __shared__ __align__(16) T Qs[CHUNK * KP];
     __shared__ __align__(16) T Ks[CHUNK * KP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) float As[CHUNK * AP];
@@ -61,10 +63,12 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<con
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t tok0 = (int64_t)n * CHUNK;
     {
-        ChunkRegs<T, DK, NT> rk;
+        ChunkRegs<T, DK, NT> rq, rk;
         ChunkRegs<T, DV, NT> rv;
+        chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
         chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
         chunk_load(rv, V.head(b, h) + tok0 * V.st, V.st);
+        chunk_store(rq, Qs, KP);
         chunk_store(rk, Ks, KP);
         chunk_store(rv, Vs, VP);
     }
@@ -74,20 +78,28 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<con
     }
     __syncthreads();
 
-    // A: strictly lower part of beta_i exp(lam_i - lam_j) (k_i . k_j)
+    // A: strictly lower part of beta_i exp(lam_i - lam_j) (k_i . k_j); and
+    // P = (Q K^T) .* D (lower, diagonal included) for the serial kernels,
+    // [B][H][N][64][64] fp32
+    const bool fac = decay_factored(tab);
+    float* pdst = Pout + (((int64_t)b * H + h) * gridDim.x + n) * CHUNK * CHUNK;
     for (int tile = w; tile < 16; tile += NW) {
         const int ib = tile >> 2, jb = tile & 3;
-        floatx4 acc = zero4();
+        floatx4 acc = zero4(), pacc = zero4();
         if (jb <= ib) {
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
+            for (int ks = 0; ks < DK / 32; ++ks) {
                 acc = mma(frag_rows(Ks, KP, 16 * ib, 32 * ks), frag_rows(Ks, KP, 16 * jb, 32 * ks), acc);
+                pacc = mma(frag_rows(Qs, KP, 16 * ib, 32 * ks), frag_rows(Ks, KP, 16 * jb, 32 * ks), pacc);
+            }
+            pacc = decay_mask<true>(pacc, tab, 16 * ib, 16 * jb, fac);
         }
         const int j = 16 * jb + t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * ib + 4 * g + r;
             As[i * AP + j] = j < i ? bet[i] * __expf(tab[TAB_LAM + i] - tab[TAB_LAM + j]) * acc[r] : 0.f;
+            pdst[i * CHUNK + j] = pacc[r];
         }
     }
     __syncthreads();
@@ -153,6 +165,7 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> K, Act<con
 template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
                                                          Act<const float> Wk, Act<const float> Wv,
+                                                         const float* __restrict__ Pm,
                                                          DecayArg dec, const float* S_in,
                                                          float* S_out, Act<OT> O,
                                                          float* __restrict__ s0_out,
@@ -189,24 +202,47 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     const T* kh = K.head(b, h);
     const float* wkh = Wk.head(b, h);
     const float* wvh = Wv.head(b, h);
-    for (int n = 0; n < N; ++n) {
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        {
-            ChunkRegs<T, DK, NT> rq, rk;
-            chunk_load(rq, qh + tok0 * Q.st, Q.st);
-            chunk_load(rk, kh + tok0 * K.st, K.st);
-            chunk_store(rq, Qs, QP);
-            chunk_store(rk, Ks, QP);
-        }
-        for (int idx = threadIdx.x; idx < CHUNK * DK / 4; idx += NT) {
-            const int row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            *reinterpret_cast<floatx4*>(Wks + row * WP + col) =
-                *reinterpret_cast<const floatx4*>(wkh + (tok0 + row) * Wk.st + col);
+    const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
+    // the next chunk's Q, K, W_k, this workgroup's W_v columns and P are
+    // loaded into registers while the current chunk computes
+    constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
+    static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK, "chunk split");
+    ChunkRegs<T, DK, NT> rq, rk;
+    floatx4 rwk[NWK], rpv[NPV], rwv;
+    auto load_next = [&](int64_t tk) {
+        chunk_load(rq, qh + tk * Q.st, Q.st);
+        chunk_load(rk, kh + tk * K.st, K.st);
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) {
+            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
+            rwk[i] = *reinterpret_cast<const floatx4*>(wkh + (tk + row) * Wk.st + col);
         }
         {
             const int row = threadIdx.x >> 2, col = 4 * (threadIdx.x & 3);
-            *reinterpret_cast<floatx4*>(Wvs + row * CP + col) =
-                *reinterpret_cast<const floatx4*>(wvh + (tok0 + row) * Wv.st + cbase + col);
+            rwv = *reinterpret_cast<const floatx4*>(wvh + (tk + row) * Wv.st + cbase + col);
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i)
+            rpv[i] = *reinterpret_cast<const floatx4*>(ph + tk * CHUNK + 4 * (threadIdx.x + NT * i));
+    };
+    load_next(0);
+    for (int n = 0; n < N; ++n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        chunk_store(rq, Qs, QP);
+        chunk_store(rk, Ks, QP);
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) {
+            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
+            *reinterpret_cast<floatx4*>(Wks + row * WP + col) = rwk[i];
+        }
+        {
+            const int row = threadIdx.x >> 2, col = 4 * (threadIdx.x & 3);
+            *reinterpret_cast<floatx4*>(Wvs + row * CP + col) = rwv;
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
+            *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
         }
         if (w == 0)
             decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
@@ -220,22 +256,9 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
                     s0_out[((bh * N + n) * DK + f) * DV + cbase + t] = S[q][r];
             }
         __syncthreads();
+        if (n + 1 < N)
+            load_next(tok0 + CHUNK);
 
-        // P = (Q K^T) .* D, causal, fp32
-        const bool fac = decay_factored(tab);
-        for (int tile = w; tile < 16; tile += NW) {
-            const int ib = tile >> 2, jb = tile & 3;
-            floatx4 acc = zero4();
-            if (jb <= ib) {
-#pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
-                acc = decay_mask<true>(acc, tab, 16 * ib, 16 * jb, fac);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Ps[(16 * ib + 4 * g + r) * PP + 16 * jb + t] = acc[r];
-        }
         // U rows [16 w, 16 w + 16) = W_v - W_k S_0
         {
             floatx4 acc = zero4();
@@ -314,6 +337,7 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
                                                           Act<const T> dO, Act<const float> Wk,
+                                                          const float* __restrict__ Pm,
                                                           DecayArg dec, const float* dS_out,
                                                           float* dS_in, float* __restrict__ dU_out,
                                                           float* __restrict__ dsc_out, int H, int N)
@@ -348,25 +372,50 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     const T* kh = K.head(b, h);
     const T* doh = dO.head(b, h);
     const float* wkh = Wk.head(b, h);
-    for (int n = N - 1; n >= 0; --n) {
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        {
-            ChunkRegs<T, DK, NT> rq, rk;
-            chunk_load(rq, qh + tok0 * Q.st, Q.st);
-            chunk_load(rk, kh + tok0 * K.st, K.st);
-            chunk_store(rq, Qs, QP);
-            chunk_store(rk, Ks, QP);
-        }
-        constexpr int VEC = 16 / sizeof(T), PER = 16 / VEC;   // 16-byte vectors per slice row
+    const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
+    // the next (earlier) chunk's Q, K, dO columns, W_k and P load into
+    // registers while the current chunk computes
+    constexpr int VEC = 16 / sizeof(T), PER = 16 / VEC;   // 16-byte vectors per dO slice row
+    constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
+    static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK && CHUNK * PER <= NT,
+                  "chunk split");
+    ChunkRegs<T, DK, NT> rq, rk;
+    floatx4 rwk[NWK], rpv[NPV];
+    u32x4 rdo = {0u, 0u, 0u, 0u};
+    auto load_next = [&](int64_t tk) {
+        chunk_load(rq, qh + tk * Q.st, Q.st);
+        chunk_load(rk, kh + tk * K.st, K.st);
         if (threadIdx.x < CHUNK * PER) {
             const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
-            *reinterpret_cast<u32x4*>(dOs + row * OP + col) =
-                *reinterpret_cast<const u32x4*>(doh + (tok0 + row) * dO.st + cbase + col);
+            rdo = *reinterpret_cast<const u32x4*>(doh + (tk + row) * dO.st + cbase + col);
         }
-        for (int idx = threadIdx.x; idx < CHUNK * DK / 4; idx += NT) {
-            const int row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            *reinterpret_cast<floatx4*>(Wks + row * WP + col) =
-                *reinterpret_cast<const floatx4*>(wkh + (tok0 + row) * Wk.st + col);
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) {
+            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
+            rwk[i] = *reinterpret_cast<const floatx4*>(wkh + (tk + row) * Wk.st + col);
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i)
+            rpv[i] = *reinterpret_cast<const floatx4*>(ph + tk * CHUNK + 4 * (threadIdx.x + NT * i));
+    };
+    load_next((int64_t)(N - 1) * CHUNK);
+    for (int n = N - 1; n >= 0; --n) {
+        const int64_t tok0 = (int64_t)n * CHUNK;
+        chunk_store(rq, Qs, QP);
+        chunk_store(rk, Ks, QP);
+        if (threadIdx.x < CHUNK * PER) {
+            const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
+            *reinterpret_cast<u32x4*>(dOs + row * OP + col) = rdo;
+        }
+#pragma unroll
+        for (int i = 0; i < NWK; ++i) {
+            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
+            *reinterpret_cast<floatx4*>(Wks + row * WP + col) = rwk[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
+            *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
         }
         if (w == 0)
             decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
@@ -379,22 +428,8 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                 dsc_out[((bh * N + n) * DK + f) * DV + cbase + t] = G[q][r];
             }
         __syncthreads();
-
-        const bool fac = decay_factored(tab);
-        for (int tile = w; tile < 16; tile += NW) {
-            const int ib = tile >> 2, jb = tile & 3;
-            floatx4 acc = zero4();
-            if (jb <= ib) {
-#pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mma(frag_rows(Qs, QP, 16 * ib, 32 * ks), frag_rows(Ks, QP, 16 * jb, 32 * ks), acc);
-                acc = decay_mask<true>(acc, tab, 16 * ib, 16 * jb, fac);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Ps[(16 * ib + 4 * g + r) * PP + 16 * jb + t] = acc[r];
-        }
-        __syncthreads();
+        if (n > 0)
+            load_next(tok0 - CHUNK);
 
         // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
         {
@@ -714,13 +749,14 @@ hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
     const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
     const int N = s.T / CHUNK;
     launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, nullptr, s.H);
+                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                  nullptr, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     launch_kernel((delta_scan_kernel<T, OT, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256),
                   stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
-                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, dec, s.S_in, s.S_out,
+                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, dec, s.S_in, s.S_out,
                   Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N);
     return hipGetLastError();
 }
@@ -733,13 +769,15 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
     const Act<float> wk{s.wk, (int64_t)s.H * s.T * DK, (int64_t)s.T * DK, DK};
     const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
     launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.tm, s.H);
+                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                  s.tm, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     launch_kernel((delta_bscan_kernel<T, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
                   dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
-                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, dec, s.dS_out, s.dS_in, s.duy,
+                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, dec, s.dS_out,
+                  s.dS_in, s.duy,
                   s.dsc, s.H, N);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;

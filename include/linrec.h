@@ -59,9 +59,11 @@
  *   S_*, dS_*, decay, the per-chunk state store and the workspace are fp32.
  *
  * ---------------------------------------------------------------- shapes
- *   chunk == 64; T % 64 == 0 and T >= 64; d_k, d_v in {64, 128};
- *   B >= 1, H >= 1.  Activation pointers and their strides sb, sh, st must
- *   keep every token row 16-byte aligned.
+ *   chunk == 64; T >= 1 (the last chunk of a piece may be partial: its
+ *   missing tokens are neither read nor written; the delta-rule calls need
+ *   T % 64 == 0); d_k, d_v in {64, 128}; B >= 1, H >= 1.  Activation
+ *   pointers and their strides sb, sh, st must keep every token row 16-byte
+ *   aligned.
  *
  * ---------------------------------------------------------------- semantics
  *   Ownership: the caller owns all device memory; the library keeps no
@@ -263,7 +265,7 @@ linrec_status linrec_bwd_da(linrec_ctx* ctx, const linrec_desc* d,
                             float* da_carry_out, void* workspace, void* stream);
 
 /* Sequence accumulation over `npieces` consecutive pieces of the sequence
- * described by `d` (d->T = total tokens; lengths[i] % 64 == 0, sum = T;
+ * described by `d` (d->T = total tokens; lengths[i] >= 1, sum = T;
  * lengths is host memory).  Piece i is processed as its own sub-sequence,
  * in order, with S carried from piece to piece; the state-transition
  * kernels run on the context's auxiliary stream so that piece i+1's state

@@ -56,7 +56,8 @@ constexpr int kChunk = 64;
 // segment in registers; only the state at each segment boundary is stored.
 constexpr int kSegChunks = 4;
 
-int64_t nseg_of(int64_t tokens) { return (tokens / kChunk + kSegChunks - 1) / kSegChunks; }
+int64_t chunks_of(int64_t tokens) { return (tokens + kChunk - 1) / kChunk; }
+int64_t nseg_of(int64_t tokens) { return (chunks_of(tokens) + kSegChunks - 1) / kSegChunks; }
 
 linrec_status hip_fail(hipError_t e, linrec_status code)
 {
@@ -74,8 +75,7 @@ linrec_status check_desc(const linrec_desc* d)
         return LINREC_E_NULL;
     if (d->dtype != LINREC_BF16 && d->dtype != LINREC_F32)
         return LINREC_E_DTYPE;
-    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 65535 || d->H > 65535 ||
-        d->T < kChunk || d->T % kChunk != 0)
+    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 65535 || d->H > 65535 || d->T < 1)
         return LINREC_E_SHAPE;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
         return LINREC_E_SHAPE;
@@ -150,7 +150,7 @@ linrec_status check_pieces(const linrec_desc* d, int32_t npieces, const int32_t*
         return LINREC_E_NULL;
     int64_t sum = 0;
     for (int32_t i = 0; i < npieces; ++i) {
-        if (lengths[i] < kChunk || lengths[i] % kChunk)
+        if (lengths[i] < 1)
             return LINREC_E_SHAPE;
         sum += lengths[i];
     }
@@ -250,7 +250,7 @@ ScanLaunch fwd_scan_of(const linrec_desc* d, const linrec_tensor& k, const linre
 {
     const int esz = elem_size(d->dtype);
     ScanLaunch s{};
-    s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = (len + kChunk - 1) / kChunk; s.tail = len - (s.N - 1) * kChunk;
     s.m = kSegChunks;
     s.reverse = false;
     s.x = advance(k, tok0, esz);
@@ -272,7 +272,7 @@ FwdIntraLaunch fwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     FwdIntraLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype;
-    s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = (len + kChunk - 1) / kChunk; s.tail = len - (s.N - 1) * kChunk;
     s.m = kSegChunks;
     s.q = advance(q, tok0, esz);
     s.k = advance(k, tok0, esz);
@@ -291,7 +291,7 @@ ScanLaunch bwd_scan_of(const linrec_desc* d, const linrec_tensor& q, const linre
 {
     const int esz = elem_size(d->dtype);
     ScanLaunch s{};
-    s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.dtype = d->dtype; s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = (len + kChunk - 1) / kChunk; s.tail = len - (s.N - 1) * kChunk;
     s.m = kSegChunks;
     s.reverse = true;
     s.x = advance(q, tok0, esz);
@@ -315,7 +315,7 @@ BwdIntraLaunch bwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     BwdIntraLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype;
-    s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = len / kChunk;
+    s.dk = d->dk; s.dv = d->dv; s.B = d->B; s.H = d->H; s.N = (len + kChunk - 1) / kChunk; s.tail = len - (s.N - 1) * kChunk;
     s.m = kSegChunks;
     s.q = advance(q, tok0, esz);
     s.k = advance(k, tok0, esz);
@@ -331,6 +331,23 @@ BwdIntraLaunch bwd_intra_of(const linrec_desc* d, const linrec_tensor& q, const 
     s.ghat = ghat;
     s.g_nseg = nseg_of(len);
     return s;
+}
+
+// The segment sums of a scan, as extra work of a segment-kernel launch.
+linrec::SumArg sum_arg_of(const ScanLaunch& sc)
+{
+    linrec::SumArg a{};
+    a.x = sc.x;
+    a.y = sc.y;
+    a.decay = sc.decay;
+    a.decay_kind = sc.decay_kind;
+    a.store = sc.store;
+    a.store_nseg = sc.store_nseg;
+    a.N = sc.N;
+    a.m = sc.m;
+    a.tail = sc.tail;
+    a.nseg = (sc.N + sc.m - 1) / sc.m;
+    return a;
 }
 
 hipError_t pool_event(linrec_ctx* ctx, hipEvent_t* ev)
@@ -651,7 +668,8 @@ linrec_status linrec_bwd_da(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor
     in.da = targ(da);
     in.da_tot = tot;
     DaFinishLaunch fin{};
-    fin.B = d->B; fin.H = d->H; fin.N = d->T / kChunk; fin.m = kSegChunks;
+    fin.B = d->B; fin.H = d->H; fin.N = (int)chunks_of(d->T); fin.m = kSegChunks;
+    fin.tail = d->T - (fin.N - 1) * kChunk;
     fin.da = targ(da);
     fin.decay = targ(decay);
     fin.decay_kind = d->decay;
@@ -777,8 +795,7 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
         }
         if (i > 1) {
             const ScanLaunch sums = scan_of(i - 2, dS_in);
-            in.sum = linrec::SumArg{sums.x, sums.y, sums.decay, sums.decay_kind, sums.store,
-                                    sums.store_nseg, sums.N, sums.m, (int)nseg_of(lengths[i - 2])};
+            in.sum = sum_arg_of(sums);
         }
         LAUNCH_BWD_INTRA(ctx, in, s);
     }
@@ -787,7 +804,7 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
 
 size_t linrec_delta_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
         return 0;
     // W_k, W_v, then P per chunk (64 x 64 per 64 tokens)
     return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv + kChunk) * sizeof(float);
@@ -795,7 +812,7 @@ size_t linrec_delta_workspace_bytes(const linrec_desc* d)
 
 size_t linrec_delta_saved_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
         return 0;
     const size_t bh = (size_t)d->B * d->H;
     return bh * ((size_t)(d->T / kChunk) * d->dk * d->dv + (size_t)d->T * d->dv) * sizeof(float);
@@ -803,7 +820,7 @@ size_t linrec_delta_saved_bytes(const linrec_desc* d)
 
 size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
         return 0;
     const size_t bh = (size_t)d->B * d->H, N = (size_t)(d->T / kChunk);
     return bh * ((size_t)d->T * (d->dk + 2 * d->dv + kChunk) + N * kChunk * kChunk + N * d->dk * d->dv) *
@@ -833,7 +850,7 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
     if (st != LINREC_OK)
         return st;
-    if (d->dk != d->dv)
+    if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
         return LINREC_E_SHAPE;
     if ((st = check_beta(beta)) != LINREC_OK)
         return st;
@@ -872,7 +889,7 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
                                       workspace);
     if (st != LINREC_OK)
         return st;
-    if (d->dk != d->dv)
+    if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
         return LINREC_E_SHAPE;
     if ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK)
         return st;

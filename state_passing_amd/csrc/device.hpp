@@ -191,12 +191,14 @@ __device__ __forceinline__ u32x4& chunk_vec(R& r)
 }
 
 template <int P, typename T, int D, int NT>
-__device__ __forceinline__ void chunk_load_one(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld)
+__device__ __forceinline__ void chunk_load_one(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld, int rows)
 {
     typedef ChunkRegs<T, D, NT> R;
     if constexpr (P < R::NV) {
         const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
-        chunk_vec<P>(r) = *reinterpret_cast<const u32x4*>(src + row * ld + col);
+        // no branch: a row past the end reads the last row that exists;
+        // chunk_store() writes zeros in its place
+        chunk_vec<P>(r) = *reinterpret_cast<const u32x4*>(src + min(row, rows - 1) * ld + col);
     }
 }
 
@@ -210,22 +212,48 @@ __device__ __forceinline__ void chunk_store_one(ChunkRegs<T, D, NT>& r, T* lds, 
     }
 }
 
-template <typename T, int D, int NT>
-__device__ __forceinline__ void chunk_load(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld)
+// Zeros over the rows >= rows of what chunk_store_one<P> wrote, by the same
+// thread (so it lands after that thread's own store).
+template <int P, typename T, int D, int NT>
+__device__ __forceinline__ void chunk_zero_one(T* lds, int pitch, int rows)
 {
-    chunk_load_one<0>(r, src, ld);
-    chunk_load_one<1>(r, src, ld);
-    chunk_load_one<2>(r, src, ld);
-    chunk_load_one<3>(r, src, ld);
+    typedef ChunkRegs<T, D, NT> R;
+    if constexpr (P < R::NV) {
+        const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
+        if (row >= rows)
+            *reinterpret_cast<u32x4*>(lds + row * pitch + col) = u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
+// rows: the chunk's tokens that exist (1..64; the last chunk of a piece may
+// be partial); nothing past them is read (chunk_store() with the same rows
+// writes zeros for them).
 template <typename T, int D, int NT>
-__device__ __forceinline__ void chunk_store(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+__device__ __forceinline__ void chunk_load(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld,
+                                           int rows = CHUNK)
+{
+    chunk_load_one<0>(r, src, ld, rows);
+    chunk_load_one<1>(r, src, ld, rows);
+    chunk_load_one<2>(r, src, ld, rows);
+    chunk_load_one<3>(r, src, ld, rows);
+}
+
+// rows: as given to the chunk_load() that filled r; rows past them are
+// written as zeros (only a piece's last chunk can be partial, and whole
+// chunks take no extra instruction but one uniform branch).
+template <typename T, int D, int NT>
+__device__ __forceinline__ void chunk_store(ChunkRegs<T, D, NT>& r, T* lds, int pitch, int rows = CHUNK)
 {
     chunk_store_one<0>(r, lds, pitch);
     chunk_store_one<1>(r, lds, pitch);
     chunk_store_one<2>(r, lds, pitch);
     chunk_store_one<3>(r, lds, pitch);
+    if (rows < CHUNK) {
+        chunk_zero_one<0, T, D, NT>(lds, pitch, rows);
+        chunk_zero_one<1, T, D, NT>(lds, pitch, rows);
+        chunk_zero_one<2, T, D, NT>(lds, pitch, rows);
+        chunk_zero_one<3, T, D, NT>(lds, pitch, rows);
+    }
 }
 
 // chunk_store() into a tile whose rows hold the k index permuted so that
@@ -254,38 +282,70 @@ __device__ __forceinline__ void chunk_store_perm_one(ChunkRegs<T, D, NT>& r, T* 
     }
 }
 
+// Zeros at the permuted positions chunk_store_perm_one<P> wrote, for rows >=
+// rows, by the same thread.
+template <int P, typename T, int D, int NT>
+__device__ __forceinline__ void chunk_zero_perm_one(T* lds, int pitch, int rows)
+{
+    typedef ChunkRegs<T, D, NT> R;
+    if constexpr (P < R::NV) {
+        const int idx = threadIdx.x + NT * P, row = idx / R::PER_ROW, col = (idx % R::PER_ROW) * R::VEC;
+        if (row >= rows) {
+            T* base = lds + row * pitch;
+            if constexpr (sizeof(T) == 2) {
+                const int u = col / 4;
+                *reinterpret_cast<u32x2*>(base + 4 * perm_unit(u)) = u32x2{0u, 0u};
+                *reinterpret_cast<u32x2*>(base + 4 * perm_unit(u + 1)) = u32x2{0u, 0u};
+            } else {
+                *reinterpret_cast<u32x4*>(base + 4 * perm_unit(col / 4)) = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+}
+
 template <typename T, int D, int NT>
-__device__ __forceinline__ void chunk_store_perm(ChunkRegs<T, D, NT>& r, T* lds, int pitch)
+__device__ __forceinline__ void chunk_store_perm(ChunkRegs<T, D, NT>& r, T* lds, int pitch,
+                                                 int rows = CHUNK)
 {
     chunk_store_perm_one<0>(r, lds, pitch);
     chunk_store_perm_one<1>(r, lds, pitch);
     chunk_store_perm_one<2>(r, lds, pitch);
     chunk_store_perm_one<3>(r, lds, pitch);
+    if (rows < CHUNK) {
+        chunk_zero_perm_one<0, T, D, NT>(lds, pitch, rows);
+        chunk_zero_perm_one<1, T, D, NT>(lds, pitch, rows);
+        chunk_zero_perm_one<2, T, D, NT>(lds, pitch, rows);
+        chunk_zero_perm_one<3, T, D, NT>(lds, pitch, rows);
+    }
 }
 
 // ---- decay ----------------------------------------------------------------
 
 // The raw decay this lane needs for the chunk starting at tok0 (token = lane
 // for per-token decay), so that it can be loaded a chunk ahead.
-__device__ __forceinline__ float decay_raw(const DecayArg& d, int b, int h, int64_t tok0)
+// rows: the chunk's tokens that exist; a lane past them reads the last
+// one (no branch) and decay_tables() with the same rows gives it decay 1.
+__device__ __forceinline__ float decay_raw(const DecayArg& d, int b, int h, int64_t tok0,
+                                          int rows = CHUNK)
 {
     if (d.kind == 0)
         return 1.f;
     if (d.kind == 1)
         return d.ptr[h * d.sh];
-    return d.ptr[b * d.sb + h * d.sh + (tok0 + lane_id()) * d.st];
+    return d.ptr[b * d.sb + h * d.sh + (tok0 + min(lane_id(), rows - 1)) * d.st];
 }
 
 // Inclusive cumulative log of the chunk's decays from decay_raw() values
 // (token = lane); called by a full wave.
-__device__ __forceinline__ float decay_log_cumsum(const DecayArg& d, float raw)
+__device__ __forceinline__ float decay_log_cumsum(const DecayArg& d, float raw, int rows = CHUNK)
 {
     const int lane = lane_id();
     if (d.kind == 0)
         return 0.f;
+    // tokens past `rows` decay by 1
     if (d.kind == 1)
-        return (float)(lane + 1) * logf(raw);
-    float x = logf(raw);
+        return (float)(min(lane, rows - 1) + 1) * logf(raw);
+    float x = lane < rows ? logf(raw) : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -307,10 +367,10 @@ enum { TAB_LAM = 0, TAB_G = CHUNK, TAB_F = 2 * CHUNK, TAB_E = 3 * CHUNK, TAB_SIZ
 constexpr float FACTOR_MIN_LOG = -40.f;
 
 // Fill the tables from decay_raw() values (token = lane); one full wave.
-__device__ __forceinline__ void decay_tables(const DecayArg& d, float raw, float* tab)
+__device__ __forceinline__ void decay_tables(const DecayArg& d, float raw, float* tab, int rows = CHUNK)
 {
     const int l = lane_id();
-    const float lam = decay_log_cumsum(d, raw);
+    const float lam = decay_log_cumsum(d, raw, rows);
     const float lamC = __shfl(lam, CHUNK - 1, 64);
     tab[TAB_LAM + l] = lam;
     tab[TAB_G + l] = __expf(lam);
@@ -587,21 +647,32 @@ __device__ __forceinline__ floatx4 load4(const float* p) { return *reinterpret_c
 // the output) to row-major global memory as OT: one 8-byte (bf16) or 16-byte
 // (fp32) store per lane.
 template <typename OT>
-__device__ __forceinline__ void store_tile_t(OT* base, int64_t ld, int rbase, int cbase, floatx4 acc);
+__device__ __forceinline__ void store_tile_t(OT* base, int64_t ld, int rbase, int cbase, floatx4 acc,
+                                             int rows = CHUNK);
 
 template <>
-__device__ __forceinline__ void store_tile_t<bf16>(bf16* base, int64_t ld, int rbase, int cbase, floatx4 acc)
+__device__ __forceinline__ void store_tile_t<bf16>(bf16* base, int64_t ld, int rbase, int cbase, floatx4 acc,
+                                                   int rows)
 {
     const int l = lane_id(), t = l & 15, g = l >> 4;
     const bf16x4 v = {(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
-    *reinterpret_cast<bf16x4*>(base + (rbase + t) * ld + cbase + 4 * g) = v;
+    bf16x4* p = reinterpret_cast<bf16x4*>(base + (rbase + t) * ld + cbase + 4 * g);
+    if (rows >= CHUNK)           // wave-uniform: whole chunks store without lane masks
+        *p = v;
+    else if (rbase + t < rows)
+        *p = v;
 }
 
 template <>
-__device__ __forceinline__ void store_tile_t<float>(float* base, int64_t ld, int rbase, int cbase, floatx4 acc)
+__device__ __forceinline__ void store_tile_t<float>(float* base, int64_t ld, int rbase, int cbase, floatx4 acc,
+                                                    int rows)
 {
     const int l = lane_id(), t = l & 15, g = l >> 4;
-    *reinterpret_cast<floatx4*>(base + (rbase + t) * ld + cbase + 4 * g) = acc;
+    floatx4* p = reinterpret_cast<floatx4*>(base + (rbase + t) * ld + cbase + 4 * g);
+    if (rows >= CHUNK)
+        *p = acc;
+    else if (rbase + t < rows)
+        *p = acc;
 }
 
 }  // namespace linrec

@@ -36,6 +36,8 @@
 // carried states) enters the MFMA as a bf16 hi + lo pair against an exact
 // bf16 activation; decay factors that depend only on an output row scale the
 // fp32 product instead of an operand.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -48,7 +50,7 @@ struct SumDev {
     DecayArg dec;
     float* store;
     int64_t store_nseg;
-    int N, m, nseg;
+    int N, m, nseg, tail;
 };
 
 // ---------------------------------------------------------------------------
@@ -146,12 +148,13 @@ __device__ __forceinline__ void put_state(T* hi, T* lo, int pitch, const floatx4
 // ---------------------------------------------------------------------------
 // The segment sum of segment s of head (b, h), in LDS the caller provides:
 // two chunk buffers for X and for Y (pitches DK + PAD and DV + PAD) and two
-// decay tables.
-template <typename T, int DK, int DV, bool REVERSE>
+// decay tables.  RAGGED: the piece's last chunk may be partial (`tail`
+// tokens); otherwise every chunk is whole and the masking compiles away.
+template <typename T, int DK, int DV, bool REVERSE, bool RAGGED>
 __device__ __forceinline__ void seg_sum_body(Act<const T> X, Act<const T> Y, DecayArg dec,
                                              float* __restrict__ store, int64_t store_nseg, int H,
-                                             int N, int m, int s, int h, int b, T* xs0, T* xs1,
-                                             T* ys0, T* ys1, float* tb0, float* tb1)
+                                             int N, int tail, int m, int s, int h, int b, T* xs0,
+                                             T* xs1, T* ys0, T* ys1, float* tb0, float* tb1)
 {
     constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
@@ -173,27 +176,31 @@ __device__ __forceinline__ void seg_sum_body(Act<const T> X, Act<const T> Y, Dec
 
     ChunkRegs<T, DK, NT> rx;
     ChunkRegs<T, DV, NT> ry;
+    // the piece's last chunk may be partial: `tail` tokens
+    auto rows_of = [&](int c) { return RAGGED && c == N - 1 ? tail : CHUNK; };
     int n = REVERSE ? n1 - 1 : n0;
-    chunk_load(rx, xh + (int64_t)n * CHUNK * X.st, X.st);
-    chunk_load(ry, yh + (int64_t)n * CHUNK * Y.st, Y.st);
-    float ra = decay_raw(dec, b, h, (int64_t)n * CHUNK);
+    int rw = rows_of(n);
+    chunk_load(rx, xh + (int64_t)n * CHUNK * X.st, X.st, rw);
+    chunk_load(ry, yh + (int64_t)n * CHUNK * Y.st, Y.st, rw);
+    float ra = decay_raw(dec, b, h, (int64_t)n * CHUNK, rw);
     for (int it = 0; it < cnt; ++it) {
         // buffer it % 2 was last read in chunk it - 2, before every wave
         // passed the previous chunk's barrier
         T* xs = (it & 1) ? xs1 : xs0;
         T* ys = (it & 1) ? ys1 : ys0;
         float* tb = (it & 1) ? tb1 : tb0;
-        chunk_store(rx, xs, XP);
-        chunk_store(ry, ys, YP);
+        chunk_store(rx, xs, XP, rw);
+        chunk_store(ry, ys, YP, rw);
         if (w == 0)
-            decay_tables(dec, ra, tb);
+            decay_tables(dec, ra, tb, rw);
         __syncthreads();
         if (it + 1 < cnt) {
             n = REVERSE ? n1 - 2 - it : n0 + 1 + it;
+            rw = rows_of(n);
             const int64_t tn = (int64_t)n * CHUNK;
-            chunk_load(rx, xh + tn * X.st, X.st);
-            chunk_load(ry, yh + tn * Y.st, Y.st);
-            ra = decay_raw(dec, b, h, tn);
+            chunk_load(rx, xh + tn * X.st, X.st, rw);
+            chunk_load(ry, yh + tn * Y.st, Y.st, rw);
+            ra = decay_raw(dec, b, h, tn, rw);
         }
         seg_log += tb[TAB_LAM + CHUNK - 1];
         float yf[2][8];
@@ -207,10 +214,10 @@ __device__ __forceinline__ void seg_sum_body(Act<const T> X, Act<const T> Y, Dec
         rec[DK * DV] = seg_log;
 }
 
-template <typename T, int DK, int DV, bool REVERSE>
+template <typename T, int DK, int DV, bool REVERSE, bool RAGGED>
 __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     Act<const T> X, Act<const T> Y, DecayArg dec, float* __restrict__ store, int64_t store_nseg,
-    int H, int N, int m)
+    int H, int N, int tail, int m)
 {
     constexpr int PAD = Pad<T>::value;
     constexpr int XP = DK + PAD, YP = DV + PAD;
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void seg_sum_kernel(
     __shared__ __align__(16) T Xs[2][CHUNK * XP];
     __shared__ __align__(16) T Ys[2][CHUNK * YP];
     __shared__ __align__(16) float tab[2][TAB_SIZE];
-    seg_sum_body<T, DK, DV, REVERSE>(X, Y, dec, store, store_nseg, H, N, m, blockIdx.x, blockIdx.y,
+    seg_sum_body<T, DK, DV, REVERSE, RAGGED>(X, Y, dec, store, store_nseg, H, N, tail, m, blockIdx.x, blockIdx.y,
                                      blockIdx.z, Xs[0], Xs[1], Ys[0], Ys[1], tab[0], tab[1]);
 }
 
@@ -303,10 +310,10 @@ __device__ __forceinline__ void fold_share(const FoldArg& f, int b, int h, int H
 // The state serves as the B operand straight from registers (k-slot order
 // of the result tiles).  The next chunk's rows load while this one computes.
 // ---------------------------------------------------------------------------
-template <typename T, typename OT, int DK, int DV>
+template <typename T, typename OT, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, DecayArg dec,
-    const float* __restrict__ bstates, int64_t bs_nseg, Act<OT> O, int H, int N, int m)
+    const float* __restrict__ bstates, int64_t bs_nseg, Act<OT> O, int H, int N, int tail, int m)
 {
     constexpr int NW = DV / 16, NT = NW * 64;
     constexpr int PAD = Pad<T>::value;
@@ -331,15 +338,17 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
     const T* qh = Q.head(b, h);
     const T* kh = K.head(b, h);
     const T* vh = V.head(b, h);
+    // the piece's last chunk may be partial: `tail` tokens
+    auto rows_of = [&](int c) { return RAGGED && c == N - 1 ? tail : CHUNK; };
     ChunkRegs<T, DK, NT> rq, rk;
     ChunkRegs<T, DV, NT> rv;
-    chunk_load(rq, qh + (int64_t)n0 * CHUNK * Q.st, Q.st);
-    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
-    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
+    chunk_load(rq, qh + (int64_t)n0 * CHUNK * Q.st, Q.st, rows_of(n0));
+    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st, rows_of(n0));
+    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st, rows_of(n0));
     // the state load is in flight together with the first chunk's
     floatx4 S[DK / 16][1];
     load_state<DK, DV, 1>(S, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
-    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
+    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK, rows_of(n0));
 
     // P tiles of this wave: row block ib, column blocks jb0, jb0 + jstep, ...
     // (the second four waves take row blocks in reverse order, so the two
@@ -349,19 +358,21 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store_perm(rq, Qs, QP);
-        chunk_store_perm(rk, Kp, QP);
-        chunk_store(rk, Ks, QP);
-        chunk_store(rv, Vs, VP);
+        const int rows_n = rows_of(n);
+        chunk_store_perm(rq, Qs, QP, rows_n);
+        chunk_store_perm(rk, Kp, QP, rows_n);
+        chunk_store(rk, Ks, QP, rows_n);
+        chunk_store(rv, Vs, VP, rows_n);
         if (w == 0)
-            decay_tables(dec, ra, tab);
+            decay_tables(dec, ra, tab, rows_n);
         __syncthreads();
         if (n + 1 < n1) {
             const int64_t tn = (int64_t)(n + 1) * CHUNK;
-            chunk_load(rq, qh + tn * Q.st, Q.st);
-            chunk_load(rk, kh + tn * K.st, K.st);
-            chunk_load(rv, vh + tn * V.st, V.st);
-            ra = decay_raw(dec, b, h, tn);
+            const int rw = rows_of(n + 1);
+            chunk_load(rq, qh + tn * Q.st, Q.st, rw);
+            chunk_load(rk, kh + tn * K.st, K.st, rw);
+            chunk_load(rv, vh + tn * V.st, V.st, rw);
+            ra = decay_raw(dec, b, h, tn, rw);
         }
         const bool fac = decay_factored(tab);
 
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
             for (int js = 0; js <= ib / 2; ++js)
                 acc = mma(frag_cols(Vs, VP, cbase, 32 * js),
                           frag_rows_split(Ps[0], Ps[1], PP, 16 * ib, 32 * js), acc);
-            store_tile_t<OT>(oh, O.st, 16 * ib, cbase, acc);
+            store_tile_t<OT>(oh, O.st, 16 * ib, cbase, acc, rows_n);
         }
 
         // S_n = gamma_C S_{n-1} + K^T (V .* gamma_C/gamma); the state after
@@ -437,12 +448,12 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 // load while this one computes; walk 2 starts on walk 1's last chunk, whose
 // K, V, dO and decay tables are still in LDS, so only Q is loaded for it.
 // ---------------------------------------------------------------------------
-template <typename T, typename OT, int DK, int DV, bool DA>
+template <typename T, typename OT, int DK, int DV, bool DA, bool RAGGED>
 __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     Act<const T> Q, Act<const T> K, Act<const T> V, Act<const T> dO, DecayArg dec,
     const float* __restrict__ bstates, int64_t bs_nseg, const float* __restrict__ gstates,
     int64_t gs_nseg, Act<OT> dQ, Act<OT> dK, Act<OT> dV, Act<float> da, float* __restrict__ da_tot,
-    int H, int N, int m, FoldArg fold, SumDev<T> sum)
+    int H, int N, int tail, int m, FoldArg fold, SumDev<T> sum)
 {
     constexpr int NW = DV / 16, NT = NW * 64, NH = NW / 4;
     constexpr int PAD = Pad<T>::value;
@@ -468,8 +479,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     const int B = sum.nseg ? (int)gridDim.z / 2 : (int)gridDim.z;
     if ((int)blockIdx.z >= B) {
         if (s < sum.nseg)
-            seg_sum_body<T, DK, DV, true>(sum.X, sum.Y, sum.dec, sum.store, sum.store_nseg, H, sum.N,
-                                          sum.m, s, h, blockIdx.z - B, Qs, Ks, Vs, dOs, tab,
+            seg_sum_body<T, DK, DV, true, RAGGED>(sum.X, sum.Y, sum.dec, sum.store, sum.store_nseg, H, sum.N,
+                                          sum.tail, sum.m, s, h, blockIdx.z - B, Qs, Ks, Vs, dOs, tab,
                                           reinterpret_cast<float*>(Ms[0]));
         return;
     }
@@ -493,32 +504,37 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     ChunkRegs<T, DK, NT> rq, rk;
     ChunkRegs<T, DV, NT> rv, rdo;
 
+    // the piece's last chunk may be partial: `tail` tokens
+    auto rows_of = [&](int c) { return RAGGED && c == N - 1 ? tail : CHUNK; };
+
     // ---------------- walk 1: dQ
-    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st);
-    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st);
-    chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st);
+    chunk_load(rk, kh + (int64_t)n0 * CHUNK * K.st, K.st, rows_of(n0));
+    chunk_load(rv, vh + (int64_t)n0 * CHUNK * V.st, V.st, rows_of(n0));
+    chunk_load(rdo, doh + (int64_t)n0 * CHUNK * dO.st, dO.st, rows_of(n0));
     load_state<DK, DV, 1>(C, bstates + (bh * bs_nseg + s) * seg_record_floats(DK, DV), cbase);
-    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK);
+    float ra = decay_raw(dec, b, h, (int64_t)n0 * CHUNK, rows_of(n0));
     // the previous piece's fold, while the first chunk's loads are in flight
     if (fold.store)
         fold_share<DK, DV, true, NT>(fold, b, h, H, s, nseg_here);
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rk, Ks, QP);
-        chunk_store(rv, Vs, VP);
-        chunk_store(rdo, dOs, VP);
+        const int rows_n = rows_of(n);
+        chunk_store(rk, Ks, QP, rows_n);
+        chunk_store(rv, Vs, VP, rows_n);
+        chunk_store(rdo, dOs, VP, rows_n);
         if (w == 0)
-            decay_tables(dec, ra, tab);
+            decay_tables(dec, ra, tab, rows_n);
         put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
         __syncthreads();
         if (n + 1 < n1) {
             const int64_t tn = (int64_t)(n + 1) * CHUNK;
-            chunk_load(rk, kh + tn * K.st, K.st);
-            chunk_load(rv, vh + tn * V.st, V.st);
-            chunk_load(rdo, doh + tn * dO.st, dO.st);
-            ra = decay_raw(dec, b, h, tn);
+            const int rw = rows_of(n + 1);
+            chunk_load(rk, kh + tn * K.st, K.st, rw);
+            chunk_load(rv, vh + tn * V.st, V.st, rw);
+            chunk_load(rdo, doh + tn * dO.st, dO.st, rw);
+            ra = decay_raw(dec, b, h, tn, rw);
         } else {
-            chunk_load(rq, qh + tok0 * Q.st, Q.st);
+            chunk_load(rq, qh + tok0 * Q.st, Q.st, rows_n);
         }
         const bool fac = decay_factored(tab);
 
@@ -545,7 +561,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
         if constexpr (DA) {
 #pragma unroll
             for (int fbi = 0; fbi < FBW; ++fbi)
-                qv[fbi] = load4(qh + (tok0 + 16 * rb + t) * Q.st + 16 * (fb0 + fbi) + 4 * g);
+                qv[fbi] = 16 * rb + t < rows_n ? load4(qh + (tok0 + 16 * rb + t) * Q.st + 16 * (fb0 + fbi) + 4 * g)
+                                               : zero4();
         }
         float qdq = 0.f;
 #pragma unroll
@@ -563,7 +580,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             if constexpr (DA)
                 qdq += acc[0] * qv[fbi][0] + acc[1] * qv[fbi][1] + acc[2] * qv[fbi][2] +
                        acc[3] * qv[fbi][3];
-            store_tile_t<OT>(out, dQ.st, 16 * rb, 16 * fb, acc);
+            store_tile_t<OT>(out, dQ.st, 16 * rb, 16 * fb, acc, rows_n);
         }
         if constexpr (DA) {
             // sum over the four lane groups: this half's share of q.dq per token
@@ -586,23 +603,25 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     float dcarry = 0.f;   // decay gradient: sum of g over the segment's later chunks (wave 0)
     for (int n = n1 - 1; n >= n0; --n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rq, Qs, QP);
+        const int rows_n = rows_of(n);
+        chunk_store(rq, Qs, QP, rows_n);
         if (n < n1 - 1) {
-            chunk_store(rk, Ks, QP);
-            chunk_store(rv, Vs, VP);
-            chunk_store(rdo, dOs, VP);
+            chunk_store(rk, Ks, QP, rows_n);
+            chunk_store(rv, Vs, VP, rows_n);
+            chunk_store(rdo, dOs, VP, rows_n);
             if (w == 0)
-                decay_tables(dec, ra, tab);
+                decay_tables(dec, ra, tab, rows_n);
         }
         put_state<T, DK, 1>(Ms[0], Ms[1], QP, C, cbase);
         __syncthreads();
         if (n > n0) {
             const int64_t tn = (int64_t)(n - 1) * CHUNK;
-            chunk_load(rq, qh + tn * Q.st, Q.st);
-            chunk_load(rk, kh + tn * K.st, K.st);
-            chunk_load(rv, vh + tn * V.st, V.st);
-            chunk_load(rdo, doh + tn * dO.st, dO.st);
-            ra = decay_raw(dec, b, h, tn);
+            const int rw = rows_of(n - 1);
+            chunk_load(rq, qh + tn * Q.st, Q.st, rw);
+            chunk_load(rk, kh + tn * K.st, K.st, rw);
+            chunk_load(rv, vh + tn * V.st, V.st, rw);
+            chunk_load(rdo, doh + tn * dO.st, dO.st, rw);
+            ra = decay_raw(dec, b, h, tn, rw);
         }
         const bool fac = decay_factored(tab);
         // dV^T and dK^T tiles: lane (g,t) holds token 16rb + t
@@ -634,7 +653,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
                 if (rb < 2)
                     acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 0), p0, acc);
                 acc = mma(frag_cols_perm(dOs, VP, 16 * cb, 32), p1, acc);
-                store_tile_t<OT>(outv, dV.st, 16 * rb, 16 * cb, acc);
+                store_tile_t<OT>(outv, dV.st, 16 * rb, 16 * cb, acc, rows_n);
             }
         }
         if (NH == 1 || half == 1) {
@@ -668,7 +687,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
                     const floatx4 kk = load4(Ks + (16 * rb + t) * QP + 16 * fb + 4 * g);
                     kdk += acc[0] * kk[0] + acc[1] * kk[1] + acc[2] * kk[2] + acc[3] * kk[3];
                 }
-                store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc);
+                store_tile_t<OT>(outk, dK.st, 16 * rb, 16 * fb, acc, rows_n);
             }
             if constexpr (DA) {
                 // g = q.dq - k.dk for the tokens of row block rb
@@ -704,7 +723,8 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
                     if (l + off < 64)
                         x += y;
                 }
-                da.ptr[b * da.sb + h * da.sh + (tok0 + l) * da.st] = x + dcarry;
+                if (l < rows_n)
+                    da.ptr[b * da.sb + h * da.sh + (tok0 + l) * da.st] = x + dcarry;
                 dcarry += __shfl(x, 0, 64);
             }
         }
@@ -799,19 +819,31 @@ DecayArg decay_arg(const TensorArg& d, int kind)
     return DecayArg{(const float*)d.ptr, d.sb, d.sh, d.st, kind};
 }
 
+// Calls f with std::integral_constant<bool, ragged>: the kernels with the
+// masking of a partial last chunk are instantiated apart, so pieces of whole
+// chunks run code without it.
+template <typename F>
+hipError_t with_ragged(bool ragged, F&& f)
+{
+    return ragged ? f(std::integral_constant<bool, true>{}) : f(std::integral_constant<bool, false>{});
+}
+
 template <typename T, typename OT, int DK, int DV>
 hipError_t sum_impl(const ScanLaunch& s, hipStream_t stream)
 {
     const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
-    if (s.reverse)
-        launch_kernel((seg_sum_kernel<T, DK, DV, true>), grid, block, stream, cact<T>(s.x),
-                      cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
-                      s.store_nseg, s.H, s.N, s.m);
-    else
-        launch_kernel((seg_sum_kernel<T, DK, DV, false>), grid, block, stream, cact<T>(s.x),
-                      cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
-                      s.store_nseg, s.H, s.N, s.m);
-    return hipGetLastError();
+    return with_ragged(s.tail < CHUNK, [&](auto rg) {
+        constexpr bool RG = decltype(rg)::value;
+        if (s.reverse)
+            launch_kernel((seg_sum_kernel<T, DK, DV, true, RG>), grid, block, stream, cact<T>(s.x),
+                          cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                          s.store_nseg, s.H, s.N, s.tail, s.m);
+        else
+            launch_kernel((seg_sum_kernel<T, DK, DV, false, RG>), grid, block, stream, cact<T>(s.x),
+                          cact<T>(s.y), decay_arg(s.decay, s.decay_kind), (float*)s.store,
+                          s.store_nseg, s.H, s.N, s.tail, s.m);
+        return hipGetLastError();
+    });
 }
 
 template <typename T, typename OT, int DK, int DV>
@@ -832,10 +864,12 @@ template <typename T, typename OT, int DK, int DV>
 hipError_t fwd_seg_impl(const FwdIntraLaunch& s, hipStream_t stream)
 {
     const dim3 grid((s.N + s.m - 1) / s.m, s.H, s.B), block(DV / 16 * 64);
-    launch_kernel((fwd_seg_kernel<T, OT, DK, DV>), grid, block, stream,
-                  cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), decay_arg(s.decay, s.decay_kind),
-                  (const float*)s.states, s.st_nseg, mact<OT>(s.o), s.H, s.N, s.m);
-    return hipGetLastError();
+    return with_ragged(s.tail < CHUNK, [&](auto rg) {
+        launch_kernel((fwd_seg_kernel<T, OT, DK, DV, decltype(rg)::value>), grid, block, stream,
+                      cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), decay_arg(s.decay, s.decay_kind),
+                      (const float*)s.states, s.st_nseg, mact<OT>(s.o), s.H, s.N, s.tail, s.m);
+        return hipGetLastError();
+    });
 }
 
 template <typename T, typename OT, int DK, int DV>
@@ -844,24 +878,29 @@ hipError_t bwd_seg_impl(const BwdIntraLaunch& s, hipStream_t stream)
     if (s.m > 4 || s.sum.m > 4)
         return hipErrorInvalidValue;
     const SumDev<T> sum{cact<T>(s.sum.x), cact<T>(s.sum.y), decay_arg(s.sum.decay, s.sum.decay_kind),
-                        (float*)s.sum.store, s.sum.store_nseg, s.sum.N, s.sum.m, s.sum.nseg};
+                        (float*)s.sum.store, s.sum.store_nseg, s.sum.N, s.sum.m, s.sum.nseg, s.sum.tail};
     const int nseg = (s.N + s.m - 1) / s.m;
     const dim3 grid(s.sum.nseg ? max(nseg, s.sum.nseg) : nseg, s.H, s.sum.nseg ? 2 * s.B : s.B),
         block(DV / 16 * 64);
-    if (s.da.ptr)
-        launch_kernel((bwd_seg_kernel<T, OT, DK, DV, true>), grid, block, stream,
-                      cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                      decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
-                      (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                      mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.m, s.fold, sum);
-    else
-        launch_kernel((bwd_seg_kernel<T, OT, DK, DV, false>), grid, block, stream,
-                      cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
-                      decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
-                      (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
-                      mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
-                      s.m, s.fold, sum);
-    return hipGetLastError();
+    const bool ragged = s.tail < CHUNK || (s.sum.nseg && s.sum.tail < CHUNK);
+    return with_ragged(ragged, [&](auto rg) {
+        constexpr bool RG = decltype(rg)::value;
+        if (s.da.ptr)
+            launch_kernel((bwd_seg_kernel<T, OT, DK, DV, true, RG>), grid, block, stream,
+                          cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                          decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                          (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                          mact<OT>(s.dv_), mact<float>(s.da), s.da_tot, s.H, s.N, s.tail, s.m, s.fold,
+                          sum);
+        else
+            launch_kernel((bwd_seg_kernel<T, OT, DK, DV, false, RG>), grid, block, stream,
+                          cact<T>(s.q), cact<T>(s.k), cact<T>(s.v), cact<T>(s.dO),
+                          decay_arg(s.decay, s.decay_kind), (const float*)s.states, s.st_nseg,
+                          (const float*)s.ghat, s.g_nseg, mact<OT>(s.dq), mact<OT>(s.dk_),
+                          mact<OT>(s.dv_), Act<float>{nullptr, 0, 0, 0}, nullptr, s.H, s.N,
+                          s.tail, s.m, s.fold, sum);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace
@@ -918,7 +957,7 @@ hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream)
     const int seg_len = s.m * CHUNK, nseg = (s.N + s.m - 1) / s.m;
     launch_kernel(da_finish_kernel, dim3(s.H, s.B), dim3(1024), stream, mact<float>(s.da),
                   decay_arg(s.decay, s.decay_kind), s.tot, s.carry_in, s.carry_out, s.H,
-                  s.N * CHUNK, seg_len, nseg);
+                  (s.N - 1) * CHUNK + s.tail, seg_len, nseg);
     return hipGetLastError();
 }
 

@@ -48,7 +48,8 @@ struct TensorArg {
 };
 
 // A piece has N chunks of 64 tokens, grouped into segments of m chunks (the
-// last one may be shorter).  Per-segment records (seg_record_floats) live in
+// last one may be shorter); its last chunk holds `tail` tokens (1..64), the
+// tokens past them do not exist and are neither read nor written.  Per-segment records (seg_record_floats) live in
 // a store laid out [B][H][nseg][record]; pointers are already offset to the
 // piece's first segment and *_nseg is the store's segments per (b, h).
 
@@ -56,7 +57,7 @@ struct TensorArg {
 // store = state entering every segment.  Reverse: x = Q, y = dO, carry
 // dS_out -> dS_in, store = gradient leaving every segment.
 struct ScanLaunch {
-    int dtype, dk, dv, B, H, N, m;
+    int dtype, dk, dv, B, H, N, m, tail;
     int out_dtype;           // unused by the scan; keeps one dispatch macro
     bool reverse;
     TensorArg x, y, decay;
@@ -89,11 +90,11 @@ struct SumArg {
     int decay_kind;
     void* store;
     int64_t store_nseg;
-    int N, m, nseg;
+    int N, m, nseg, tail;
 };
 
 struct FwdIntraLaunch {
-    int dtype, out_dtype, dk, dv, B, H, N, m;
+    int dtype, out_dtype, dk, dv, B, H, N, m, tail;
     TensorArg q, k, v, decay, o;
     int decay_kind;
     const void* states;
@@ -104,7 +105,7 @@ struct FwdIntraLaunch {
 // the reverse cumulative sum within its segment of q.dq - k.dk into da and
 // each segment's total into da_tot ([B][H][nseg of the piece]).
 struct BwdIntraLaunch {
-    int dtype, out_dtype, dk, dv, B, H, N, m;
+    int dtype, out_dtype, dk, dv, B, H, N, m, tail;
     TensorArg q, k, v, dO, decay, dq, dk_, dv_;
     int decay_kind;
     const void* states;
@@ -121,7 +122,7 @@ struct BwdIntraLaunch {
 // segments and the carry from later pieces, divides by the decay, and
 // writes the carry for the previous piece.
 struct DaFinishLaunch {
-    int B, H, N, m;
+    int B, H, N, m, tail;
     TensorArg da, decay;
     int decay_kind;
     const float* tot;

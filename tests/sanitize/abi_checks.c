@@ -163,9 +163,12 @@ int main(void)
         e.out_dtype = 9;
         EXPECT(linrec_fwd(NULL, &e, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) != LINREC_OK,
                "unknown out dtype");
-        const int32_t ragged[2] = {100, 220};   /* not multiples of 64 before the last */
+        const int32_t ragged[2] = {100, 220};   /* ragged pieces are valid */
         EXPECT(linrec_fwd_seq(NULL, &d, 2, ragged, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) ==
-                   LINREC_E_SHAPE, "ragged inner piece");
+                   LINREC_E_NULL, "ragged pieces");
+        const int32_t empty[2] = {0, 320};
+        EXPECT(linrec_fwd_seq(NULL, &d, 2, empty, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) ==
+                   LINREC_E_SHAPE, "empty piece");
         const int32_t short_sum[2] = {64, 64};
         EXPECT(linrec_fwd_seq(NULL, &d, 2, short_sum, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) ==
                    LINREC_E_SHAPE, "pieces do not sum to T");

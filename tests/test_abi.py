@@ -62,12 +62,17 @@ def test_sizes():
     # sequence store: the sum of the pieces' stores
     assert linrec.seq_states_bytes(d(T=8192), [2048, 4096, 2048]) == linrec.states_bytes(d(T=8192))
     assert linrec.seq_states_bytes(d(T=384), [64, 320]) == 16 * 3 * rec
-    assert linrec.seq_states_bytes(d(T=384), [64, 300]) == 0
+    assert linrec.seq_states_bytes(d(T=384), [64, 300]) == 0            # sums to 364
+    # ragged lengths: a partial last chunk counts as a chunk
+    assert linrec.seq_states_bytes(d(T=364), [64, 300]) == 16 * (1 + 2) * rec
+    assert linrec.states_bytes(d(T=100)) == 16 * 1 * rec
+    assert linrec.states_bytes(d(T=1)) == 16 * 1 * rec
+    assert linrec.states_bytes(d(T=257)) == 16 * 2 * rec
     # three slots of one piece's records, sized for the longest piece
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \
         3 * linrec.states_bytes(d(T=4096))
     assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == 3 * linrec.states_bytes(d())
-    for bad in (d(T=100), d(T=0), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
+    for bad in (d(T=0), d(T=-64), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
         assert linrec.states_bytes(bad) == 0
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [4096, 4000]) == 0
 
@@ -110,8 +115,9 @@ E = {v: k for k, v in linrec.STATUS.items()}
 
 
 @pytest.mark.parametrize("desc,code", [
-    (d(T=100), "LINREC_E_SHAPE"),
+    (d(T=-64), "LINREC_E_SHAPE"),
     (d(T=0), "LINREC_E_SHAPE"),
+    (d(T=100), "LINREC_E_NULL"),           # a ragged length is valid; no context
     (d(dk=96), "LINREC_E_SHAPE"),
     (d(B=0), "LINREC_E_SHAPE"),
     (d(H=0), "LINREC_E_SHAPE"),
@@ -161,7 +167,8 @@ def test_decay_gradient_arguments():
     rec = (128 * 128 + 64) * 4
     # the gradient records plus one fp32 total per segment (padded to 256 bytes)
     assert linrec.bwd_da_workspace_bytes(good) == 16 * 16 * rec + 1024
-    assert linrec.bwd_da_workspace_bytes(d(T=100)) == 0
+    assert linrec.bwd_da_workspace_bytes(d(T=0)) == 0
+    assert linrec.bwd_da_workspace_bytes(d(T=100, decay=linrec.DECAY_TOKEN)) > 0
     assert call_bwd_da(good) == E["LINREC_E_NULL"]            # all checks pass, no context
     assert call_bwd_da(d(decay=linrec.DECAY_HEAD)) == E["LINREC_E_NULL"]
     assert call_bwd_da(d(decay=linrec.DECAY_NONE)) == E["LINREC_E_LAYOUT"]
@@ -180,8 +187,9 @@ def test_recompute_arguments():
     assert linrec.bwd_recompute_workspace_bytes(good) == 2 * 16 * 16 * rec + 16 * 128 * 128 * 4
     assert linrec.bwd_recompute_workspace_bytes(d(T=8192)) == \
         2 * linrec.states_bytes(d(T=8192)) + 16 * 128 * 128 * 4
-    assert linrec.bwd_recompute_workspace_bytes(d(T=100)) == 0
-    assert call_bwd_recompute(d(T=100)) == E["LINREC_E_SHAPE"]
+    assert linrec.bwd_recompute_workspace_bytes(d(T=0)) == 0
+    assert call_bwd_recompute(d(T=0)) == E["LINREC_E_SHAPE"]
+    assert call_bwd_recompute(d(T=100)) == E["LINREC_E_NULL"]
     assert call_bwd_recompute(good, workspace=None) == E["LINREC_E_WORKSPACE"]
     assert call_bwd_recompute(good, workspace=FAKE + 8) == E["LINREC_E_WORKSPACE"]
     assert call_bwd_recompute(good, S_in=FAKE + 2) == E["LINREC_E_ALIGN"]
@@ -197,10 +205,11 @@ def test_bad_piece_lists():
                                 linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE, None)
         # the piece list is checked before the context
         assert rc == E["LINREC_E_SHAPE"], lengths
-    arr = (ctypes.c_int32 * 2)(4096, 4096)
-    assert lib.linrec_fwd_seq(None, ctypes.byref(desc), 2, arr, act(), act(), act(),
-                              linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE,
-                              None) == E["LINREC_E_NULL"]
+    for lengths in ([4096, 4096], [4000, 4192], [1, 8191]):   # ragged pieces are valid
+        arr = (ctypes.c_int32 * 2)(*lengths)
+        assert lib.linrec_fwd_seq(None, ctypes.byref(desc), 2, arr, act(), act(), act(),
+                                  linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE,
+                                  None) == E["LINREC_E_NULL"], lengths
     assert lib.linrec_fwd_seq(None, ctypes.byref(desc), 0, arr, act(), act(), act(),
                               linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE, FAKE,
                               None) == E["LINREC_E_SHAPE"]
@@ -228,7 +237,8 @@ def test_noalloc_arguments():
     assert call(d(T=7936)) == E["LINREC_E_NULL"]           # 31 segments: fits 32 MiB
     assert linrec.bwd_workspace_bytes(d(T=7936)) <= linrec.NOALLOC_SCRATCH_BYTES
     assert call(d(T=8192)) == E["LINREC_E_SCRATCH"]        # 32 segments: does not
-    assert call(d(T=100)) == E["LINREC_E_SHAPE"]
+    assert call(d(T=0)) == E["LINREC_E_SHAPE"]
+    assert call(d(T=100)) == E["LINREC_E_NULL"]
     assert call(d(), states=None) == E["LINREC_E_WORKSPACE"]
     assert call(d(), dS_in=None) == E["LINREC_E_NULL"]
 

@@ -77,12 +77,12 @@ KERNEL_DESIGN_BYTES = {
     "bwd_seg": 768 + 256 + 576 + 768 + 512 + 512 * 63 / 64 + 768 * 62 / 64,
 }
 KERNEL_SYMBOL = {
-    "fwd_sum": "seg_sum_kernel<bf16,128,128,false>",
+    "fwd_sum": "seg_sum_kernel<bf16,128,128,false,false>",
     "fwd_fold": "seg_fold_kernel<128,128,false>",
-    "fwd_seg": "fwd_seg_kernel<bf16,bf16,128,128>",
-    "bwd_sum": "seg_sum_kernel<bf16,128,128,true>",
+    "fwd_seg": "fwd_seg_kernel<bf16,bf16,128,128,false>",
+    "bwd_sum": "seg_sum_kernel<bf16,128,128,true,false>",
     "bwd_fold": "seg_fold_kernel<128,128,true>",
-    "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128,false>",
+    "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128,false,false>",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_seg_sa256k_traffic.txt")
 SQ_FILE = os.path.join(ROOT, "profiles", "linrec_kernels_sa256k_sq_counters.txt")

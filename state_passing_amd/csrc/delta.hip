@@ -51,11 +51,16 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
     constexpr int PAD = Pad<T>::value;
     constexpr int KP = DK + PAD, VP = DV + PAD;
     constexpr int AP = CHUNK + 4;            // fp32 pitch of A and T
-    __shared__ __align__(16) T Qs[CHUNK * KP];
+    // Q is read only before T is formed: the two share one buffer, which
+    // keeps the workgroup under half the CU's LDS (two per CU)
+    constexpr int QT_BYTES = CHUNK * KP * (int)sizeof(T) > CHUNK * AP * 4 ? CHUNK * KP * (int)sizeof(T)
+                                                                          : CHUNK * AP * 4;
+    __shared__ __align__(16) unsigned char qt_buf[QT_BYTES];
+    T* const Qs = reinterpret_cast<T*>(qt_buf);
+    float* const Ts = reinterpret_cast<float*>(qt_buf);
     __shared__ __align__(16) T Ks[CHUNK * KP];
     __shared__ __align__(16) T Vs[CHUNK * VP];
     __shared__ __align__(16) float As[CHUNK * AP];
-    __shared__ __align__(16) float Ts[CHUNK * AP];
     __shared__ __align__(16) float tab[TAB_SIZE];
     __shared__ float bet[CHUNK];
 
@@ -181,8 +186,11 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     __shared__ __align__(16) float Wks[CHUNK * WP];
     __shared__ __align__(16) float Wvs[CHUNK * CP];
     __shared__ __align__(16) float Ps[CHUNK * PP];
-    __shared__ __align__(16) float Ss[DK * CP];
-    __shared__ __align__(16) float Us[CHUNK * CP];
+    // the state and U as bf16 hi/lo planes, transposed ([column][f] and
+    // [column][token]), so that every product reads them with 16-byte reads
+    constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
+    __shared__ __align__(16) T Ssp[2][16 * SPP];
+    __shared__ __align__(16) T Usp[2][16 * UPP];
     __shared__ __align__(16) float tab[TAB_SIZE];
 
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -247,14 +255,15 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
         if (w == 0)
             decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
 #pragma unroll
-        for (int q = 0; q < FPW; ++q)
+        for (int q = 0; q < FPW; ++q) {
+            put_split4(Ssp[0], Ssp[1], t * SPP + 16 * (FPW * w + q), S[q]);
+            if (s0_out)   // the state entering chunk n, for the backward
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int f = 16 * (FPW * w + q) + 4 * g + r;
-                Ss[f * CP + t] = S[q][r];
-                if (s0_out)   // the state entering chunk n, for the backward
+                for (int r = 0; r < 4; ++r) {
+                    const int f = 16 * (FPW * w + q) + 4 * g + r;
                     s0_out[((bh * N + n) * DK + f) * DV + cbase + t] = S[q][r];
-            }
+                }
+        }
         __syncthreads();
         if (n + 1 < N)
             load_next(tok0 + CHUNK);
@@ -264,16 +273,17 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             floatx4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(split_rows_f32<T>(Wks, WP, 16 * w, 32 * ks), split_cols_f32<T>(Ss, CP, 0, 32 * ks),
-                          acc);
+                acc = mma(split_rows_f32<T>(Wks, WP, 16 * w, 32 * ks),
+                          frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), acc);
+            floatx4 u4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r;
-                const float u = Wvs[i * CP + t] - acc[r];
-                Us[i * CP + t] = u;
+                u4[r] = Wvs[i * CP + t] - acc[r];
                 if (u_out)    // U for the backward, [B][H][T][DV]
-                    u_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u;
+                    u_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
             }
+            put_split4(Usp[0], Usp[1], t * UPP + 16 * w, u4);
         }
         __syncthreads();
 
@@ -282,11 +292,13 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             floatx4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(split_cols_f32<T>(Ss, CP, 0, 32 * ks), frag_rows(Qs, QP, 16 * w, 32 * ks), acc);
+                acc = mma(frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), frag_rows(Qs, QP, 16 * w, 32 * ks),
+                          acc);
             acc *= tab[TAB_G + 16 * w + t];
 #pragma unroll
             for (int js = 0; js <= w / 2; ++js)
-                acc = mma(split_cols_f32<T>(Us, CP, 0, 32 * js), split_rows_f32<T>(Ps, PP, 16 * w, 32 * js), acc);
+                acc = mma(frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * js), split_rows_f32<T>(Ps, PP, 16 * w, 32 * js),
+                          acc);
             store_tile_t<OT>(O.head(b, h) + tok0 * O.st, O.st, 16 * w, cbase, acc);
         }
         // S <- gamma_C S + K~^T U for this wave's row blocks
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 #pragma unroll
                 for (int ks = 0; ks < CHUNK / 32; ++ks)
                     S[q] = mma(split_scaled<T>(frag_cols(Ks, QP, 16 * fb, 32 * ks), kf[ks]),
-                               split_cols_f32<T>(Us, CP, 0, 32 * ks), S[q]);
+                               frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * ks), S[q]);
             }
         }
         __syncthreads();
@@ -345,14 +357,16 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, OP = 16 + PAD;
-    constexpr int WP = DK + 4, CP = 16 + 4, PP = CHUNK + 4;
+    constexpr int WP = DK + 4, PP = CHUNK + 4;
     __shared__ __align__(16) T Qs[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T dOs[CHUNK * OP];
     __shared__ __align__(16) float Wks[CHUNK * WP];
     __shared__ __align__(16) float Ps[CHUNK * PP];
-    __shared__ __align__(16) float Gs[DK * CP];
-    __shared__ __align__(16) float dUs[CHUNK * CP];
+    // the carried gradient and dU as bf16 hi/lo planes, transposed
+    constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
+    __shared__ __align__(16) T Gsp[2][16 * SPP];
+    __shared__ __align__(16) T dUsp[2][16 * UPP];
     __shared__ __align__(16) float tab[TAB_SIZE];
 
     const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -420,13 +434,14 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
         if (w == 0)
             decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
 #pragma unroll
-        for (int q = 0; q < FPW; ++q)
+        for (int q = 0; q < FPW; ++q) {
+            put_split4(Gsp[0], Gsp[1], t * SPP + 16 * (FPW * w + q), G[q]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int f = 16 * (FPW * w + q) + 4 * g + r;
-                Gs[f * CP + t] = G[q][r];
                 dsc_out[((bh * N + n) * DK + f) * DV + cbase + t] = G[q][r];
             }
+        }
         __syncthreads();
         if (n > 0)
             load_next(tok0 - CHUNK);
@@ -439,14 +454,16 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                 acc = mma(split_cols_f32<T>(Ps, PP, 16 * w, 32 * js), frag_cols(dOs, OP, 0, 32 * js), acc);
 #pragma unroll
             for (int ks = 0; ks < DK / 32; ++ks)
-                acc2 = mma(frag_rows(Ks, QP, 16 * w, 32 * ks), split_cols_f32<T>(Gs, CP, 0, 32 * ks), acc2);
+                acc2 = mma(frag_rows(Ks, QP, 16 * w, 32 * ks), frag_rows_split(Gsp[0], Gsp[1], SPP, 0, 32 * ks),
+                           acc2);
+            floatx4 u4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r;
-                const float u = acc[r] + tab[TAB_F + i] * acc2[r];
-                dUs[i * CP + t] = u;
-                dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u;
+                u4[r] = acc[r] + tab[TAB_F + i] * acc2[r];
+                dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
             }
+            put_split4(dUsp[0], dUsp[1], t * UPP + 16 * w, u4);
         }
         __syncthreads();
 
@@ -463,7 +480,7 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                 for (int ks = 0; ks < CHUNK / 32; ++ks) {
                     acc = mma(split_scaled<T>(frag_cols(Qs, QP, 16 * fb, 32 * ks), qf[ks]),
                               frag_cols(dOs, OP, 0, 32 * ks), acc);
-                    acc2 = mma(split_cols_f32<T>(Wks, WP, 16 * fb, 32 * ks), split_cols_f32<T>(dUs, CP, 0, 32 * ks),
+                    acc2 = mma(split_cols_f32<T>(Wks, WP, 16 * fb, 32 * ks), frag_rows_split(dUsp[0], dUsp[1], UPP, 0, 32 * ks),
                                acc2);
                 }
                 G[q] = gC * G[q] + acc - acc2;

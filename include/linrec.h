@@ -59,11 +59,18 @@
  *   S_*, dS_*, decay, the per-chunk state store and the workspace are fp32.
  *
  * ---------------------------------------------------------------- shapes
- *   chunk == 64; T >= 1 (the last chunk of a piece may be partial: its
+ *   chunk == 64; T >= 0 (the last chunk of a piece may be partial: its
  *   missing tokens are neither read nor written; the delta-rule calls need
  *   T % 64 == 0); d_k, d_v in {64, 128}; B >= 1, H >= 1.  Activation
  *   pointers and their strides sb, sh, st must keep every token row 16-byte
  *   aligned.
+ *   T == 0 (per-piece calls only; every piece of a sequence call has at
+ *   least one token): the piece is empty and the recurrence is the
+ *   identity on its carry, so the call copies S_in to S_out (dS_out to
+ *   dS_in, da_carry_in to da_carry_out; zeros for a NULL input) on `stream`
+ *   and nothing else.  Activations, decay, beta, states, saved and the
+ *   workspace are then not read, written or checked and may be NULL; the
+ *   size functions return 0 for them.
  *
  * ---------------------------------------------------------------- semantics
  *   Ownership: the caller owns all device memory; the library keeps no

@@ -75,7 +75,7 @@ linrec_status check_desc(const linrec_desc* d)
         return LINREC_E_NULL;
     if (d->dtype != LINREC_BF16 && d->dtype != LINREC_F32)
         return LINREC_E_DTYPE;
-    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 65535 || d->H > 65535 || d->T < 1)
+    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 65535 || d->H > 65535 || d->T < 0)
         return LINREC_E_SHAPE;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
         return LINREC_E_SHAPE;
@@ -204,6 +204,8 @@ linrec_status check_fwd_args(const linrec_desc* d, const linrec_tensor& q,
     linrec_status s;
     if ((s = check_desc(d)) != LINREC_OK)
         return s;
+    if (d->T == 0)   // nothing is read or written but the carried state
+        return (s = check_state_ptr(S_in, false)) != LINREC_OK ? s : check_state_ptr(S_out, true);
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     if ((s = check_act(q, d->dk, esz)) != LINREC_OK || (s = check_act(k, d->dk, esz)) != LINREC_OK ||
         (s = check_act(v, d->dv, esz)) != LINREC_OK || (s = check_act(o, d->dv, osz)) != LINREC_OK)
@@ -226,6 +228,8 @@ linrec_status check_bwd_args(const linrec_desc* d, const linrec_tensor& q,
     linrec_status s;
     if ((s = check_desc(d)) != LINREC_OK)
         return s;
+    if (d->T == 0)   // nothing is read or written but the carried gradient
+        return (s = check_state_ptr(dS_out, false)) != LINREC_OK ? s : check_state_ptr(dS_in, true);
     const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
     if ((s = check_act(q, d->dk, esz)) != LINREC_OK || (s = check_act(k, d->dk, esz)) != LINREC_OK ||
         (s = check_act(v, d->dv, esz)) != LINREC_OK || (s = check_act(dO, d->dv, esz)) != LINREC_OK ||
@@ -240,6 +244,17 @@ linrec_status check_bwd_args(const linrec_desc* d, const linrec_tensor& q,
     if ((s = check_buffer(states)) != LINREC_OK)
         return s;
     return check_buffer(workspace);
+}
+
+// A piece of zero tokens: the carry passes through unchanged (zeros for a
+// NULL input), one copy of B*H*n floats on `stream`.
+linrec_status pass_carry(const linrec_desc* d, const float* in, float* out, int64_t n,
+                         hipStream_t stream)
+{
+    if (in == out)
+        return LINREC_OK;
+    const hipError_t e = linrec::launch_carry_copy(in, out, (int64_t)d->B * d->H * n, stream);
+    return e == hipSuccess ? LINREC_OK : hip_fail(e, LINREC_E_LAUNCH);
 }
 
 // Launch descriptions of one piece [tok0, tok0 + len) of the sequence.
@@ -531,7 +546,7 @@ size_t linrec_bwd_workspace_bytes(const linrec_desc* d) { return linrec_states_b
 
 size_t linrec_bwd_recompute_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK)
+    if (check_desc(d) != LINREC_OK || d->T == 0)
         return 0;
     return 2 * linrec_states_bytes(d) + (size_t)d->B * d->H * d->dk * d->dv * sizeof(float);
 }
@@ -545,7 +560,7 @@ size_t da_tot_bytes(const linrec_desc* d)
 
 size_t linrec_bwd_da_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK)
+    if (check_desc(d) != LINREC_OK || d->T == 0)
         return 0;
     return linrec_states_bytes(d) + da_tot_bytes(d);
 }
@@ -580,6 +595,8 @@ linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     if (st != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    if (d->T == 0)
+        return pass_carry(d, S_in, S_out, (int64_t)d->dk * d->dv, s);
     const int64_t ns = nseg_of(d->T);
     const ScanLaunch sc = fwd_scan_of(d, k, v, decay, 0, d->T, S_in, S_out, states, 0, ns);
     const FwdIntraLaunch in = fwd_intra_of(d, q, k, v, decay, o, 0, d->T, states, 0, ns);
@@ -599,6 +616,8 @@ linrec_status linrec_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
     if (st != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    if (d->T == 0)
+        return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, s);
     const int64_t ns = nseg_of(d->T);
     const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
     const BwdIntraLaunch in =
@@ -624,6 +643,8 @@ linrec_status linrec_bwd_noalloc(linrec_ctx* ctx, const linrec_desc* d, linrec_t
         return LINREC_E_SCRATCH;
     if ((st = check_ctx(ctx)) != LINREC_OK)
         return st;
+    if (d->T == 0)
+        return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, (hipStream_t)stream);
     if (!ctx->scratch)
         return hip_fail(ctx->scratch_err != hipSuccess ? ctx->scratch_err : hipErrorInvalidSymbol,
                         LINREC_E_DEVICE);
@@ -650,16 +671,23 @@ linrec_status linrec_bwd_da(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor
         return st;
     if (d->decay == LINREC_DECAY_NONE)
         return LINREC_E_LAYOUT;
-    if (!da.ptr || !da_carry_out)
-        return LINREC_E_NULL;
-    if (!aligned(da.ptr, 4))
-        return LINREC_E_ALIGN;
-    if (da.sb < 0 || da.sh < 0 || da.st < 1)
-        return LINREC_E_LAYOUT;
+    if (d->T > 0) {
+        if (!da.ptr)
+            return LINREC_E_NULL;
+        if (!aligned(da.ptr, 4))
+            return LINREC_E_ALIGN;
+        if (da.sb < 0 || da.sh < 0 || da.st < 1)
+            return LINREC_E_LAYOUT;
+    }
     if ((st = check_state_ptr(da_carry_in, false)) != LINREC_OK ||
         (st = check_state_ptr(da_carry_out, true)) != LINREC_OK || (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    if (d->T == 0) {
+        if ((st = pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, s)) != LINREC_OK)
+            return st;
+        return pass_carry(d, da_carry_in, da_carry_out, 1, s);
+    }
     const int64_t ns = nseg_of(d->T);
     float* tot = (float*)((char*)workspace + linrec_states_bytes(d));
     const ScanLaunch sc = bwd_scan_of(d, q, dO, decay, 0, d->T, dS_out, dS_in, workspace);
@@ -696,6 +724,8 @@ linrec_status linrec_bwd_recompute(linrec_ctx* ctx, const linrec_desc* d, linrec
         (st = check_ctx(ctx)) != LINREC_OK)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    if (d->T == 0)
+        return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, s);
     const int64_t ns = nseg_of(d->T);
     char* ws = (char*)workspace;
     void* states = ws;
@@ -852,12 +882,14 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
         return st;
     if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
         return LINREC_E_SHAPE;
-    if ((st = check_beta(beta)) != LINREC_OK)
+    if (d->T > 0 && (st = check_beta(beta)) != LINREC_OK)
         return st;
     if (saved && !aligned(saved, 16))
         return LINREC_E_WORKSPACE;
     if ((st = check_ctx(ctx)) != LINREC_OK)
         return st;
+    if (d->T == 0)
+        return pass_carry(d, S_in, S_out, (int64_t)d->dk * d->dv, (hipStream_t)stream);
     linrec::DeltaFwdLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
     s.B = d->B; s.H = d->H; s.T = d->T;
@@ -891,10 +923,12 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
         return st;
     if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
         return LINREC_E_SHAPE;
-    if ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK)
+    if (d->T > 0 && ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK))
         return st;
     if ((st = check_ctx(ctx)) != LINREC_OK)
         return st;
+    if (d->T == 0)
+        return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, (hipStream_t)stream);
     const size_t bh = (size_t)d->B * d->H, T = (size_t)d->T, N = T / kChunk;
     linrec::DeltaBwdLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;

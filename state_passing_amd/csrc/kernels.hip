@@ -736,6 +736,16 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// A piece of zero tokens passes its carry through: dst = src, or zeros when
+// src is NULL (src may equal dst).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void carry_copy_kernel(const float* src, float* dst, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // Decay gradient of a piece, last step.  With g_t = q_t.dq_t - k_t.dk_t the
 // gradient of the loss with respect to the log-decay of token r is the sum
 // of g_t over t >= r (through the end of the sequence: the carry from later
@@ -950,6 +960,16 @@ hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream)
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream)
 {
     LINREC_DISPATCH(bwd_seg_impl, s, stream);
+}
+
+hipError_t launch_carry_copy(const float* src, float* dst, int64_t n, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    launch_kernel(carry_copy_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), stream, src,
+                  dst, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream)

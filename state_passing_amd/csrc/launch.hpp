@@ -172,6 +172,7 @@ hipError_t launch_seg_fold(const ScanLaunch& s, hipStream_t stream);
 hipError_t launch_fwd_intra(const FwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_bwd_intra(const BwdIntraLaunch& s, hipStream_t stream);
 hipError_t launch_da_finish(const DaFinishLaunch& s, hipStream_t stream);
+hipError_t launch_carry_copy(const float* src, float* dst, int64_t n, hipStream_t stream);
 hipError_t launch_delta_fwd(const DeltaFwdLaunch& s, hipStream_t stream);
 hipError_t launch_delta_bwd(const DeltaBwdLaunch& s, hipStream_t stream);
 

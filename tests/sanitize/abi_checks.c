@@ -169,6 +169,16 @@ int main(void)
         const int32_t empty[2] = {0, 320};
         EXPECT(linrec_fwd_seq(NULL, &d, 2, empty, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) ==
                    LINREC_E_SHAPE, "empty piece");
+        /* an empty piece: only the carried pointers are checked */
+        linrec_desc z = d;
+        z.T = 0;
+        linrec_tensor none = {NULL, 0, 0, 0};
+        EXPECT(linrec_fwd(NULL, &z, none, none, none, none, NULL, none, S_out, NULL, NULL) == LINREC_E_NULL,
+               "empty piece fwd");
+        EXPECT(linrec_bwd_da(NULL, &z, none, none, none, none, NULL, none, NULL, none, none, none, S_out,
+                             none, NULL, carry, NULL, NULL) == LINREC_E_NULL, "empty piece bwd_da");
+        EXPECT(linrec_bwd_recompute_workspace_bytes(&z) == 0 && linrec_bwd_da_workspace_bytes(&z) == 0,
+               "empty piece sizes");
         const int32_t short_sum[2] = {64, 64};
         EXPECT(linrec_fwd_seq(NULL, &d, 2, short_sum, tq, tk, tv, tdec, S_in, to, S_out, states, NULL) ==
                    LINREC_E_SHAPE, "pieces do not sum to T");

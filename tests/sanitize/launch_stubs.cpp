@@ -21,5 +21,6 @@ hipError_t launch_bwd_intra(const BwdIntraLaunch&, hipStream_t) { return unexpec
 hipError_t launch_da_finish(const DaFinishLaunch&, hipStream_t) { return unexpected("launch_da_finish"); }
 hipError_t launch_delta_fwd(const DeltaFwdLaunch&, hipStream_t) { return unexpected("launch_delta_fwd"); }
 hipError_t launch_delta_bwd(const DeltaBwdLaunch&, hipStream_t) { return unexpected("launch_delta_bwd"); }
+hipError_t launch_carry_copy(const float*, float*, int64_t, hipStream_t) { return unexpected("launch_carry_copy"); }
 
 }  // namespace linrec

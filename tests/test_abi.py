@@ -72,8 +72,11 @@ def test_sizes():
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [2048, 4096, 2048]) == \
         3 * linrec.states_bytes(d(T=4096))
     assert linrec.bwd_seq_workspace_bytes(d(T=4096), [4096]) == 3 * linrec.states_bytes(d())
-    for bad in (d(T=0), d(T=-64), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
+    for bad in (d(T=-64), d(dk=96), d(dtype=linrec.F32), d(B=0), d(decay=7)):
         assert linrec.states_bytes(bad) == 0
+    # an empty piece is valid and needs no records
+    assert linrec.states_bytes(d(T=0)) == 0 and linrec.bwd_workspace_bytes(d(T=0)) == 0
+    assert linrec.seq_states_bytes(d(T=0), [0]) == 0
     assert linrec.bwd_seq_workspace_bytes(d(T=8192), [4096, 4000]) == 0
 
 
@@ -116,7 +119,7 @@ E = {v: k for k, v in linrec.STATUS.items()}
 
 @pytest.mark.parametrize("desc,code", [
     (d(T=-64), "LINREC_E_SHAPE"),
-    (d(T=0), "LINREC_E_SHAPE"),
+    (d(T=0), "LINREC_E_NULL"),             # an empty piece is valid; no context
     (d(T=100), "LINREC_E_NULL"),           # a ragged length is valid; no context
     (d(dk=96), "LINREC_E_SHAPE"),
     (d(B=0), "LINREC_E_SHAPE"),
@@ -188,7 +191,7 @@ def test_recompute_arguments():
     assert linrec.bwd_recompute_workspace_bytes(d(T=8192)) == \
         2 * linrec.states_bytes(d(T=8192)) + 16 * 128 * 128 * 4
     assert linrec.bwd_recompute_workspace_bytes(d(T=0)) == 0
-    assert call_bwd_recompute(d(T=0)) == E["LINREC_E_SHAPE"]
+    assert call_bwd_recompute(d(T=0)) == E["LINREC_E_NULL"]
     assert call_bwd_recompute(d(T=100)) == E["LINREC_E_NULL"]
     assert call_bwd_recompute(good, workspace=None) == E["LINREC_E_WORKSPACE"]
     assert call_bwd_recompute(good, workspace=FAKE + 8) == E["LINREC_E_WORKSPACE"]
@@ -237,7 +240,7 @@ def test_noalloc_arguments():
     assert call(d(T=7936)) == E["LINREC_E_NULL"]           # 31 segments: fits 32 MiB
     assert linrec.bwd_workspace_bytes(d(T=7936)) <= linrec.NOALLOC_SCRATCH_BYTES
     assert call(d(T=8192)) == E["LINREC_E_SCRATCH"]        # 32 segments: does not
-    assert call(d(T=0)) == E["LINREC_E_SHAPE"]
+    assert call(d(T=0)) == E["LINREC_E_NULL"]
     assert call(d(T=100)) == E["LINREC_E_NULL"]
     assert call(d(), states=None) == E["LINREC_E_WORKSPACE"]
     assert call(d(), dS_in=None) == E["LINREC_E_NULL"]
@@ -277,3 +280,44 @@ def test_delta_arguments():
     assert bcall(d(), dbeta=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
     assert bcall(d(), saved=None) == E["LINREC_E_WORKSPACE"]
     assert bcall(d(dk=64)) == E["LINREC_E_SHAPE"]
+
+
+def test_empty_piece_arguments():
+    """T = 0: only the carried state and gradient pointers are checked;
+    activations, decay, beta, states, saved and workspace may all be NULL.
+    The sequence calls still want every piece to hold a token."""
+    lib = linrec._lib()
+    e = d(T=0, decay=linrec.DECAY_TOKEN)
+    none = linrec.Tensor(None, 0, 0, 0)
+    assert lib.linrec_fwd(None, ctypes.byref(e), none, none, none, none, None, none, FAKE, None,
+                          None) == E["LINREC_E_NULL"]
+    assert lib.linrec_fwd(None, ctypes.byref(e), none, none, none, none, FAKE + 2, none, FAKE,
+                          None, None) == E["LINREC_E_ALIGN"]      # S_in still checked
+    assert lib.linrec_bwd(None, ctypes.byref(e), none, none, none, none, None, none, FAKE + 2,
+                          none, none, none, FAKE, None, None) == E["LINREC_E_ALIGN"]
+    assert lib.linrec_bwd(None, ctypes.byref(e), none, none, none, none, None, none, None,
+                          none, none, none, FAKE, None, None) == E["LINREC_E_NULL"]
+    assert lib.linrec_bwd_noalloc(None, ctypes.byref(e), none, none, none, none, None, none,
+                                  FAKE + 2, none, none, none, FAKE, None) == E["LINREC_E_ALIGN"]
+    assert lib.linrec_bwd_recompute(None, ctypes.byref(e), none, none, none, none, FAKE + 2, none,
+                                    None, none, none, none, FAKE, None, None) == E["LINREC_E_ALIGN"]
+    assert lib.linrec_bwd_da(None, ctypes.byref(e), none, none, none, none, None, none, None,
+                             none, none, none, FAKE, none, None, FAKE, None,
+                             None) == E["LINREC_E_NULL"]
+    assert lib.linrec_bwd_da(None, ctypes.byref(e), none, none, none, none, None, none, None,
+                             none, none, none, FAKE, none, FAKE + 2, FAKE, None,
+                             None) == E["LINREC_E_ALIGN"]          # the carry still checked
+    assert lib.linrec_bwd_da(None, ctypes.byref(d(T=0, decay=linrec.DECAY_NONE)), none, none, none,
+                             none, None, none, None, none, none, none, FAKE, none, None, FAKE,
+                             None, None) == E["LINREC_E_LAYOUT"]   # no decay, no gradient
+    assert lib.linrec_delta_fwd(None, ctypes.byref(e), none, none, none, none, none, FAKE + 2, none,
+                                FAKE, None, None, None) == E["LINREC_E_ALIGN"]
+    assert lib.linrec_delta_bwd(None, ctypes.byref(e), none, none, none, none, none, None, none,
+                                FAKE + 2, none, none, none, none, FAKE, None,
+                                None) == E["LINREC_E_ALIGN"]
+    assert linrec.delta_workspace_bytes(e) == 0 and linrec.delta_saved_bytes(e) == 0
+    arr = (ctypes.c_int32 * 1)(0)
+    assert lib.linrec_fwd_seq(None, ctypes.byref(e), 1, arr, none, none, none, none, None, none,
+                              FAKE, None, None) == E["LINREC_E_SHAPE"]
+    assert lib.linrec_bwd_seq(None, ctypes.byref(e), 1, arr, none, none, none, none, None, none,
+                              None, none, none, none, FAKE, None, None) == E["LINREC_E_SHAPE"]

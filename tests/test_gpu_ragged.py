@@ -185,3 +185,44 @@ def test_ragged_decay_gradient(wl):
     err = rel_err(da, da_ref)
     print(f"[ragged-da] {wl.name} pieces {lengths}: da={err:.2e}", flush=True)
     assert err <= TOL[wl.torch_dtype], err
+
+
+def test_empty_piece_passes_the_carry_through():
+    """T = 0: S_out = S_in, dS_in = dS_out, the decay-gradient carry passes
+    unchanged (a NULL input gives zeros), for every per-piece call; a
+    zero-length piece inside the per-piece loop changes nothing."""
+    B, H, dk, dv = 2, 3, 128, 128
+    g = torch.Generator().manual_seed(11)
+    S = torch.randn(B, H, dk, dv, generator=g).to(DEV)
+    dS = torch.randn(B, H, dk, dv, generator=g).to(DEV)
+    carry = torch.randn(B, H, generator=g).to(DEV)
+    q = torch.empty(B, H, 0, dk, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(B, H, 0, dv, dtype=torch.bfloat16, device=DEV)
+    dec = torch.empty(B, H, 0, dtype=torch.float32, device=DEV)
+    print("case empty piece B=2 H=3 d=128", flush=True)
+    o, S_out, st = linrec.fwd(q, q, v, dec, S)
+    _, S_zero, _ = linrec.fwd(q, q, v, dec, None)
+    dq, dk_, dv_, dS_in = linrec.bwd(q, q, v, dec, st, v, dS)
+    _, _, _, dS_rec = linrec.bwd_recompute(q, q, v, dec, S, v, dS)
+    _, _, _, dS_na = linrec.bwd_noalloc(q, q, v, dec, st, v, dS)
+    _, _, _, dS_da, da, c_out = linrec.bwd_da(q, q, v, dec, st, v, dS, carry)
+    _, _, _, _, _, c_zero = linrec.bwd_da(q, q, v, dec, st, v, None, None)
+    beta = torch.empty(B, H, 0, dtype=torch.float32, device=DEV)
+    _, S_delta, saved = linrec.delta_fwd(q, q, v, beta, dec, S, save=True)
+    *_, dS_delta = linrec.delta_bwd(q, q, v, beta, dec, saved, v, dS)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and dq.numel() == 0 and da.numel() == 0
+    for got in (S_out, S_delta):
+        assert torch.equal(got, S)
+    for got in (dS_in, dS_rec, dS_na, dS_da, dS_delta):
+        assert torch.equal(got, dS)
+    assert torch.equal(c_out, carry)
+    assert not bool(S_zero.any()) and not bool(c_zero.any())
+
+    wl = RAGGED[4]
+    inp = gpu_inputs(wl)
+    base = run_loop(inp, [256, 744], torch.float32)
+    got = run_loop(inp, [256, 0, 744], torch.float32)
+    same = {k: bool(torch.equal(got[k], base[k])) for k in got}
+    print(f"  loop with an empty piece bitwise equal: {same}", flush=True)
+    assert all(same.values()), same

@@ -70,11 +70,12 @@ KERNEL_DESIGN_BYTES = {
     "fwd_seg": 1024 + 256,         # q, k, v, o; reads the segment-start state
     "bwd_sum": 512 + 256,          # q, dO; writes the gradient records
     "bwd_fold": 256 + 256,
-    # k, v, dO for dQ; q, and k, v, dO again except on the chunk both walks
-    # share (one of four); dq, dk, dv; the S and G segment states; the fold
-    # it carries (63 launches of 64 in a step) and the segment sums it
-    # carries (62 of 64)
-    "bwd_seg": 768 + 256 + 576 + 768 + 512 + 512 * 63 / 64 + 768 * 62 / 64,
+    # k, v, dO for dQ; q, and k, v, dO again for the segment's first chunk
+    # only (walk 2 finds the last chunk in LDS and the two before it in
+    # registers); dq, dk, dv; the S and G segment states; the fold it
+    # carries (63 launches of 64 in a step) and the segment sums it carries
+    # (62 of 64)
+    "bwd_seg": 768 + 256 + 192 + 768 + 512 + 512 * 63 / 64 + 768 * 62 / 64,
 }
 KERNEL_SYMBOL = {
     "fwd_sum": "seg_sum_kernel<bf16,128,128,false,false>",

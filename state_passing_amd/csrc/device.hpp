@@ -190,6 +190,20 @@ __device__ __forceinline__ u32x4& chunk_vec(R& r)
         return r.v3;
 }
 
+// d = s, vector by vector (only the NV vectors in use).
+template <typename T, int D, int NT>
+__device__ __forceinline__ void chunk_copy(ChunkRegs<T, D, NT>& d, const ChunkRegs<T, D, NT>& s)
+{
+    constexpr int NV = ChunkRegs<T, D, NT>::NV;
+    d.v0 = s.v0;
+    if constexpr (NV > 1)
+        d.v1 = s.v1;
+    if constexpr (NV > 2)
+        d.v2 = s.v2;
+    if constexpr (NV > 3)
+        d.v3 = s.v3;
+}
+
 template <int P, typename T, int D, int NT>
 __device__ __forceinline__ void chunk_load_one(ChunkRegs<T, D, NT>& r, const T* src, int64_t ld, int rows)
 {

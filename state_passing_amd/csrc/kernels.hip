@@ -446,7 +446,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void fwd_seg_kernel(
 // frag_cols_perm reads of the other operand); outputs are computed
 // transposed (one vector store per lane and tile).  The next chunk's rows
 // load while this one computes; walk 2 starts on walk 1's last chunk, whose
-// K, V, dO and decay tables are still in LDS, so only Q is loaded for it.
+// K, V, dO and decay tables are still in LDS, so only Q is loaded for it,
+// and takes K, V and dO of the two chunks before it from registers that
+// walk 1 filled: of the segment's K, V and dO only the first chunk's are
+// read twice from memory.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV, bool DA, bool RAGGED>
 __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
@@ -503,6 +506,13 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     const T* doh = dO.head(b, h);
     ChunkRegs<T, DK, NT> rq, rk;
     ChunkRegs<T, DV, NT> rv, rdo;
+    // K, V and dO of the segment's chunks n1 - 3 (ka, va, da_) and n1 - 2
+    // (kb, vb, db), kept from walk 1 for walk 2, which would otherwise read
+    // them again.  They move through the pair as a queue (fixed registers,
+    // no indexing).  The decay-gradient variant has no registers to spare.
+    constexpr bool KEEP = !DA;
+    ChunkRegs<T, DK, NT> ka, kb;
+    ChunkRegs<T, DV, NT> va, vb, da_, db;
 
     // the piece's last chunk may be partial: `tail` tokens
     auto rows_of = [&](int c) { return RAGGED && c == N - 1 ? tail : CHUNK; };
@@ -519,6 +529,10 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
     for (int n = n0; n < n1; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         const int rows_n = rows_of(n);
+        if (KEEP && n >= n1 - 3 && n < n1 - 1) {
+            chunk_copy(ka, kb); chunk_copy(va, vb); chunk_copy(da_, db);
+            chunk_copy(kb, rk); chunk_copy(vb, rv); chunk_copy(db, rdo);
+        }
         chunk_store(rk, Ks, QP, rows_n);
         chunk_store(rv, Vs, VP, rows_n);
         chunk_store(rdo, dOs, VP, rows_n);
@@ -618,9 +632,14 @@ __global__ __launch_bounds__(DV / 16 * 64) void bwd_seg_kernel(
             const int64_t tn = (int64_t)(n - 1) * CHUNK;
             const int rw = rows_of(n - 1);
             chunk_load(rq, qh + tn * Q.st, Q.st, rw);
-            chunk_load(rk, kh + tn * K.st, K.st, rw);
-            chunk_load(rv, vh + tn * V.st, V.st, rw);
-            chunk_load(rdo, doh + tn * dO.st, dO.st, rw);
+            if (KEEP && n >= n1 - 2) {
+                chunk_copy(rk, kb); chunk_copy(rv, vb); chunk_copy(rdo, db);
+                chunk_copy(kb, ka); chunk_copy(vb, va); chunk_copy(db, da_);
+            } else {
+                chunk_load(rk, kh + tn * K.st, K.st, rw);
+                chunk_load(rv, vh + tn * V.st, V.st, rw);
+                chunk_load(rdo, doh + tn * dO.st, dO.st, rw);
+            }
             ra = decay_raw(dec, b, h, tn, rw);
         }
         const bool fac = decay_factored(tab);

@@ -59,9 +59,11 @@
  *   S_*, dS_*, decay, the per-chunk state store and the workspace are fp32.
  *
  * ---------------------------------------------------------------- shapes
- *   chunk == 64; T >= 0 (the last chunk of a piece may be partial: its
- *   missing tokens are neither read nor written; the delta-rule calls need
- *   T % 64 == 0); d_k, d_v in {64, 128}; B >= 1, H >= 1.  Activation
+ *   chunk == 64; 0 <= T <= LINREC_MAX_T (the last chunk of a piece may be
+ *   partial: its missing tokens are neither read nor written; the
+ *   delta-rule calls need T % 64 == 0); d_k, d_v in {64, 128};
+ *   1 <= B, H <= 65535.  Offsets into every tensor are 64-bit, so a tensor
+ *   may hold more than 2^31 elements (one head's T * d included).  Activation
  *   pointers and their strides sb, sh, st must keep every token row 16-byte
  *   aligned.
  *   T == 0 (per-piece calls only; every piece of a sequence call has at
@@ -126,6 +128,10 @@ typedef struct {
     void* ptr;
     int64_t sb, sh, st;
 } linrec_tensor;
+
+/* Largest T of a call (2^31 - 4096): token counts, rounded up to whole
+ * chunks and segments, stay within int32_t. */
+#define LINREC_MAX_T 2147479552
 
 /* Problem description of one call (T = tokens of this piece or sequence). */
 typedef struct {

@@ -34,6 +34,8 @@ STATUS = {
 
 # Fixed device scratch of linrec_bwd_noalloc (LINREC_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 32 << 20
+# Largest T of a call (LINREC_MAX_T).
+MAX_T = 2147479552
 
 # Every function include/linrec.h declares.
 EXPORTS = (

@@ -120,6 +120,9 @@ E = {v: k for k, v in linrec.STATUS.items()}
 @pytest.mark.parametrize("desc,code", [
     (d(T=-64), "LINREC_E_SHAPE"),
     (d(T=0), "LINREC_E_NULL"),             # an empty piece is valid; no context
+    (d(T=2147479552), "LINREC_E_NULL"),    # LINREC_MAX_T
+    (d(T=2147479553), "LINREC_E_SHAPE"),
+    (d(T=2147483647), "LINREC_E_SHAPE"),
     (d(T=100), "LINREC_E_NULL"),           # a ragged length is valid; no context
     (d(dk=96), "LINREC_E_SHAPE"),
     (d(B=0), "LINREC_E_SHAPE"),

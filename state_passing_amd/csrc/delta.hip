@@ -158,6 +158,31 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup -> (column block, head, batch) for the serial kernels, whose
+// d_v / 16 column workgroups of one head all read that head's chunk operands
+// (Q, K, W_k, P; dO in the backward).  Workgroups go to the eight XCDs in
+// turn by flat index, and each XCD has its own L2; this mapping puts the
+// column workgroups of one head on one XCD (flat index f: XCD f % 8, head
+// group (f % 8) + 8 (f / 8 / ncb), column block (f / 8) % ncb), so that seven
+// of every eight reads of those operands can hit the L2.  With B * H not a
+// multiple of 8 the plain mapping is kept.
+// ---------------------------------------------------------------------------
+struct ColHead {
+    int cb, h, b;
+};
+
+__device__ __forceinline__ ColHead xcd_col_head(int H, int B)
+{
+    const int ncb = gridDim.x;
+    if ((B * H) % 8 != 0)
+        return ColHead{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    const int f = blockIdx.x + ncb * (blockIdx.y + H * blockIdx.z);
+    const int slot = f / 8;
+    const int grp = f % 8 + 8 * (slot / ncb);
+    return ColHead{slot % ncb, grp % H, grp / H};
+}
+
+// ---------------------------------------------------------------------------
 // Serial walk over a piece's chunks for one (b, h) and state columns
 // [16 cb, 16 cb + 16).  4 waves; wave w carries state row blocks
 // FPW w .. FPW w + FPW - 1 (fp32 result tiles) and computes the chunk's rows
@@ -193,7 +218,8 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     __shared__ __align__(16) T Usp[2][16 * UPP];
     __shared__ __align__(16) float tab[TAB_SIZE];
 
-    const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const ColHead wg = xcd_col_head(H, gridDim.z);
+    const int cb = wg.cb, h = wg.h, b = wg.b;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * cb;
@@ -369,7 +395,8 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     __shared__ __align__(16) T dUsp[2][16 * UPP];
     __shared__ __align__(16) float tab[TAB_SIZE];
 
-    const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const ColHead wg = xcd_col_head(H, gridDim.z);
+    const int cb = wg.cb, h = wg.h, b = wg.b;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * cb;

@@ -346,7 +346,8 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d,
 
 /* Bytes of workspace linrec_delta_fwd needs (0 if `d` is invalid or
  * d_k != d_v): W_k and W_v of every token, then P = (Q K^T) .* D of every
- * chunk, fp32, B*H*T*(d_k + d_v + 64)*4. */
+ * chunk, then the chunk's decay tables (256 values), fp32,
+ * B*H*T*(d_k + d_v + 64 + 4)*4. */
 size_t linrec_delta_workspace_bytes(const linrec_desc* d);
 
 /* Bytes linrec_delta_fwd writes to `saved` for the backward (0 if `d` is
@@ -371,8 +372,8 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d,
 
 /* Bytes of workspace linrec_delta_bwd needs (0 if `d` is invalid or
  * d_k != d_v): W_k, W_v, per-chunk T (then the masked gradient of A),
- * dU (then T^T dU), the gradient leaving every chunk and per-chunk P, all
- * fp32. */
+ * dU (then T^T dU), the gradient leaving every chunk, per-chunk P and the
+ * per-chunk decay tables (256 values), all fp32. */
 size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d);
 
 /* Delta-rule backward over one piece, for L = <dO, o> + <dS_out, S_out>:

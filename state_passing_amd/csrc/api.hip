@@ -837,8 +837,9 @@ size_t linrec_delta_workspace_bytes(const linrec_desc* d)
 {
     if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
         return 0;
-    // W_k, W_v, then P per chunk (64 x 64 per 64 tokens)
-    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv + kChunk) * sizeof(float);
+    // W_k, W_v, then P per chunk (64 x 64 per 64 tokens), then the decay
+    // tables per chunk (256 per 64 tokens)
+    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv + kChunk + 4) * sizeof(float);
 }
 
 size_t linrec_delta_saved_bytes(const linrec_desc* d)
@@ -854,7 +855,7 @@ size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
     if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
         return 0;
     const size_t bh = (size_t)d->B * d->H, N = (size_t)(d->T / kChunk);
-    return bh * ((size_t)d->T * (d->dk + 2 * d->dv + kChunk) + N * kChunk * kChunk + N * d->dk * d->dv) *
+    return bh * ((size_t)d->T * (d->dk + 2 * d->dv + kChunk + 4) + N * kChunk * kChunk + N * d->dk * d->dv) *
            sizeof(float);
 }
 
@@ -902,6 +903,7 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.wk = (float*)workspace;
     s.wv = (float*)workspace + (size_t)d->B * d->H * (size_t)d->T * d->dk;
     s.pm = s.wv + (size_t)d->B * d->H * (size_t)d->T * d->dv;
+    s.tabs = s.pm + (size_t)d->B * d->H * (size_t)d->T * kChunk;
     if (saved) {
         s.s0 = (float*)saved;
         s.u = (float*)saved + (size_t)d->B * d->H * (size_t)(d->T / kChunk) * d->dk * d->dv;
@@ -948,6 +950,7 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.duy = s.tm + bh * N * kChunk * kChunk;
     s.dsc = s.duy + bh * T * d->dv;
     s.pm = s.dsc + bh * N * d->dk * d->dv;
+    s.tabs = s.pm + bh * T * kChunk;
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_bwd(s, (hipStream_t)stream); }));
     return LINREC_OK;

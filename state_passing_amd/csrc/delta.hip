@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
                                                          Act<const float> beta, DecayArg dec,
                                                          Act<float> Wk, Act<float> Wv,
                                                          float* __restrict__ Pout,
-                                                         float* __restrict__ Tout, int H)
+                                                         float* __restrict__ Tout,
+                                                         float* __restrict__ TabOut, int H)
 {
     constexpr int NT = 256, NW = 4;
     constexpr int PAD = Pad<T>::value;
@@ -82,6 +83,10 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
         bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
     }
     __syncthreads();
+    // the chunk's decay tables for the serial kernels, [B][H][N][TAB_SIZE]
+    if (threadIdx.x < TAB_SIZE / 4)
+        *reinterpret_cast<floatx4*>(TabOut + (((int64_t)b * H + h) * gridDim.x + n) * TAB_SIZE +
+                                    4 * threadIdx.x) = *reinterpret_cast<const floatx4*>(tab + 4 * threadIdx.x);
 
     // A: strictly lower part of beta_i exp(lam_i - lam_j) (k_i . k_j); and
     // P = (Q K^T) .* D (lower, diagonal included) for the serial kernels,
@@ -196,7 +201,8 @@ template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
                                                          Act<const float> Wk, Act<const float> Wv,
                                                          const float* __restrict__ Pm,
-                                                         DecayArg dec, const float* S_in,
+                                                         const float* __restrict__ tabs,
+                                                         const float* S_in,
                                                          float* S_out, Act<OT> O,
                                                          float* __restrict__ s0_out,
                                                          float* __restrict__ u_out, int H, int N)
@@ -237,13 +243,17 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     const float* wkh = Wk.head(b, h);
     const float* wvh = Wv.head(b, h);
     const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
-    // the next chunk's Q, K, W_k, this workgroup's W_v columns and P are
-    // loaded into registers while the current chunk computes
+    const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
+    // the next chunk's Q, K, W_k, this workgroup's W_v columns, P and decay
+    // tables (formed by the prep kernel) are loaded into registers while the
+    // current chunk computes
     constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
     static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK, "chunk split");
     ChunkRegs<T, DK, NT> rq, rk;
-    floatx4 rwk[NWK], rpv[NPV], rwv;
+    floatx4 rwk[NWK], rpv[NPV], rwv, rtab = zero4();
     auto load_next = [&](int64_t tk) {
+        if (threadIdx.x < TAB_SIZE / 4)
+            rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
         chunk_load(rq, qh + tk * Q.st, Q.st);
         chunk_load(rk, kh + tk * K.st, K.st);
 #pragma unroll
@@ -278,8 +288,8 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
             *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
         }
-        if (w == 0)
-            decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
+        if (threadIdx.x < TAB_SIZE / 4)
+            *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
 #pragma unroll
         for (int q = 0; q < FPW; ++q) {
             put_split4(Ssp[0], Ssp[1], t * SPP + 16 * (FPW * w + q), S[q]);
@@ -376,7 +386,8 @@ template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
                                                           Act<const T> dO, Act<const float> Wk,
                                                           const float* __restrict__ Pm,
-                                                          DecayArg dec, const float* dS_out,
+                                                          const float* __restrict__ tabs,
+                                                          const float* dS_out,
                                                           float* dS_in, float* __restrict__ dU_out,
                                                           float* __restrict__ dsc_out, int H, int N)
 {
@@ -414,16 +425,19 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     const T* doh = dO.head(b, h);
     const float* wkh = Wk.head(b, h);
     const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
-    // the next (earlier) chunk's Q, K, dO columns, W_k and P load into
-    // registers while the current chunk computes
+    const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
+    // the next (earlier) chunk's Q, K, dO columns, W_k, P and decay tables
+    // load into registers while the current chunk computes
     constexpr int VEC = 16 / sizeof(T), PER = 16 / VEC;   // 16-byte vectors per dO slice row
     constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
     static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK && CHUNK * PER <= NT,
                   "chunk split");
     ChunkRegs<T, DK, NT> rq, rk;
-    floatx4 rwk[NWK], rpv[NPV];
+    floatx4 rwk[NWK], rpv[NPV], rtab = zero4();
     u32x4 rdo = {0u, 0u, 0u, 0u};
     auto load_next = [&](int64_t tk) {
+        if (threadIdx.x < TAB_SIZE / 4)
+            rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
         chunk_load(rq, qh + tk * Q.st, Q.st);
         chunk_load(rk, kh + tk * K.st, K.st);
         if (threadIdx.x < CHUNK * PER) {
@@ -458,8 +472,8 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
             const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
             *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
         }
-        if (w == 0)
-            decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
+        if (threadIdx.x < TAB_SIZE / 4)
+            *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
 #pragma unroll
         for (int q = 0; q < FPW; ++q) {
             put_split4(Gsp[0], Gsp[1], t * SPP + 16 * (FPW * w + q), G[q]);
@@ -794,13 +808,14 @@ hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
     const int N = s.T / CHUNK;
     launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
                   dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                  nullptr, s.H);
+                  nullptr, s.tabs, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     launch_kernel((delta_scan_kernel<T, OT, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256),
                   stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
-                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, dec, s.S_in, s.S_out,
+                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, (const float*)s.tabs,
+                  s.S_in, s.S_out,
                   Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N);
     return hipGetLastError();
 }
@@ -814,13 +829,14 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
     const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
     launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
                   dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                  s.tm, s.H);
+                  s.tm, s.tabs, s.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     launch_kernel((delta_bscan_kernel<T, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
                   dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
-                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, dec, s.dS_out,
+                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, (const float*)s.tabs,
+                  s.dS_out,
                   s.dS_in, s.duy,
                   s.dsc, s.H, N);
     if ((e = hipGetLastError()) != hipSuccess)

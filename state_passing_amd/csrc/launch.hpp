@@ -143,12 +143,13 @@ struct DeltaFwdLaunch {
     float* s0;               // optional: the state entering every chunk, [B][H][N][d_k][d_v]
     float* u;                // optional: U of every token, [B][H][T][d_v]
     float* pm;               // P = (Q K^T) .* D per chunk, [B][H][N][64][64] (workspace)
+    float* tabs;             // the decay tables of every chunk, [B][H][N][256] (workspace)
 };
 
 // Gated delta rule, backward over one piece, from the forward's saved s0 and
 // u.  Workspace: W_k, W_v (as the forward), T then M per chunk
 // ([B][H][N][64][64]), dU then Y ([B][H][T][d_v]), dS_C per chunk, P per
-// chunk.
+// chunk, the decay tables per chunk.
 struct DeltaBwdLaunch {
     int dtype, out_dtype, dk, dv, B, H, T;
     TensorArg q, k, v, beta, decay, dO, dq, dk_, dv_, dbeta;
@@ -163,6 +164,7 @@ struct DeltaBwdLaunch {
     float* duy;
     float* dsc;
     float* pm;
+    float* tabs;
 };
 
 // The state transition is two launches: the parallel segment sum, then the

@@ -251,8 +251,8 @@ def test_noalloc_arguments():
 
 def test_delta_arguments():
     lib = linrec._lib()
-    # W_k and W_v per token, then P (64 x 64) per chunk
-    assert linrec.delta_workspace_bytes(d()) == 16 * 4096 * (256 + 64) * 4
+    # W_k and W_v per token, then P (64 x 64) and the decay tables (256) per chunk
+    assert linrec.delta_workspace_bytes(d()) == 16 * 4096 * (256 + 64 + 4) * 4
     assert linrec.delta_workspace_bytes(d(dk=64)) == 0        # d_k != d_v
     assert linrec.delta_workspace_bytes(d(T=100)) == 0
 
@@ -268,11 +268,12 @@ def test_delta_arguments():
     assert call(d(), saved=FAKE + 8) == E["LINREC_E_WORKSPACE"]
     assert call(d(), saved=FAKE) == E["LINREC_E_NULL"]
     # saved: one state per chunk and U per token; backward workspace: W_k, W_v,
-    # T per chunk, dU per token, one gradient state per chunk and P per chunk
+    # T per chunk, dU per token, one gradient state per chunk, P and the decay
+    # tables per chunk
     N = 4096 // 64
     assert linrec.delta_saved_bytes(d()) == 16 * (N * 128 * 128 + 4096 * 128) * 4
     assert linrec.delta_bwd_workspace_bytes(d()) == \
-        16 * (4096 * 384 + 2 * N * 64 * 64 + N * 128 * 128) * 4
+        16 * (4096 * 384 + 2 * N * 64 * 64 + N * 256 + N * 128 * 128) * 4
 
     def bcall(desc, dbeta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), saved=FAKE):
         return lib.linrec_delta_bwd(None, ctypes.byref(desc), act(), act(), act(),

@@ -36,6 +36,31 @@
 
 namespace linrec {
 
+// 16 x 16 x 16 fp32 products on v_mfma_f32_16x16x4_f32: sub-step r contracts
+// the k-slots {4g + r}.  X is read as rows of an fp32 LDS tile (lane (g,t)
+// takes X[t][4g .. 4g + 3] in one read); Y either from LDS (Y[4g + r][t]) or
+// as a result tile in registers (lane (g,t) holds Y[4g + r][t]), so results
+// chain without moving between lanes.  Result: lane (g,t) gets D[4g + r][t].
+__device__ __forceinline__ floatx4 mm16_f32(const float* X, int xp, const float* Y, int yp, floatx4 acc)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const floatx4 xa = *reinterpret_cast<const floatx4*>(X + t * xp + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[r], Y[(4 * g + r) * yp + t], acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ __forceinline__ floatx4 mm16_f32_reg(const float* X, int xp, floatx4 y, floatx4 acc)
+{
+    const int l = lane_id(), t = l & 15, g = l >> 4;
+    const floatx4 xa = *reinterpret_cast<const floatx4*>(X + t * xp + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[r], y[r], acc, 0, 0, 0);
+    return acc;
+}
+
 // ---------------------------------------------------------------------------
 // Per chunk: T = (I + A)^{-1}, then W_v, W_k (fp32, [B][H][T][d]).
 // Workgroup = (chunk, h, b), 4 waves.
@@ -69,18 +94,24 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t tok0 = (int64_t)n * CHUNK;
     {
+        // the gate and beta first: their use waits on nothing else
+        float raw = 0.f, bt = 0.f;
+        if (w == 0) {
+            raw = decay_raw(dec, b, h, tok0);
+            bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+        }
         ChunkRegs<T, DK, NT> rq, rk;
         ChunkRegs<T, DV, NT> rv;
         chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
         chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
         chunk_load(rv, V.head(b, h) + tok0 * V.st, V.st);
+        if (w == 0) {
+            decay_tables(dec, raw, tab);
+            bet[l] = bt;
+        }
         chunk_store(rq, Qs, KP);
         chunk_store(rk, Ks, KP);
         chunk_store(rv, Vs, VP);
-    }
-    if (w == 0) {
-        decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
-        bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
     }
     __syncthreads();
     // the chunk's decay tables for the serial kernels, [B][H][N][TAB_SIZE]
@@ -114,51 +145,83 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
     }
     __syncthreads();
 
-    // T = (I + A)^{-1} by forward substitution, one column per lane of wave 0:
-    // x_i = [i == j] - sum_{m < i} A_im x_m  (x_m = 0 for m < j)
-    if (w == 0) {
-        float x[CHUNK];
+    // T = (I + A)^{-1}, unit lower triangular, by 16 x 16 blocks (block
+    // row i, column j).  Wave w inverts the diagonal block w by forward
+    // substitution (lane c < 16 takes column c:
+    // x_r = [r == c] - sum_{m < r} A_ww[r][m] x_m) and clears the blocks
+    // right of it; then, one block diagonal at a time, wave i forms
+    //     T_ij = -T_ii sum_{k = j .. i-1} A_ik T_kj
+    // with fp32 MFMA (the blocks it needs are all on earlier diagonals).
+    {
+        if (l < 16) {
+            float x[16];
 #pragma unroll
-        for (int i = 0; i < CHUNK; ++i) {
-            float acc = i == l ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) {
+                float acc = r == l ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m)
-                acc -= As[i * AP + m] * x[m];
-            x[i] = acc;
+                for (int m = 0; m < r; ++m)
+                    acc -= As[(16 * w + r) * AP + 16 * w + m] * x[m];
+                x[r] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                Ts[(16 * w + r) * AP + 16 * w + l] = x[r];
         }
+        for (int e = l; e < 16 * 16 * (3 - w); e += 64)
+            Ts[(16 * w + (e & 15)) * AP + 16 * (w + 1) + (e >> 4)] = 0.f;
+        __syncthreads();
+        for (int dg = 1; dg < 4; ++dg) {
+            if (w >= dg) {
+                const int i = w, j = w - dg;
+                floatx4 m4 = zero4();
+                for (int k = j; k < i; ++k)
+                    m4 = mm16_f32(As + (16 * i) * AP + 16 * k, AP, Ts + (16 * k) * AP + 16 * j, AP, m4);
+                floatx4 t4 = mm16_f32_reg(Ts + (16 * i) * AP + 16 * i, AP, m4, zero4());
 #pragma unroll
-        for (int i = 0; i < CHUNK; ++i)
-            Ts[i * AP + l] = x[i];
+                for (int r = 0; r < 4; ++r)
+                    Ts[(16 * i + 4 * g + r) * AP + 16 * j + t] = -t4[r];
+            }
+            __syncthreads();
+        }
         if (Tout) {   // the backward's copy: [B][H][N][64][64]
             float* dst = Tout + (((int64_t)b * H + h) * gridDim.x + n) * CHUNK * CHUNK;
-#pragma unroll
-            for (int i = 0; i < CHUNK; ++i)
-                dst[i * CHUNK + l] = x[i];
+            for (int e = 4 * (int)threadIdx.x; e < CHUNK * CHUNK; e += 4 * NT)
+                *reinterpret_cast<floatx4*>(dst + e) =
+                    *reinterpret_cast<const floatx4*>(Ts + (e / CHUNK) * AP + e % CHUNK);
         }
     }
-    __syncthreads();
 
     // W^T[c][i] = sum_j X[j][c] (T[i][j] beta_j [gamma_j]) with X = V (W_v) or
-    // K (W_k); transposed tiles so each lane stores four consecutive features
-    constexpr int JV = 4 * (DV / 16), JOBS = JV + 4 * (DK / 16);
-    for (int job = w; job < JOBS; job += NW) {
-        const bool isk = job >= JV;
-        const int jj = isk ? job - JV : job, ib = jj & 3, cb = jj >> 2;
-        floatx4 acc = zero4();
+    // K (W_k); wave w takes the rows i of block w, so it forms its B operand
+    // (T beta [gamma], split) once per k32 step and reuses it for every column
+    // block; transposed tiles so each lane stores four consecutive features
+#pragma unroll
+    for (int isk = 0; isk < 2; ++isk) {
+        Split<T> top[CHUNK / 32];
 #pragma unroll
         for (int ks = 0; ks < CHUNK / 32; ++ks) {
             float x[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int j = 32 * ks + 8 * g + r;
-                x[r] = Ts[(16 * ib + t) * AP + j] * bet[j] * (isk ? tab[TAB_G + j] : 1.f);
+                x[r] = Ts[(16 * w + t) * AP + j] * bet[j] * (isk ? tab[TAB_G + j] : 1.f);
             }
-            const Split<T> top = split8<T>(x);
-            acc = mma(isk ? frag_cols(Ks, KP, 16 * cb, 32 * ks) : frag_cols(Vs, VP, 16 * cb, 32 * ks), top,
-                      acc);
+            top[ks] = split8<T>(x);
         }
         Act<float>& W = isk ? Wk : Wv;
-        store_tile_t<float>(W.head(b, h) + tok0 * W.st, W.st, 16 * ib, 16 * cb, acc);
+        const T* X = isk ? Ks : Vs;
+        const int XP = isk ? KP : VP;
+        constexpr int NCB = (DK > DV ? DK : DV) / 16;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            if (cb < (isk ? DK : DV) / 16) {
+                floatx4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < CHUNK / 32; ++ks)
+                    acc = mma(frag_cols(X, XP, 16 * cb, 32 * ks), top[ks], acc);
+                store_tile_t<float>(W.head(b, h) + tok0 * W.st, W.st, 16 * w, 16 * cb, acc);
+            }
+        }
     }
 }
 

@@ -553,7 +553,6 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
         // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
         {
             floatx4 acc = zero4(), acc2 = zero4();
-#pragma unroll
             for (int js = w / 2; js < 2; ++js)
                 acc = mma(split_cols_f32<T>(Ps, PP, 16 * w, 32 * js), frag_cols(dOs, OP, 0, 32 * js), acc);
 #pragma unroll
@@ -604,7 +603,8 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
 // [16 w, 16 w + 16) of Y, dV, M and dbeta (no reduction crosses waves).
 template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<const T> V,
-                                                           Act<const float> beta, DecayArg dec,
+                                                           Act<const float> beta,
+                                                           const float* __restrict__ tabs,
                                                            const float* __restrict__ s0,
                                                            const float* __restrict__ u,
                                                            float* __restrict__ Tm, float* __restrict__ dUY,
@@ -612,14 +612,25 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
 {
     constexpr int NT = 256;
     constexpr int PAD = Pad<T>::value;
-    constexpr int KP = DK + PAD;
+    constexpr int KP = DK + PAD, SPP = DK + PAD;
     constexpr int UP = DV + 4, AP = CHUNK + 4;
+    // One LDS region serves three phases in turn: T and dU (Y from them);
+    // S_0 as bf16 hi/lo planes, transposed ([c][f]), for K S_0; then Y and U
+    // for the gradient of A.
+    constexpr int PH1 = (CHUNK * AP + CHUNK * UP) * 4;
+    constexpr int PH2 = 2 * DV * SPP * (int)sizeof(T);
+    constexpr int PH3 = 2 * CHUNK * UP * 4;
+    constexpr int RBYTES = PH1 > PH2 ? (PH1 > PH3 ? PH1 : PH3) : (PH2 > PH3 ? PH2 : PH3);
     __shared__ __align__(16) T Ks[CHUNK * KP];
-    __shared__ __align__(16) float Ts[CHUNK * AP];
-    __shared__ __align__(16) float Us[CHUNK * UP];
-    __shared__ __align__(16) float Ys[CHUNK * UP];   // dU, then Y
+    __shared__ __align__(16) unsigned char region[RBYTES];
     __shared__ __align__(16) float tab[TAB_SIZE];
     __shared__ float bet[CHUNK];
+    float* const Ts = reinterpret_cast<float*>(region);
+    float* const dUs = Ts + CHUNK * AP;
+    T* const S0h = reinterpret_cast<T*>(region);
+    T* const S0l = S0h + DV * SPP;
+    float* const Ys = reinterpret_cast<float*>(region);
+    float* const Us = Ys + CHUNK * UP;
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z, N = gridDim.x;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
@@ -629,23 +640,49 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     const float* S0 = s0 + (bh * N + n) * DK * DV;
     const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
     float* yc = dUY + (bh * (int64_t)N * CHUNK + tok0) * DV;
-    {
-        ChunkRegs<T, DK, NT> rk;
-        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
-        chunk_store(rk, Ks, KP);
+    const T* vh = V.head(b, h) + tok0 * V.st;
+
+    // every global read of the kernel but S_0 is issued here, together:
+    // beta, the decay tables, K, T, dU, U, and this lane's V values
+    constexpr int NTV = CHUNK * CHUNK / 4 / NT, NUV = CHUNK * DV / 4 / NT;
+    static_assert(NTV * NT * 4 == CHUNK * CHUNK && NUV * NT * 4 == CHUNK * DV, "chunk split");
+    float bt = 0.f;
+    floatx4 rtab = zero4(), rt[NTV], rdu[NUV], ru[NUV];
+    if (threadIdx.x < CHUNK)
+        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + threadIdx.x) * beta.st];
+    if (threadIdx.x < TAB_SIZE / 4)
+        rtab = *reinterpret_cast<const floatx4*>(tabs + (bh * N + n) * TAB_SIZE + 4 * threadIdx.x);
+    ChunkRegs<T, DK, NT> rk;
+    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
+#pragma unroll
+    for (int i = 0; i < NTV; ++i)
+        rt[i] = *reinterpret_cast<const floatx4*>(Tc + 4 * (threadIdx.x + NT * i));
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+        rdu[i] = *reinterpret_cast<const floatx4*>(yc + 4 * (threadIdx.x + NT * i));
+        ru[i] = *reinterpret_cast<const floatx4*>(uc + 4 * (threadIdx.x + NT * i));
     }
-    for (int idx = threadIdx.x; idx < CHUNK * CHUNK / 4; idx += NT) {
-        const int row = idx / (CHUNK / 4), col = 4 * (idx % (CHUNK / 4));
-        *reinterpret_cast<floatx4*>(Ts + row * AP + col) = *reinterpret_cast<const floatx4*>(Tc + row * CHUNK + col);
+    float vv[DV / 16][4];   // V[16 w + 4 g + r][16 cb + t]
+#pragma unroll
+    for (int cb = 0; cb < DV / 16; ++cb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vv[cb][r] = (float)vh[(16 * w + 4 * g + r) * V.st + 16 * cb + t];
+
+    if (threadIdx.x < CHUNK)
+        bet[threadIdx.x] = bt;
+    if (threadIdx.x < TAB_SIZE / 4)
+        *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
+    chunk_store(rk, Ks, KP);
+#pragma unroll
+    for (int i = 0; i < NTV; ++i) {
+        const int e = 4 * (threadIdx.x + NT * i);
+        *reinterpret_cast<floatx4*>(Ts + (e / CHUNK) * AP + e % CHUNK) = rt[i];
     }
-    for (int idx = threadIdx.x; idx < CHUNK * DV / 4; idx += NT) {
-        const int row = idx / (DV / 4), col = 4 * (idx % (DV / 4));
-        *reinterpret_cast<floatx4*>(Us + row * UP + col) = *reinterpret_cast<const floatx4*>(uc + row * DV + col);
-        *reinterpret_cast<floatx4*>(Ys + row * UP + col) = *reinterpret_cast<const floatx4*>(yc + row * DV + col);
-    }
-    if (w == 0) {
-        decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
-        bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+        const int e = 4 * (threadIdx.x + NT * i);
+        *reinterpret_cast<floatx4*>(dUs + (e / DV) * UP + e % DV) = rdu[i];
     }
     __syncthreads();
 
@@ -654,40 +691,72 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
 #pragma unroll
     for (int cb = 0; cb < DV / 16; ++cb) {
         Y[cb] = zero4();
-#pragma unroll
         for (int ms = w / 2; ms < 2; ++ms)
-            Y[cb] = mma(split_cols_f32<T>(Ts, AP, 16 * w, 32 * ms), split_cols_f32<T>(Ys, UP, 16 * cb, 32 * ms),
+            Y[cb] = mma(split_cols_f32<T>(Ts, AP, 16 * w, 32 * ms), split_cols_f32<T>(dUs, UP, 16 * cb, 32 * ms),
                         Y[cb]);
     }
-    __syncthreads();   // every wave has read dU
-    float db[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta of rows 16 w + 4g + r, this lane's columns
     {
+        // Y to the workspace (over dU, which every thread read before the
+        // barrier above) and dV
         OT* dvh = dVo.head(b, h) + tok0 * dVo.st;
-        const T* vh = V.head(b, h) + tok0 * V.st;
-        // ROCm 7.2's hipcc merged two of the Y stores below into one
-        // ds_write2_b32 whose first offset was wrong (one Y element per row
-        // 4g + 3 stayed dU); volatile keeps the stores apart.
-        auto* ysv = (volatile __attribute__((address_space(3))) float*)Ys;
 #pragma unroll
-        for (int cb = 0; cb < DV / 16; ++cb) {
-            // (K S_0) tile of rows 16 w, columns 16 cb
-            floatx4 ks0 = zero4();
-#pragma unroll
-            for (int fs = 0; fs < DK / 32; ++fs)
-                ks0 = mma(frag_rows(Ks, KP, 16 * w, 32 * fs), split_cols_glob<T>(S0, DV, 16 * cb, 32 * fs), ks0);
+        for (int cb = 0; cb < DV / 16; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r, c = 16 * cb + t;
-                const float y = Y[cb][r];
-                ysv[i * UP + c] = y;
-                yc[i * DV + c] = y;
-                dvh[i * dVo.st + c] = (OT)(bet[i] * y);
-                const float z = (float)vh[i * V.st + c] - tab[TAB_G + i] * ks0[r];
-                db[r] += z * y;
+                yc[i * DV + c] = Y[cb][r];
+                dvh[i * dVo.st + c] = (OT)(bet[i] * Y[cb][r]);
             }
+    }
+    // S_0 (fp32 [f][c]) in result-tile order: lane (g, t) of wave w takes
+    // the tiles (fb, cb) with fb = w, w + 4, ...
+    constexpr int NFB = DK / 16, NCB = DV / 16, SPW = NFB * NCB / 4;
+    float sv[SPW][4];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int fb = w + 4 * (k / NCB), cb = k % NCB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sv[k][r] = S0[(16 * fb + 4 * g + r) * DV + 16 * cb + t];
+    }
+    __syncthreads();   // every wave has read T and dU
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+        const int fb = w + 4 * (k / NCB), cb = k % NCB;
+        put_split4(S0h, S0l, (16 * cb + t) * SPP + 16 * fb, floatx4{sv[k][0], sv[k][1], sv[k][2], sv[k][3]});
+    }
+    __syncthreads();
+
+    // (K S_0) of rows 16 w; z = V - gamma (K S_0); dbeta gets < z_i, Y_i >
+    float db[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta of rows 16 w + 4g + r, this lane's columns
+#pragma unroll
+    for (int cb = 0; cb < DV / 16; ++cb) {
+        floatx4 ks0 = zero4();
+#pragma unroll
+        for (int fs = 0; fs < DK / 32; ++fs)
+            ks0 = mma(frag_rows(Ks, KP, 16 * w, 32 * fs), frag_rows_split(S0h, S0l, SPP, 16 * cb, 32 * fs), ks0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * g + r;
+            db[r] += (vv[cb][r] - tab[TAB_G + i] * ks0[r]) * Y[cb][r];
         }
     }
-    __syncthreads();   // Y rows in LDS
+    __syncthreads();   // every wave has read S_0
+    // Y and U to LDS (over S_0)
+    {
+        auto* ysv = (volatile __attribute__((address_space(3))) float*)Ys;
+#pragma unroll
+        for (int cb = 0; cb < DV / 16; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                ysv[(16 * w + 4 * g + r) * UP + 16 * cb + t] = Y[cb][r];
+    }
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+        const int e = 4 * (threadIdx.x + NT * i);
+        *reinterpret_cast<floatx4*>(Us + (e / DV) * UP + e % DV) = ru[i];
+    }
+    __syncthreads();
     // dA = -Y U^T (j < i), M = dA .* gamma_i / gamma_j; sum_j M_ij k_i . k_j into dbeta
     for (int jb = 0; jb <= w; ++jb) {
         floatx4 dA = zero4(), gk = zero4();
@@ -727,7 +796,8 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
 // output tiles are spread over the waves.
 template <typename T, typename OT, int DK, int DV>
 __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
-                                                           Act<const float> beta, DecayArg dec,
+                                                           Act<const float> beta,
+                                                           const float* __restrict__ tabs,
                                                            const float* __restrict__ s0,
                                                            const float* __restrict__ dsc,
                                                            const float* __restrict__ u,
@@ -743,6 +813,7 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
     __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T dOs[CHUNK * OP];
     __shared__ __align__(16) float Us[CHUNK * UP];
+    __shared__ __align__(16) float Ys[CHUNK * UP];
     __shared__ __align__(16) float Ms[CHUNK * AP];
     __shared__ __align__(16) float dPs[CHUNK * AP];
     __shared__ __align__(16) float tab[TAB_SIZE];
@@ -757,27 +828,63 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
     const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
     const float* yc = Y + (bh * (int64_t)N * CHUNK + tok0) * DV;
     const float* Mc = Mg + (bh * N + n) * CHUNK * CHUNK;
-    {
-        ChunkRegs<T, DK, NT> rq, rk;
-        ChunkRegs<T, DV, NT> ro;
-        chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
-        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
-        chunk_load(ro, dO.head(b, h) + tok0 * dO.st, dO.st);
-        chunk_store(rq, Qs, QP);
-        chunk_store(rk, Ks, QP);
-        chunk_store(ro, dOs, OP);
+
+    // Wave w takes the feature blocks fb = w, w + 4, ... of dQ and dK, every
+    // row block of each; the rows of S_0 and dS_C it needs (as B operands,
+    // row 16 fb + t, columns 32 cs + 8 g ..) are read once, up front,
+    // together with everything else the kernel reads.
+    constexpr int NFB = DK / 16, FBW = NFB / NW, NCS = DV / 32;
+    static_assert(FBW * NW == NFB, "d_k must be 64 or 128");
+    constexpr int NUV = CHUNK * DV / 4 / NT, NMV = CHUNK * CHUNK / 4 / NT;
+    static_assert(NUV * NT * 4 == CHUNK * DV && NMV * NT * 4 == CHUNK * CHUNK, "chunk split");
+    float bt = 0.f;
+    floatx4 rtab = zero4(), ru[NUV], ry[NUV], rm[NMV];
+    floatx4 s0r[FBW][NCS][2], dsr[FBW][NCS][2];
+    if (threadIdx.x < CHUNK)
+        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + threadIdx.x) * beta.st];
+    if (threadIdx.x < TAB_SIZE / 4)
+        rtab = *reinterpret_cast<const floatx4*>(tabs + (bh * N + n) * TAB_SIZE + 4 * threadIdx.x);
+    ChunkRegs<T, DK, NT> rq, rk;
+    ChunkRegs<T, DV, NT> ro;
+    chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
+    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
+    chunk_load(ro, dO.head(b, h) + tok0 * dO.st, dO.st);
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+        ru[i] = *reinterpret_cast<const floatx4*>(uc + 4 * (threadIdx.x + NT * i));
+        ry[i] = *reinterpret_cast<const floatx4*>(yc + 4 * (threadIdx.x + NT * i));
     }
-    for (int idx = threadIdx.x; idx < CHUNK * DV / 4; idx += NT) {
-        const int row = idx / (DV / 4), col = 4 * (idx % (DV / 4));
-        *reinterpret_cast<floatx4*>(Us + row * UP + col) = *reinterpret_cast<const floatx4*>(uc + row * DV + col);
+#pragma unroll
+    for (int i = 0; i < NMV; ++i)
+        rm[i] = *reinterpret_cast<const floatx4*>(Mc + 4 * (threadIdx.x + NT * i));
+#pragma unroll
+    for (int q = 0; q < FBW; ++q)
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+            const int off = (16 * (w + NW * q) + t) * DV + 32 * cs + 8 * g;
+            s0r[q][cs][0] = *reinterpret_cast<const floatx4*>(S0 + off);
+            s0r[q][cs][1] = *reinterpret_cast<const floatx4*>(S0 + off + 4);
+            dsr[q][cs][0] = *reinterpret_cast<const floatx4*>(dSC + off);
+            dsr[q][cs][1] = *reinterpret_cast<const floatx4*>(dSC + off + 4);
+        }
+
+    if (threadIdx.x < CHUNK)
+        bet[threadIdx.x] = bt;
+    if (threadIdx.x < TAB_SIZE / 4)
+        *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
+    chunk_store(rq, Qs, QP);
+    chunk_store(rk, Ks, QP);
+    chunk_store(ro, dOs, OP);
+#pragma unroll
+    for (int i = 0; i < NUV; ++i) {
+        const int e = 4 * (threadIdx.x + NT * i);
+        *reinterpret_cast<floatx4*>(Us + (e / DV) * UP + e % DV) = ru[i];
+        *reinterpret_cast<floatx4*>(Ys + (e / DV) * UP + e % DV) = ry[i];
     }
-    for (int idx = threadIdx.x; idx < CHUNK * CHUNK / 4; idx += NT) {
-        const int row = idx / (CHUNK / 4), col = 4 * (idx % (CHUNK / 4));
-        *reinterpret_cast<floatx4*>(Ms + row * AP + col) = *reinterpret_cast<const floatx4*>(Mc + row * CHUNK + col);
-    }
-    if (w == 0) {
-        decay_tables(dec, decay_raw(dec, b, h, tok0), tab);
-        bet[l] = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+#pragma unroll
+    for (int i = 0; i < NMV; ++i) {
+        const int e = 4 * (threadIdx.x + NT * i);
+        *reinterpret_cast<floatx4*>(Ms + (e / CHUNK) * AP + e % CHUNK) = rm[i];
     }
     __syncthreads();
 
@@ -798,58 +905,66 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
     }
     __syncthreads();
 
-    constexpr int NFB = DK / 16;
-    for (int job = w; job < 8 * NFB; job += NW) {
-        const bool isk = job >= 4 * NFB;
-        const int jj = isk ? job - 4 * NFB : job, rb = jj & 3, fb = jj >> 2;
-        floatx4 acc = zero4();
-        if (!isk) {
+    OT* outq = dQo.head(b, h) + tok0 * dQo.st;
+    OT* outk = dKo.head(b, h) + tok0 * dKo.st;
+#pragma unroll
+    for (int q = 0; q < FBW; ++q) {
+        const int fb = w + NW * q;
+        Split<T> s0f[NCS], dsf[NCS];
+#pragma unroll
+        for (int cs = 0; cs < NCS; ++cs) {
+            const float xs[8] = {s0r[q][cs][0][0], s0r[q][cs][0][1], s0r[q][cs][0][2], s0r[q][cs][0][3],
+                                 s0r[q][cs][1][0], s0r[q][cs][1][1], s0r[q][cs][1][2], s0r[q][cs][1][3]};
+            const float xd[8] = {dsr[q][cs][0][0], dsr[q][cs][0][1], dsr[q][cs][0][2], dsr[q][cs][0][3],
+                                 dsr[q][cs][1][0], dsr[q][cs][1][1], dsr[q][cs][1][2], dsr[q][cs][1][3]};
+            s0f[cs] = split8<T>(xs);
+            dsf[cs] = split8<T>(xd);
+        }
+        for (int rb = 0; rb < 4; ++rb) {
             // dQ[i][f] = gamma_i (dO S_0^T)[i][f] + (dP .* D) K
+            {
+                floatx4 acc = zero4();
 #pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs)
-                acc = mma(frag_rows(dOs, OP, 16 * rb, 32 * cs), split_rows_glob<T>(S0, DV, 16 * fb, 32 * cs), acc);
+                for (int cs = 0; cs < NCS; ++cs)
+                    acc = mma(frag_rows(dOs, OP, 16 * rb, 32 * cs), s0f[cs], acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                acc[r] *= tab[TAB_G + 16 * rb + 4 * g + r];
+                for (int r = 0; r < 4; ++r)
+                    acc[r] *= tab[TAB_G + 16 * rb + 4 * g + r];
+                for (int js = 0; js <= rb / 2; ++js)
+                    acc = mma(split_rows_f32<T>(dPs, AP, 16 * rb, 32 * js), frag_cols(Ks, QP, 16 * fb, 32 * js), acc);
 #pragma unroll
-            for (int js = 0; js <= rb / 2; ++js)
-                acc = mma(split_rows_f32<T>(dPs, AP, 16 * rb, 32 * js), frag_cols(Ks, QP, 16 * fb, 32 * js), acc);
-            OT* out = dQo.head(b, h) + tok0 * dQo.st;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out[(16 * rb + 4 * g + r) * dQo.st + 16 * fb + t] = (OT)acc[r];
-        } else {
+                for (int r = 0; r < 4; ++r)
+                    outq[(16 * rb + 4 * g + r) * dQo.st + 16 * fb + t] = (OT)acc[r];
+            }
             // dK[j][f]: five terms with different row factors
-            floatx4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4();
+            {
+                floatx4 acc = zero4(), a1 = zero4(), a2 = zero4(), a3 = zero4();
+                for (int is = rb / 2; is < 2; ++is) {
+                    // (dP .* D)^T Q  and  M^T (beta .* K)    (i >= j)
+                    acc = mma(split_cols_f32<T>(dPs, AP, 16 * rb, 32 * is), frag_cols(Qs, QP, 16 * fb, 32 * is), acc);
+                    float bf[8];
 #pragma unroll
-            for (int is = rb / 2; is < 2; ++is) {
-                // (dP .* D)^T Q  and  M^T (beta .* K)    (i >= j)
-                acc = mma(split_cols_f32<T>(dPs, AP, 16 * rb, 32 * is), frag_cols(Qs, QP, 16 * fb, 32 * is), acc);
-                float bf[8];
+                    for (int r = 0; r < 8; ++r)
+                        bf[r] = bet[32 * is + 8 * g + r];
+                    acc = mma(split_cols_f32<T>(Ms, AP, 16 * rb, 32 * is),
+                              split_scaled<T>(frag_cols(Ks, QP, 16 * fb, 32 * is), bf), acc);
+                }
+                for (int is = 0; is <= rb / 2; ++is)   // M K  (i < j)
+                    a3 = mma(split_rows_f32<T>(Ms, AP, 16 * rb, 32 * is), frag_cols(Ks, QP, 16 * fb, 32 * is), a3);
 #pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    bf[r] = bet[32 * is + 8 * g + r];
-                acc = mma(split_cols_f32<T>(Ms, AP, 16 * rb, 32 * is),
-                          split_scaled<T>(frag_cols(Ks, QP, 16 * fb, 32 * is), bf), acc);
+                for (int cs = 0; cs < NCS; ++cs) {
+                    a1 = mma(split_rows_f32<T>(Us, UP, 16 * rb, 32 * cs), dsf[cs], a1);
+                    a2 = mma(split_rows_f32<T>(Ys, UP, 16 * rb, 32 * cs), s0f[cs], a2);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * rb + 4 * g + r;
+                    acc[r] += tab[TAB_F + j] * a1[r] - bet[j] * tab[TAB_G + j] * a2[r] + bet[j] * a3[r];
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    outk[(16 * rb + 4 * g + r) * dKo.st + 16 * fb + t] = (OT)acc[r];
             }
-#pragma unroll
-            for (int is = 0; is <= rb / 2; ++is)   // M K  (i < j)
-                a3 = mma(split_rows_f32<T>(Ms, AP, 16 * rb, 32 * is), frag_cols(Ks, QP, 16 * fb, 32 * is), a3);
-#pragma unroll
-            for (int cs = 0; cs < DV / 32; ++cs) {
-                a1 = mma(split_rows_f32<T>(Us, UP, 16 * rb, 32 * cs), split_rows_glob<T>(dSC, DV, 16 * fb, 32 * cs), a1);
-                a2 = mma(split_rows_glob<T>(yc, DV, 16 * rb, 32 * cs), split_rows_glob<T>(S0, DV, 16 * fb, 32 * cs), a2);
-            }
-            (void)a4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * rb + 4 * g + r;
-                acc[r] += tab[TAB_F + j] * a1[r] - bet[j] * tab[TAB_G + j] * a2[r] + bet[j] * a3[r];
-            }
-            OT* out = dKo.head(b, h) + tok0 * dKo.st;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                out[(16 * rb + 4 * g + r) * dKo.st + 16 * fb + t] = (OT)acc[r];
         }
     }
 }
@@ -905,13 +1020,13 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, (const float*)s.s0,
+                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), (const float*)s.tabs, (const float*)s.s0,
                   (const float*)s.u, s.tm, s.duy, Act<OT>{(OT*)s.dv_.ptr, s.dv_.sb, s.dv_.sh, s.dv_.st},
                   Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), dec,
+                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), (const float*)s.tabs,
                   (const float*)s.s0, (const float*)s.dsc, (const float*)s.u, (const float*)s.duy,
                   (const float*)s.tm, Act<OT>{(OT*)s.dq.ptr, s.dq.sb, s.dq.sh, s.dq.st},
                   Act<OT>{(OT*)s.dk_.ptr, s.dk_.sb, s.dk_.sh, s.dk_.st}, s.H);

@@ -225,6 +225,38 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
     }
 }
 
+// Eight consecutive values of one row of an activation in global memory,
+// as a fragment (frag_rows() layout: lane (g, t) holds row t, columns 8g ..).
+template <typename T>
+struct RowFrag;
+template <>
+struct RowFrag<bf16> {
+    u32x4 v;
+    __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ Frag<bf16> frag() const
+    {
+        Frag<bf16> f;
+        f.v = __builtin_bit_cast(bf16x8, v);
+        return f;
+    }
+};
+template <>
+struct RowFrag<float> {
+    floatx4 a, b;
+    __device__ __forceinline__ void load(const float* p)
+    {
+        a = *reinterpret_cast<const floatx4*>(p);
+        b = *reinterpret_cast<const floatx4*>(p + 4);
+    }
+    __device__ __forceinline__ Frag<float> frag() const
+    {
+        Frag<float> f;
+        f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+        f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+        return f;
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Workgroup -> (column block, head, batch) for the serial kernels, whose
 // d_v / 16 column workgroups of one head all read that head's chunk operands
@@ -274,12 +306,7 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     static_assert(FPW >= 1 && FPW * NW == NFB, "d_k must be 64 or 128");
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD;
-    constexpr int WP = DK + 4, CP = 16 + 4, PP = CHUNK + 4;   // fp32 pitches
-    __shared__ __align__(16) T Qs[CHUNK * QP];
     __shared__ __align__(16) T Ks[CHUNK * QP];
-    __shared__ __align__(16) float Wks[CHUNK * WP];
-    __shared__ __align__(16) float Wvs[CHUNK * CP];
-    __shared__ __align__(16) float Ps[CHUNK * PP];
     // the state and U as bf16 hi/lo planes, transposed ([column][f] and
     // [column][token]), so that every product reads them with 16-byte reads
     constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
@@ -301,56 +328,58 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             S[q][r] = S_in ? S_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t]
                            : 0.f;
 
-    const T* qh = Q.head(b, h);
     const T* kh = K.head(b, h);
-    const float* wkh = Wk.head(b, h);
-    const float* wvh = Wv.head(b, h);
-    const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
+    // Row operands of this wave's 16 tokens go from global memory straight
+    // into the registers of the products that take them: W_k (rows of U's
+    // A operand), W_v (U's result-tile entries), Q and P (the output's B
+    // operands), lane (g, t) holding row 16 w + t, columns 8g .. 8g + 7 of
+    // each k32 step.  Each is reloaded for the next chunk as soon as the
+    // current chunk's products have taken it.  K, which every wave reads
+    // transposed, and the decay tables are staged through LDS, loaded a
+    // chunk ahead.
+    const T* qrow = Q.head(b, h) + (int64_t)(16 * w + t) * Q.st + 8 * g;
+    const float* wkrow = Wk.head(b, h) + (int64_t)(16 * w + t) * Wk.st + 8 * g;
+    const float* prow = Pm + bh * (int64_t)N * CHUNK * CHUNK + (16 * w + t) * CHUNK + 8 * g;
+    const float* wvh = Wv.head(b, h) + cbase + t;
     const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
-    // the next chunk's Q, K, W_k, this workgroup's W_v columns, P and decay
-    // tables (formed by the prep kernel) are loaded into registers while the
-    // current chunk computes
-    constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
-    static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK, "chunk split");
-    ChunkRegs<T, DK, NT> rq, rk;
-    floatx4 rwk[NWK], rpv[NPV], rwv, rtab = zero4();
-    auto load_next = [&](int64_t tk) {
+    constexpr int NKS = DK / 32;
+    typedef RowFrag<T> QF;
+    floatx4 wk[NKS][2], pv[2][2];
+    float wv[4];
+    QF qv[NKS];
+    auto load_wk_wv = [&](int64_t tk) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            wk[ks][0] = *reinterpret_cast<const floatx4*>(wkrow + tk * Wk.st + 32 * ks);
+            wk[ks][1] = *reinterpret_cast<const floatx4*>(wkrow + tk * Wk.st + 32 * ks + 4);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wv[r] = wvh[(tk + 16 * w + 4 * g + r) * Wv.st];
+    };
+    auto load_q_p = [&](int64_t tk) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qv[ks].load(qrow + tk * Q.st + 32 * ks);
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            pv[js][0] = *reinterpret_cast<const floatx4*>(prow + tk * CHUNK + 32 * js);
+            pv[js][1] = *reinterpret_cast<const floatx4*>(prow + tk * CHUNK + 32 * js + 4);
+        }
+    };
+    ChunkRegs<T, DK, NT> rk;
+    floatx4 rtab = zero4();
+    auto load_k_tab = [&](int64_t tk) {
         if (threadIdx.x < TAB_SIZE / 4)
             rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
-        chunk_load(rq, qh + tk * Q.st, Q.st);
         chunk_load(rk, kh + tk * K.st, K.st);
-#pragma unroll
-        for (int i = 0; i < NWK; ++i) {
-            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            rwk[i] = *reinterpret_cast<const floatx4*>(wkh + (tk + row) * Wk.st + col);
-        }
-        {
-            const int row = threadIdx.x >> 2, col = 4 * (threadIdx.x & 3);
-            rwv = *reinterpret_cast<const floatx4*>(wvh + (tk + row) * Wv.st + cbase + col);
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i)
-            rpv[i] = *reinterpret_cast<const floatx4*>(ph + tk * CHUNK + 4 * (threadIdx.x + NT * i));
     };
-    load_next(0);
+    load_k_tab(0);
+    load_wk_wv(0);
+    load_q_p(0);
     for (int n = 0; n < N; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rq, Qs, QP);
         chunk_store(rk, Ks, QP);
-#pragma unroll
-        for (int i = 0; i < NWK; ++i) {
-            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            *reinterpret_cast<floatx4*>(Wks + row * WP + col) = rwk[i];
-        }
-        {
-            const int row = threadIdx.x >> 2, col = 4 * (threadIdx.x & 3);
-            *reinterpret_cast<floatx4*>(Wvs + row * CP + col) = rwv;
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
-            *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
-        }
         if (threadIdx.x < TAB_SIZE / 4)
             *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
 #pragma unroll
@@ -365,23 +394,27 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
         }
         __syncthreads();
         if (n + 1 < N)
-            load_next(tok0 + CHUNK);
+            load_k_tab(tok0 + CHUNK);
 
         // U rows [16 w, 16 w + 16) = W_v - W_k S_0
         {
             floatx4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(split_rows_f32<T>(Wks, WP, 16 * w, 32 * ks),
-                          frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), acc);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const float x[8] = {wk[ks][0][0], wk[ks][0][1], wk[ks][0][2], wk[ks][0][3],
+                                    wk[ks][1][0], wk[ks][1][1], wk[ks][1][2], wk[ks][1][3]};
+                acc = mma(split8<T>(x), frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), acc);
+            }
             floatx4 u4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * g + r;
-                u4[r] = Wvs[i * CP + t] - acc[r];
-                if (u_out)    // U for the backward, [B][H][T][DV]
-                    u_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
-            }
+            for (int r = 0; r < 4; ++r)
+                u4[r] = wv[r] - acc[r];
+            if (n + 1 < N)
+                load_wk_wv(tok0 + CHUNK);
+            if (u_out)    // U for the backward, [B][H][T][DV]
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    u_out[(bh * (int64_t)N * CHUNK + tok0 + 16 * w + 4 * g + r) * DV + cbase + t] = u4[r];
             put_split4(Usp[0], Usp[1], t * UPP + 16 * w, u4);
         }
         __syncthreads();
@@ -390,14 +423,19 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
         {
             floatx4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mma(frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), frag_rows(Qs, QP, 16 * w, 32 * ks),
-                          acc);
+            for (int ks = 0; ks < NKS; ++ks)
+                acc = mma(frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), qv[ks].frag(), acc);
             acc *= tab[TAB_G + 16 * w + t];
 #pragma unroll
-            for (int js = 0; js <= w / 2; ++js)
-                acc = mma(frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * js), split_rows_f32<T>(Ps, PP, 16 * w, 32 * js),
-                          acc);
+            for (int js = 0; js < 2; ++js) {
+                if (js <= w / 2) {
+                    const float x[8] = {pv[js][0][0], pv[js][0][1], pv[js][0][2], pv[js][0][3],
+                                        pv[js][1][0], pv[js][1][1], pv[js][1][2], pv[js][1][3]};
+                    acc = mma(frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * js), split8<T>(x), acc);
+                }
+            }
+            if (n + 1 < N)
+                load_q_p(tok0 + CHUNK);
             store_tile_t<OT>(O.head(b, h) + tok0 * O.st, O.st, 16 * w, cbase, acc);
         }
         // S <- gamma_C S + K~^T U for this wave's row blocks

@@ -495,12 +495,8 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, OP = 16 + PAD;
-    constexpr int WP = DK + 4, PP = CHUNK + 4;
     __shared__ __align__(16) T Qs[CHUNK * QP];
-    __shared__ __align__(16) T Ks[CHUNK * QP];
     __shared__ __align__(16) T dOs[CHUNK * OP];
-    __shared__ __align__(16) float Wks[CHUNK * WP];
-    __shared__ __align__(16) float Ps[CHUNK * PP];
     // the carried gradient and dU as bf16 hi/lo planes, transposed
     constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
     __shared__ __align__(16) T Gsp[2][16 * SPP];
@@ -522,56 +518,63 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                              : 0.f;
 
     const T* qh = Q.head(b, h);
-    const T* kh = K.head(b, h);
     const T* doh = dO.head(b, h);
-    const float* wkh = Wk.head(b, h);
-    const float* ph = Pm + bh * (int64_t)N * CHUNK * CHUNK;
     const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
-    // the next (earlier) chunk's Q, K, dO columns, W_k, P and decay tables
-    // load into registers while the current chunk computes
+    // Operands only this wave reads go from global memory straight into the
+    // registers of its products, in fragment layout, and are reloaded for
+    // the next (earlier) chunk as soon as the current chunk's products have
+    // taken them: K rows 16 w .. (dU's A operand), P columns 16 w .. (dU's
+    // P^T), and the W_k columns of this wave's feature blocks (the gradient
+    // update's W_k^T).  Q and dO, which every wave reads transposed, and the
+    // decay tables are staged through LDS, a chunk ahead.
+    constexpr int NKS = DK / 32;
+    const T* krow = K.head(b, h) + (int64_t)(16 * w + t) * K.st + 8 * g;
+    const float* pcol = Pm + bh * (int64_t)N * CHUNK * CHUNK + 8 * g * CHUNK + 16 * w + t;
+    const float* wkcol = Wk.head(b, h) + (int64_t)(8 * g) * Wk.st + 16 * FPW * w + t;
+    RowFrag<T> kv[NKS];
+    float pc[2][8], wkc[FPW][2][8];
+    auto load_k_p = [&](int64_t tk) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kv[ks].load(krow + tk * K.st + 32 * ks);
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                pc[js][r] = pcol[tk * CHUNK + (32 * js + r) * CHUNK];
+    };
+    auto load_wk = [&](int64_t tk) {
+#pragma unroll
+        for (int q = 0; q < FPW; ++q)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    wkc[q][ks][r] = wkcol[(tk + 32 * ks + r) * Wk.st + 16 * q];
+    };
     constexpr int VEC = 16 / sizeof(T), PER = 16 / VEC;   // 16-byte vectors per dO slice row
-    constexpr int NWK = CHUNK * DK / 4 / NT, NPV = CHUNK * CHUNK / 4 / NT;
-    static_assert(NWK * NT * 4 == CHUNK * DK && NPV * NT * 4 == CHUNK * CHUNK && CHUNK * PER <= NT,
-                  "chunk split");
-    ChunkRegs<T, DK, NT> rq, rk;
-    floatx4 rwk[NWK], rpv[NPV], rtab = zero4();
+    static_assert(CHUNK * PER <= NT, "chunk split");
+    ChunkRegs<T, DK, NT> rq;
+    floatx4 rtab = zero4();
     u32x4 rdo = {0u, 0u, 0u, 0u};
-    auto load_next = [&](int64_t tk) {
+    auto load_q_do_tab = [&](int64_t tk) {
         if (threadIdx.x < TAB_SIZE / 4)
             rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
         chunk_load(rq, qh + tk * Q.st, Q.st);
-        chunk_load(rk, kh + tk * K.st, K.st);
         if (threadIdx.x < CHUNK * PER) {
             const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
             rdo = *reinterpret_cast<const u32x4*>(doh + (tk + row) * dO.st + cbase + col);
         }
-#pragma unroll
-        for (int i = 0; i < NWK; ++i) {
-            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            rwk[i] = *reinterpret_cast<const floatx4*>(wkh + (tk + row) * Wk.st + col);
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i)
-            rpv[i] = *reinterpret_cast<const floatx4*>(ph + tk * CHUNK + 4 * (threadIdx.x + NT * i));
     };
-    load_next((int64_t)(N - 1) * CHUNK);
+    load_q_do_tab((int64_t)(N - 1) * CHUNK);
+    load_k_p((int64_t)(N - 1) * CHUNK);
+    load_wk((int64_t)(N - 1) * CHUNK);
     for (int n = N - 1; n >= 0; --n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
         chunk_store(rq, Qs, QP);
-        chunk_store(rk, Ks, QP);
         if (threadIdx.x < CHUNK * PER) {
             const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
             *reinterpret_cast<u32x4*>(dOs + row * OP + col) = rdo;
-        }
-#pragma unroll
-        for (int i = 0; i < NWK; ++i) {
-            const int idx = threadIdx.x + NT * i, row = idx / (DK / 4), col = 4 * (idx % (DK / 4));
-            *reinterpret_cast<floatx4*>(Wks + row * WP + col) = rwk[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            const int e = 4 * (threadIdx.x + NT * i), row = e / CHUNK, col = e % CHUNK;
-            *reinterpret_cast<floatx4*>(Ps + row * PP + col) = rpv[i];
         }
         if (threadIdx.x < TAB_SIZE / 4)
             *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
@@ -586,17 +589,20 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
         }
         __syncthreads();
         if (n > 0)
-            load_next(tok0 - CHUNK);
+            load_q_do_tab(tok0 - CHUNK);
 
         // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
         {
             floatx4 acc = zero4(), acc2 = zero4();
-            for (int js = w / 2; js < 2; ++js)
-                acc = mma(split_cols_f32<T>(Ps, PP, 16 * w, 32 * js), frag_cols(dOs, OP, 0, 32 * js), acc);
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc2 = mma(frag_rows(Ks, QP, 16 * w, 32 * ks), frag_rows_split(Gsp[0], Gsp[1], SPP, 0, 32 * ks),
-                           acc2);
+            for (int js = 0; js < 2; ++js)
+                if (js >= w / 2)
+                    acc = mma(split8<T>(pc[js]), frag_cols(dOs, OP, 0, 32 * js), acc);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                acc2 = mma(kv[ks].frag(), frag_rows_split(Gsp[0], Gsp[1], SPP, 0, 32 * ks), acc2);
+            if (n > 0)
+                load_k_p(tok0 - CHUNK);
             floatx4 u4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -621,11 +627,12 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                 for (int ks = 0; ks < CHUNK / 32; ++ks) {
                     acc = mma(split_scaled<T>(frag_cols(Qs, QP, 16 * fb, 32 * ks), qf[ks]),
                               frag_cols(dOs, OP, 0, 32 * ks), acc);
-                    acc2 = mma(split_cols_f32<T>(Wks, WP, 16 * fb, 32 * ks), frag_rows_split(dUsp[0], dUsp[1], UPP, 0, 32 * ks),
-                               acc2);
+                    acc2 = mma(split8<T>(wkc[q][ks]), frag_rows_split(dUsp[0], dUsp[1], UPP, 0, 32 * ks), acc2);
                 }
                 G[q] = gC * G[q] + acc - acc2;
             }
+            if (n > 0)
+                load_wk(tok0 - CHUNK);
         }
         __syncthreads();
     }

@@ -580,29 +580,6 @@ __device__ __forceinline__ Split<T> split_cols_f32(const float* tile, int pitch,
     return split8<T>(x);
 }
 
-// Split operands read straight from fp32 global memory (row stride ld).
-template <typename T>
-__device__ __forceinline__ Split<T> split_rows_glob(const float* base, int64_t ld, int rbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    const float* p = base + (rbase + t) * ld + kbase + 8 * g;
-    const floatx4 a = *reinterpret_cast<const floatx4*>(p);
-    const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    return split8<T>(x);
-}
-
-template <typename T>
-__device__ __forceinline__ Split<T> split_cols_glob(const float* base, int64_t ld, int cbase, int kbase)
-{
-    const int l = lane_id(), t = l & 15, g = l >> 4;
-    float x[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        x[r] = base[(kbase + 8 * g + r) * ld + cbase + t];
-    return split8<T>(x);
-}
-
 // Split fragments read from LDS plane pairs.
 template <typename T>
 __device__ __forceinline__ Split<T> frag_rows_split(const T* hi, const T* lo, int pitch, int rbase, int kbase)

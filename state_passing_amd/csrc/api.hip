@@ -833,29 +833,37 @@ linrec_status linrec_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npie
     return LINREC_OK;
 }
 
+namespace {
+
+// Tokens of a delta-rule piece rounded up to whole chunks: the rows its
+// workspace and saved buffers hold.
+size_t delta_tokens(const linrec_desc* d) { return (size_t)chunks_of(d->T) * kChunk; }
+
+}  // namespace
+
 size_t linrec_delta_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
         return 0;
     // W_k, W_v, then P per chunk (64 x 64 per 64 tokens), then the decay
-    // tables per chunk (256 per 64 tokens)
-    return (size_t)d->B * d->H * (size_t)d->T * (size_t)(d->dk + d->dv + kChunk + 4) * sizeof(float);
+    // tables per chunk (256 per 64 tokens); a partial last chunk counts whole
+    return (size_t)d->B * d->H * (size_t)delta_tokens(d) * (size_t)(d->dk + d->dv + kChunk + 4) * sizeof(float);
 }
 
 size_t linrec_delta_saved_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
         return 0;
-    const size_t bh = (size_t)d->B * d->H;
-    return bh * ((size_t)(d->T / kChunk) * d->dk * d->dv + (size_t)d->T * d->dv) * sizeof(float);
+    const size_t bh = (size_t)d->B * d->H, Tp = delta_tokens(d);
+    return bh * (Tp / kChunk * d->dk * d->dv + Tp * d->dv) * sizeof(float);
 }
 
 size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
 {
-    if (check_desc(d) != LINREC_OK || d->dk != d->dv || d->T % kChunk != 0)
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv)
         return 0;
-    const size_t bh = (size_t)d->B * d->H, N = (size_t)(d->T / kChunk);
-    return bh * ((size_t)d->T * (d->dk + 2 * d->dv + kChunk + 4) + N * kChunk * kChunk + N * d->dk * d->dv) *
+    const size_t bh = (size_t)d->B * d->H, Tp = delta_tokens(d), N = Tp / kChunk;
+    return bh * (Tp * (d->dk + 2 * d->dv + kChunk + 4) + N * kChunk * kChunk + N * d->dk * d->dv) *
            sizeof(float);
 }
 
@@ -882,7 +890,7 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
     if (st != LINREC_OK)
         return st;
-    if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
+    if (d->dk != d->dv)
         return LINREC_E_SHAPE;
     if (d->T > 0 && (st = check_beta(beta)) != LINREC_OK)
         return st;
@@ -900,13 +908,14 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
     s.decay_kind = d->decay;
     s.S_in = S_in;
     s.S_out = S_out;
+    const size_t bh = (size_t)d->B * d->H, Tp = delta_tokens(d);
     s.wk = (float*)workspace;
-    s.wv = (float*)workspace + (size_t)d->B * d->H * (size_t)d->T * d->dk;
-    s.pm = s.wv + (size_t)d->B * d->H * (size_t)d->T * d->dv;
-    s.tabs = s.pm + (size_t)d->B * d->H * (size_t)d->T * kChunk;
+    s.wv = s.wk + bh * Tp * d->dk;
+    s.pm = s.wv + bh * Tp * d->dv;
+    s.tabs = s.pm + bh * Tp * kChunk;
     if (saved) {
         s.s0 = (float*)saved;
-        s.u = (float*)saved + (size_t)d->B * d->H * (size_t)(d->T / kChunk) * d->dk * d->dv;
+        s.u = (float*)saved + bh * (Tp / kChunk) * d->dk * d->dv;
     }
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_FWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_fwd(s, (hipStream_t)stream); }));
@@ -924,7 +933,7 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
                                       workspace);
     if (st != LINREC_OK)
         return st;
-    if (d->dk != d->dv || d->T % kChunk != 0)   // the delta rule takes whole chunks
+    if (d->dk != d->dv)
         return LINREC_E_SHAPE;
     if (d->T > 0 && ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK))
         return st;
@@ -932,7 +941,8 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
         return st;
     if (d->T == 0)
         return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, (hipStream_t)stream);
-    const size_t bh = (size_t)d->B * d->H, T = (size_t)d->T, N = T / kChunk;
+    // workspace and saved rows cover whole chunks; the last may be partial
+    const size_t bh = (size_t)d->B * d->H, T = delta_tokens(d), N = T / kChunk;
     linrec::DeltaBwdLaunch s{};
     s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
     s.B = d->B; s.H = d->H; s.T = d->T;

@@ -65,13 +65,13 @@ __device__ __forceinline__ floatx4 mm16_f32_reg(const float* X, int xp, floatx4 
 // Per chunk: T = (I + A)^{-1}, then W_v, W_k (fp32, [B][H][T][d]).
 // Workgroup = (chunk, h, b), 4 waves.
 // ---------------------------------------------------------------------------
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<const T> K, Act<const T> V,
                                                          Act<const float> beta, DecayArg dec,
                                                          Act<float> Wk, Act<float> Wv,
                                                          float* __restrict__ Pout,
                                                          float* __restrict__ Tout,
-                                                         float* __restrict__ TabOut, int H)
+                                                         float* __restrict__ TabOut, int H, int tail)
 {
     constexpr int NT = 256, NW = 4;
     constexpr int PAD = Pad<T>::value;
@@ -93,25 +93,29 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<con
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t tok0 = (int64_t)n * CHUNK;
+    // the piece's last chunk may hold fewer tokens: the rows past them enter
+    // as zeros (q, k, v) with beta = 0 and decay 1, so that they add nothing
+    // to T, W, P or the state, and nothing is written for them but zeros
+    const int rows = RAGGED && n == (int)gridDim.x - 1 ? tail : CHUNK;
     {
         // the gate and beta first: their use waits on nothing else
         float raw = 0.f, bt = 0.f;
         if (w == 0) {
-            raw = decay_raw(dec, b, h, tok0);
-            bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + l) * beta.st];
+            raw = decay_raw(dec, b, h, tok0, rows);
+            bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + (RAGGED ? min(l, rows - 1) : l)) * beta.st];
         }
         ChunkRegs<T, DK, NT> rq, rk;
         ChunkRegs<T, DV, NT> rv;
-        chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
-        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
-        chunk_load(rv, V.head(b, h) + tok0 * V.st, V.st);
+        chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st, rows);
+        chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st, rows);
+        chunk_load(rv, V.head(b, h) + tok0 * V.st, V.st, rows);
         if (w == 0) {
-            decay_tables(dec, raw, tab);
-            bet[l] = bt;
+            decay_tables(dec, raw, tab, rows);
+            bet[l] = !RAGGED || l < rows ? bt : 0.f;
         }
-        chunk_store(rq, Qs, KP);
-        chunk_store(rk, Ks, KP);
-        chunk_store(rv, Vs, VP);
+        chunk_store(rq, Qs, KP, rows);
+        chunk_store(rk, Ks, KP, rows);
+        chunk_store(rv, Vs, VP, rows);
     }
     __syncthreads();
     // the chunk's decay tables for the serial kernels, [B][H][N][TAB_SIZE]
@@ -292,7 +296,7 @@ __device__ __forceinline__ ColHead xcd_col_head(int H, int B)
 //   O^T = gamma .* (S_0^T Q^T) + U^T P^T   (stored transposed: 4 features a lane)
 //   S <- gamma_C S + (K .* gamma_C/gamma)^T U
 // ---------------------------------------------------------------------------
-template <typename T, typename OT, int DK, int DV>
+template <typename T, typename OT, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
                                                          Act<const float> Wk, Act<const float> Wv,
                                                          const float* __restrict__ Pm,
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
                                                          const float* S_in,
                                                          float* S_out, Act<OT> O,
                                                          float* __restrict__ s0_out,
-                                                         float* __restrict__ u_out, int H, int N)
+                                                         float* __restrict__ u_out, int H, int N, int tail)
 {
     constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
     static_assert(FPW >= 1 && FPW * NW == NFB, "d_k must be 64 or 128");
@@ -337,7 +341,11 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     // current chunk's products have taken it.  K, which every wave reads
     // transposed, and the decay tables are staged through LDS, loaded a
     // chunk ahead.
-    const T* qrow = Q.head(b, h) + (int64_t)(16 * w + t) * Q.st + 8 * g;
+    // the last chunk may be partial (tail tokens): its row reads are clamped
+    // to the last token; K's padded rows are zeroed in LDS, the prep
+    // kernel's operands are zero there, and no output is stored for them
+    auto rows_of = [&](int64_t tk) { return RAGGED && tk / CHUNK == N - 1 ? tail : CHUNK; };
+    const T* qh = Q.head(b, h);
     const float* wkrow = Wk.head(b, h) + (int64_t)(16 * w + t) * Wk.st + 8 * g;
     const float* prow = Pm + bh * (int64_t)N * CHUNK * CHUNK + (16 * w + t) * CHUNK + 8 * g;
     const float* wvh = Wv.head(b, h) + cbase + t;
@@ -358,9 +366,10 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             wv[r] = wvh[(tk + 16 * w + 4 * g + r) * Wv.st];
     };
     auto load_q_p = [&](int64_t tk) {
+        const T* qrow = qh + (tk + (RAGGED ? min(16 * w + t, rows_of(tk) - 1) : 16 * w + t)) * Q.st + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            qv[ks].load(qrow + tk * Q.st + 32 * ks);
+            qv[ks].load(qrow + 32 * ks);
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
             pv[js][0] = *reinterpret_cast<const floatx4*>(prow + tk * CHUNK + 32 * js);
@@ -372,14 +381,15 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
     auto load_k_tab = [&](int64_t tk) {
         if (threadIdx.x < TAB_SIZE / 4)
             rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
-        chunk_load(rk, kh + tk * K.st, K.st);
+        chunk_load(rk, kh + tk * K.st, K.st, rows_of(tk));
     };
     load_k_tab(0);
     load_wk_wv(0);
     load_q_p(0);
     for (int n = 0; n < N; ++n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rk, Ks, QP);
+        const int rows_n = rows_of(tok0);
+        chunk_store(rk, Ks, QP, rows_n);
         if (threadIdx.x < TAB_SIZE / 4)
             *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
 #pragma unroll
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             }
             if (n + 1 < N)
                 load_q_p(tok0 + CHUNK);
-            store_tile_t<OT>(O.head(b, h) + tok0 * O.st, O.st, 16 * w, cbase, acc);
+            store_tile_t<OT>(O.head(b, h) + tok0 * O.st, O.st, 16 * w, cbase, acc, rows_n);
         }
         // S <- gamma_C S + K~^T U for this wave's row blocks
         {
@@ -483,14 +493,14 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
 // columns [16 cb, 16 cb + 16), 4 waves as in delta_scan_kernel.  Writes dU
 // ([B][H][T][DV] fp32), the gradient leaving every chunk (dS_C, per chunk
 // [B][H][N][DK][DV]) and dS_in.
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
                                                           Act<const T> dO, Act<const float> Wk,
                                                           const float* __restrict__ Pm,
                                                           const float* __restrict__ tabs,
                                                           const float* dS_out,
                                                           float* dS_in, float* __restrict__ dU_out,
-                                                          float* __restrict__ dsc_out, int H, int N)
+                                                          float* __restrict__ dsc_out, int H, int N, int tail)
 {
     constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
     constexpr int PAD = Pad<T>::value;
@@ -528,15 +538,20 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     // update's W_k^T).  Q and dO, which every wave reads transposed, and the
     // decay tables are staged through LDS, a chunk ahead.
     constexpr int NKS = DK / 32;
-    const T* krow = K.head(b, h) + (int64_t)(16 * w + t) * K.st + 8 * g;
+    // the last chunk may be partial (tail tokens): row reads are clamped to
+    // its last token, Q and dO are zeroed past it in LDS, and dU is zero
+    // there (the prep kernel's W_k and P are zero for those tokens)
+    auto rows_of = [&](int64_t tk) { return RAGGED && tk / CHUNK == N - 1 ? tail : CHUNK; };
+    const T* kh = K.head(b, h);
     const float* pcol = Pm + bh * (int64_t)N * CHUNK * CHUNK + 8 * g * CHUNK + 16 * w + t;
     const float* wkcol = Wk.head(b, h) + (int64_t)(8 * g) * Wk.st + 16 * FPW * w + t;
     RowFrag<T> kv[NKS];
     float pc[2][8], wkc[FPW][2][8];
     auto load_k_p = [&](int64_t tk) {
+        const T* krow = kh + (tk + (RAGGED ? min(16 * w + t, rows_of(tk) - 1) : 16 * w + t)) * K.st + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            kv[ks].load(krow + tk * K.st + 32 * ks);
+            kv[ks].load(krow + 32 * ks);
 #pragma unroll
         for (int js = 0; js < 2; ++js)
 #pragma unroll
@@ -560,9 +575,10 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     auto load_q_do_tab = [&](int64_t tk) {
         if (threadIdx.x < TAB_SIZE / 4)
             rtab = *reinterpret_cast<const floatx4*>(th + tk / CHUNK * TAB_SIZE + 4 * threadIdx.x);
-        chunk_load(rq, qh + tk * Q.st, Q.st);
+        chunk_load(rq, qh + tk * Q.st, Q.st, rows_of(tk));
         if (threadIdx.x < CHUNK * PER) {
-            const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
+            const int row = RAGGED ? min((int)threadIdx.x / PER, rows_of(tk) - 1) : (int)threadIdx.x / PER;
+            const int col = VEC * (threadIdx.x % PER);
             rdo = *reinterpret_cast<const u32x4*>(doh + (tk + row) * dO.st + cbase + col);
         }
     };
@@ -571,10 +587,11 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
     load_wk((int64_t)(N - 1) * CHUNK);
     for (int n = N - 1; n >= 0; --n) {
         const int64_t tok0 = (int64_t)n * CHUNK;
-        chunk_store(rq, Qs, QP);
+        const int rows_n = rows_of(tok0);
+        chunk_store(rq, Qs, QP, rows_n);
         if (threadIdx.x < CHUNK * PER) {
             const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
-            *reinterpret_cast<u32x4*>(dOs + row * OP + col) = rdo;
+            *reinterpret_cast<u32x4*>(dOs + row * OP + col) = !RAGGED || row < rows_n ? rdo : u32x4{0u, 0u, 0u, 0u};
         }
         if (threadIdx.x < TAB_SIZE / 4)
             *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
@@ -607,7 +624,7 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r;
-                u4[r] = acc[r] + tab[TAB_F + i] * acc2[r];
+                u4[r] = !RAGGED || i < rows_n ? acc[r] + tab[TAB_F + i] * acc2[r] : 0.f;
                 dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
             }
             put_split4(dUsp[0], dUsp[1], t * UPP + 16 * w, u4);
@@ -646,14 +663,14 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
 // Per chunk, first part: Y = T^T dU (written over dU), dV, M (written over
 // T) and dbeta.  Workgroup = (chunk, h, b), 4 waves; wave w owns token rows
 // [16 w, 16 w + 16) of Y, dV, M and dbeta (no reduction crosses waves).
-template <typename T, typename OT, int DK, int DV>
+template <typename T, typename OT, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<const T> V,
                                                            Act<const float> beta,
                                                            const float* __restrict__ tabs,
                                                            const float* __restrict__ s0,
                                                            const float* __restrict__ u,
                                                            float* __restrict__ Tm, float* __restrict__ dUY,
-                                                           Act<OT> dVo, Act<float> dbeta, int H)
+                                                           Act<OT> dVo, Act<float> dbeta, int H, int tail)
 {
     constexpr int NT = 256;
     constexpr int PAD = Pad<T>::value;
@@ -686,6 +703,9 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
     float* yc = dUY + (bh * (int64_t)N * CHUNK + tok0) * DV;
     const T* vh = V.head(b, h) + tok0 * V.st;
+    // the last chunk may be partial: reads stay on its tokens, K and beta
+    // are zero past them, and nothing is stored for them but workspace rows
+    const int rows = RAGGED && n == N - 1 ? tail : CHUNK;
 
     // every global read of the kernel but S_0 is issued here, together:
     // beta, the decay tables, K, T, dU, U, and this lane's V values
@@ -694,11 +714,11 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     float bt = 0.f;
     floatx4 rtab = zero4(), rt[NTV], rdu[NUV], ru[NUV];
     if (threadIdx.x < CHUNK)
-        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + threadIdx.x) * beta.st];
+        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + (RAGGED ? min((int)threadIdx.x, rows - 1) : (int)threadIdx.x)) * beta.st];
     if (threadIdx.x < TAB_SIZE / 4)
         rtab = *reinterpret_cast<const floatx4*>(tabs + (bh * N + n) * TAB_SIZE + 4 * threadIdx.x);
     ChunkRegs<T, DK, NT> rk;
-    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
+    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st, rows);
 #pragma unroll
     for (int i = 0; i < NTV; ++i)
         rt[i] = *reinterpret_cast<const floatx4*>(Tc + 4 * (threadIdx.x + NT * i));
@@ -712,13 +732,13 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     for (int cb = 0; cb < DV / 16; ++cb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            vv[cb][r] = (float)vh[(16 * w + 4 * g + r) * V.st + 16 * cb + t];
+            vv[cb][r] = (float)vh[(RAGGED ? min(16 * w + 4 * g + r, rows - 1) : 16 * w + 4 * g + r) * V.st + 16 * cb + t];
 
     if (threadIdx.x < CHUNK)
-        bet[threadIdx.x] = bt;
+        bet[threadIdx.x] = !RAGGED || (int)threadIdx.x < rows ? bt : 0.f;
     if (threadIdx.x < TAB_SIZE / 4)
         *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
-    chunk_store(rk, Ks, KP);
+    chunk_store(rk, Ks, KP, rows);
 #pragma unroll
     for (int i = 0; i < NTV; ++i) {
         const int e = 4 * (threadIdx.x + NT * i);
@@ -750,7 +770,8 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * w + 4 * g + r, c = 16 * cb + t;
                 yc[i * DV + c] = Y[cb][r];
-                dvh[i * dVo.st + c] = (OT)(bet[i] * Y[cb][r]);
+                if (!RAGGED || i < rows)
+                    dvh[i * dVo.st + c] = (OT)(bet[i] * Y[cb][r]);
             }
     }
     // S_0 (fp32 [f][c]) in result-tile order: lane (g, t) of wave w takes
@@ -832,14 +853,14 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        if (t == 0)
+        if (t == 0 && (!RAGGED || 16 * w + 4 * g + r < rows))
             dbeta.ptr[b * dbeta.sb + h * dbeta.sh + (tok0 + 16 * w + 4 * g + r) * dbeta.st] = x;
     }
 }
 
 // Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), 4 waves;
 // output tiles are spread over the waves.
-template <typename T, typename OT, int DK, int DV>
+template <typename T, typename OT, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
                                                            Act<const float> beta,
                                                            const float* __restrict__ tabs,
@@ -848,7 +869,7 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
                                                            const float* __restrict__ u,
                                                            const float* __restrict__ Y,
                                                            const float* __restrict__ Mg, Act<OT> dQo,
-                                                           Act<OT> dKo, int H)
+                                                           Act<OT> dKo, int H, int tail)
 {
     constexpr int NT = 256, NW = 4;
     constexpr int PAD = Pad<T>::value;
@@ -873,6 +894,9 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
     const float* uc = u + (bh * (int64_t)N * CHUNK + tok0) * DV;
     const float* yc = Y + (bh * (int64_t)N * CHUNK + tok0) * DV;
     const float* Mc = Mg + (bh * N + n) * CHUNK * CHUNK;
+    // the last chunk may be partial: reads stay on its tokens, Q, K, dO and
+    // beta are zero past them, and no gradient is stored for them
+    const int rows = RAGGED && n == N - 1 ? tail : CHUNK;
 
     // Wave w takes the feature blocks fb = w, w + 4, ... of dQ and dK, every
     // row block of each; the rows of S_0 and dS_C it needs (as B operands,
@@ -886,14 +910,14 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
     floatx4 rtab = zero4(), ru[NUV], ry[NUV], rm[NMV];
     floatx4 s0r[FBW][NCS][2], dsr[FBW][NCS][2];
     if (threadIdx.x < CHUNK)
-        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + threadIdx.x) * beta.st];
+        bt = beta.ptr[b * beta.sb + h * beta.sh + (tok0 + (RAGGED ? min((int)threadIdx.x, rows - 1) : (int)threadIdx.x)) * beta.st];
     if (threadIdx.x < TAB_SIZE / 4)
         rtab = *reinterpret_cast<const floatx4*>(tabs + (bh * N + n) * TAB_SIZE + 4 * threadIdx.x);
     ChunkRegs<T, DK, NT> rq, rk;
     ChunkRegs<T, DV, NT> ro;
-    chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st);
-    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st);
-    chunk_load(ro, dO.head(b, h) + tok0 * dO.st, dO.st);
+    chunk_load(rq, Q.head(b, h) + tok0 * Q.st, Q.st, rows);
+    chunk_load(rk, K.head(b, h) + tok0 * K.st, K.st, rows);
+    chunk_load(ro, dO.head(b, h) + tok0 * dO.st, dO.st, rows);
 #pragma unroll
     for (int i = 0; i < NUV; ++i) {
         ru[i] = *reinterpret_cast<const floatx4*>(uc + 4 * (threadIdx.x + NT * i));
@@ -914,12 +938,12 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
         }
 
     if (threadIdx.x < CHUNK)
-        bet[threadIdx.x] = bt;
+        bet[threadIdx.x] = !RAGGED || (int)threadIdx.x < rows ? bt : 0.f;
     if (threadIdx.x < TAB_SIZE / 4)
         *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
-    chunk_store(rq, Qs, QP);
-    chunk_store(rk, Ks, QP);
-    chunk_store(ro, dOs, OP);
+    chunk_store(rq, Qs, QP, rows);
+    chunk_store(rk, Ks, QP, rows);
+    chunk_store(ro, dOs, OP, rows);
 #pragma unroll
     for (int i = 0; i < NUV; ++i) {
         const int e = 4 * (threadIdx.x + NT * i);
@@ -979,7 +1003,8 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
                     acc = mma(split_rows_f32<T>(dPs, AP, 16 * rb, 32 * js), frag_cols(Ks, QP, 16 * fb, 32 * js), acc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    outq[(16 * rb + 4 * g + r) * dQo.st + 16 * fb + t] = (OT)acc[r];
+                    if (!RAGGED || 16 * rb + 4 * g + r < rows)
+                        outq[(16 * rb + 4 * g + r) * dQo.st + 16 * fb + t] = (OT)acc[r];
             }
             // dK[j][f]: five terms with different row factors
             {
@@ -1008,7 +1033,8 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    outk[(16 * rb + 4 * g + r) * dKo.st + 16 * fb + t] = (OT)acc[r];
+                    if (!RAGGED || 16 * rb + 4 * g + r < rows)
+                        outk[(16 * rb + 4 * g + r) * dKo.st + 16 * fb + t] = (OT)acc[r];
             }
         }
     }
@@ -1026,56 +1052,62 @@ template <typename T, typename OT, int DK, int DV>
 hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
 {
     const DecayArg dec{(const float*)s.decay.ptr, s.decay.sb, s.decay.sh, s.decay.st, s.decay_kind};
-    const Act<float> wk{s.wk, (int64_t)s.H * s.T * DK, (int64_t)s.T * DK, DK};
-    const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
-    const int N = s.T / CHUNK;
-    launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                  nullptr, s.tabs, s.H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    launch_kernel((delta_scan_kernel<T, OT, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256),
-                  stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
-                  Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, (const float*)s.tabs,
-                  s.S_in, s.S_out,
-                  Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N);
-    return hipGetLastError();
+    // workspace rows cover whole chunks (Tp tokens); the last may be partial
+    const int N = (s.T + CHUNK - 1) / CHUNK, tail = s.T - (N - 1) * CHUNK;
+    const int64_t Tp = (int64_t)N * CHUNK;
+    const Act<float> wk{s.wk, (int64_t)s.H * Tp * DK, Tp * DK, DK};
+    const Act<float> wv{s.wv, (int64_t)s.H * Tp * DV, Tp * DV, DV};
+    return with_ragged(tail < CHUNK, [&](auto rg) {
+        constexpr bool RG = decltype(rg)::value;
+        launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                      nullptr, s.tabs, s.H, tail);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        launch_kernel((delta_scan_kernel<T, OT, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256),
+                      stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
+                      Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, (const float*)s.tabs,
+                      s.S_in, s.S_out, Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N, tail);
+        return hipGetLastError();
+    });
 }
 
 template <typename T, typename OT, int DK, int DV>
 hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
 {
     const DecayArg dec{(const float*)s.decay.ptr, s.decay.sb, s.decay.sh, s.decay.st, s.decay_kind};
-    const int N = s.T / CHUNK;
-    const Act<float> wk{s.wk, (int64_t)s.H * s.T * DK, (int64_t)s.T * DK, DK};
-    const Act<float> wv{s.wv, (int64_t)s.H * s.T * DV, (int64_t)s.T * DV, DV};
-    launch_kernel((delta_prep_kernel<T, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                  s.tm, s.tabs, s.H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    launch_kernel((delta_bscan_kernel<T, DK, DV>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
-                  Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, (const float*)s.tabs,
-                  s.dS_out,
-                  s.dS_in, s.duy,
-                  s.dsc, s.H, N);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), (const float*)s.tabs, (const float*)s.s0,
-                  (const float*)s.u, s.tm, s.duy, Act<OT>{(OT*)s.dv_.ptr, s.dv_.sb, s.dv_.sh, s.dv_.st},
-                  Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
-    launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV>), dim3(N, s.H, s.B), dim3(256), stream,
-                  dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), (const float*)s.tabs,
-                  (const float*)s.s0, (const float*)s.dsc, (const float*)s.u, (const float*)s.duy,
-                  (const float*)s.tm, Act<OT>{(OT*)s.dq.ptr, s.dq.sb, s.dq.sh, s.dq.st},
-                  Act<OT>{(OT*)s.dk_.ptr, s.dk_.sb, s.dk_.sh, s.dk_.st}, s.H);
-    return hipGetLastError();
+    const int N = (s.T + CHUNK - 1) / CHUNK, tail = s.T - (N - 1) * CHUNK;
+    const int64_t Tp = (int64_t)N * CHUNK;
+    const Act<float> wk{s.wk, (int64_t)s.H * Tp * DK, Tp * DK, DK};
+    const Act<float> wv{s.wv, (int64_t)s.H * Tp * DV, Tp * DV, DV};
+    return with_ragged(tail < CHUNK, [&](auto rg) {
+        constexpr bool RG = decltype(rg)::value;
+        launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                      s.tm, s.tabs, s.H, tail);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        launch_kernel((delta_bscan_kernel<T, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
+                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
+                      Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, (const float*)s.tabs,
+                      s.dS_out, s.dS_in, s.duy, s.dsc, s.H, N, tail);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                      dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), (const float*)s.tabs, (const float*)s.s0,
+                      (const float*)s.u, s.tm, s.duy, Act<OT>{(OT*)s.dv_.ptr, s.dv_.sb, s.dv_.sh, s.dv_.st},
+                      Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H, tail);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), (const float*)s.tabs,
+                      (const float*)s.s0, (const float*)s.dsc, (const float*)s.u, (const float*)s.duy,
+                      (const float*)s.tm, Act<OT>{(OT*)s.dq.ptr, s.dq.sb, s.dq.sh, s.dq.st},
+                      Act<OT>{(OT*)s.dk_.ptr, s.dk_.sb, s.dk_.sh, s.dk_.st}, s.H, tail);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace

@@ -848,14 +848,6 @@ DecayArg decay_arg(const TensorArg& d, int kind)
     return DecayArg{(const float*)d.ptr, d.sb, d.sh, d.st, kind};
 }
 
-// Calls f with std::integral_constant<bool, ragged>: the kernels with the
-// masking of a partial last chunk are instantiated apart, so pieces of whole
-// chunks run code without it.
-template <typename F>
-hipError_t with_ragged(bool ragged, F&& f)
-{
-    return ragged ? f(std::integral_constant<bool, true>{}) : f(std::integral_constant<bool, false>{});
-}
 
 template <typename T, typename OT, int DK, int DV>
 hipError_t sum_impl(const ScanLaunch& s, hipStream_t stream)

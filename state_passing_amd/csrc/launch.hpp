@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace linrec {
 
 // Per-kernel timing.  When `stop` is set, the kernels launched on this thread
@@ -22,6 +24,15 @@ inline LaunchStamps& launch_stamps()
 {
     static thread_local LaunchStamps s;
     return s;
+}
+
+// Calls f with std::integral_constant<bool, ragged>: the kernels with the
+// masking of a partial last chunk are instantiated apart, so pieces of whole
+// chunks run code without it.
+template <typename F>
+inline hipError_t with_ragged(bool ragged, F&& f)
+{
+    return ragged ? f(std::integral_constant<bool, true>{}) : f(std::integral_constant<bool, false>{});
 }
 
 // Every kernel of the library is launched through here (no dynamic LDS).

@@ -254,7 +254,10 @@ def test_delta_arguments():
     # W_k and W_v per token, then P (64 x 64) and the decay tables (256) per chunk
     assert linrec.delta_workspace_bytes(d()) == 16 * 4096 * (256 + 64 + 4) * 4
     assert linrec.delta_workspace_bytes(d(dk=64)) == 0        # d_k != d_v
-    assert linrec.delta_workspace_bytes(d(T=100)) == 0
+    # a partial last chunk counts whole
+    assert linrec.delta_workspace_bytes(d(T=100)) == 16 * 128 * (256 + 64 + 4) * 4
+    assert linrec.delta_saved_bytes(d(T=100)) == linrec.delta_saved_bytes(d(T=128))
+    assert linrec.delta_bwd_workspace_bytes(d(T=100)) == linrec.delta_bwd_workspace_bytes(d(T=128))
 
     def call(desc, beta=linrec.Tensor(FAKE, 16 * 4096, 4096, 1), ws=FAKE, saved=None):
         return lib.linrec_delta_fwd(None, ctypes.byref(desc), act(), act(), act(), beta,

@@ -170,3 +170,43 @@ def test_delta_gated_16k_sampled_heads():
     print(f"[{wl.name} {len(wl.pieces())} pieces] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
           flush=True)
     assert all(v <= TOL[wl.dtype] for v in errs.values()), errs
+
+
+RAGGED = [
+    small("delta-one-token", 1, 2, 1, 128, "bf16", "token", s_in=0.1),
+    small("delta-ragged-100", 1, 2, 100, 128, "bf16", "token", s_in=0.1),
+    small("delta-ragged-333-head", 2, 2, 333, 128, "bf16", "head"),
+    small("delta-ragged-200-64", 1, 3, 200, 64, "bf16", "token", s_in=0.1),
+    small("delta-ragged-130-f32", 1, 2, 130, 64, "f32", "token", s_in=0.1),
+]
+
+
+@pytest.mark.parametrize("wl", RAGGED, ids=[w.name for w in RAGGED])
+def test_delta_ragged(wl):
+    """Lengths that are not whole chunks: the piece's last chunk holds 1..63
+    tokens.  Forward and backward against the oracle, as one piece and as
+    pieces that end mid-chunk; outputs past the last token are untouched."""
+    print(f"case {wl}", flush=True)
+    inp = to_dev(make_inputs(wl, device="cpu", seed=12, with_dS_out=True))
+    ref = oracle_delta(inp, backward=True)
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    splits = [[wl.T]]
+    if wl.T >= 100:
+        splits.append([37, wl.T - 37 - 50, 50])
+    for lens in splits:
+        errs = errors(run_pieces(inp, lens, backward=True), ref, heads)
+        print(f"[{wl.name} pieces {lens}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+              flush=True)
+        assert all(v <= TOL[wl.dtype] for v in errs.values()), errs
+    # nothing is written past the piece: views into longer buffers keep their fill
+    T, fill = wl.T, 7.0
+    o = torch.full((wl.B, wl.H, T + 64, wl.dv), fill, dtype=torch.float32, device=DEV)
+    dq = torch.full((wl.B, wl.H, T + 64, wl.dk), fill, dtype=torch.float32, device=DEV)
+    db = torch.full((wl.B, wl.H, T + 64), fill, dtype=torch.float32, device=DEV)
+    _, _, sv = linrec.delta_fwd(inp.q, inp.k, inp.v, inp.beta, inp.decay, inp.S_in, o=o[:, :, :T],
+                                save=True)
+    linrec.delta_bwd(inp.q, inp.k, inp.v, inp.beta, inp.decay, sv, inp.dO, inp.dS_out,
+                     dq=dq[:, :, :T], dbeta=db[:, :, :T], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool((o[:, :, T:] == fill).all()) and bool((dq[:, :, T:] == fill).all())
+    assert bool((db[:, :, T:] == fill).all())

@@ -62,7 +62,7 @@
  *   chunk == 64; 0 <= T <= LINREC_MAX_T (the last chunk of a piece may be
  *   partial: its missing tokens are neither read nor written; the
  *   delta-rule buffers count it whole); d_k, d_v in {64, 128};
- *   1 <= B, H <= 65535.  Offsets into every tensor are 64-bit, so a tensor
+ *   1 <= B <= 32767, 1 <= H <= 65535.  Offsets into every tensor are 64-bit, so a tensor
  *   may hold more than 2^31 elements (one head's T * d included).  Activation
  *   pointers and their strides sb, sh, st must keep every token row 16-byte
  *   aligned.

@@ -75,7 +75,9 @@ linrec_status check_desc(const linrec_desc* d)
         return LINREC_E_NULL;
     if (d->dtype != LINREC_BF16 && d->dtype != LINREC_F32)
         return LINREC_E_DTYPE;
-    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 65535 || d->H > 65535 || d->T < 0 ||
+    // B: the sequence backward's launches carry another piece's segment sums
+    // as a second set of grid rows z, so 2 B must fit the grid's 65535
+    if (d->chunk != kChunk || d->B < 1 || d->H < 1 || d->B > 32767 || d->H > 65535 || d->T < 0 ||
         d->T > LINREC_MAX_T)
         return LINREC_E_SHAPE;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))

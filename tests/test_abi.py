@@ -126,6 +126,10 @@ E = {v: k for k, v in linrec.STATUS.items()}
     (d(T=100), "LINREC_E_NULL"),           # a ragged length is valid; no context
     (d(dk=96), "LINREC_E_SHAPE"),
     (d(B=0), "LINREC_E_SHAPE"),
+    (d(B=32767), "LINREC_E_NULL"),         # the largest batch; no context
+    (d(B=32768), "LINREC_E_SHAPE"),
+    (d(H=65535), "LINREC_E_NULL"),
+    (d(H=65536), "LINREC_E_SHAPE"),
     (d(H=0), "LINREC_E_SHAPE"),
     (d(dtype=5), "LINREC_E_DTYPE"),
     (d(dtype=linrec.F32), "LINREC_E_DTYPE"),

@@ -82,7 +82,7 @@ def _lib():
         return _LIB
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
-                           "(python -c 'import __graft_entry__ as g; g.build()')")
+                           "(python -m state_passing_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
     P, T, D = ctypes.c_void_p, Tensor, ctypes.POINTER(Desc)
     I32 = ctypes.c_int32

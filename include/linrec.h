@@ -171,7 +171,10 @@ size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int3
  *   q, k: [B,H,T,d_k];  v, o: [B,H,T,d_v];  decay per d->decay.
  *   S_in: fp32 [B,H,d_k,d_v] or NULL (zeros).  S_out: fp32, required.
  *   states: required (linrec_states_bytes(d) bytes); pass it unmodified to
- *   linrec_bwd for the same piece.
+ *   linrec_bwd for the same piece.  The forward itself runs through it (the
+ *   state entering every 256-token segment is formed there, then read by
+ *   the output kernel), so a forward-only caller passes it too and may
+ *   reuse one buffer for every piece.
  * Reference: the recurrence above (Sequence Accumulation and Beyond,
  * "Approach"; StateFlow, Abstract). */
 linrec_status linrec_fwd(linrec_ctx* ctx, const linrec_desc* d,

@@ -1,4 +1,5 @@
-// delta.hip -- gfx950 kernels of the gated delta-rule recurrence, forward.
+// delta.hip -- gfx950 kernels of the gated delta-rule recurrence, forward and
+// backward.
 //
 // Per (b,h), row vectors q_t, k_t (d_k), v_t (d_v), gate a_t, write strength
 // beta_t, and a d_k x d_v state:
@@ -62,8 +63,9 @@ __device__ __forceinline__ floatx4 mm16_f32_reg(const float* X, int xp, floatx4 
 }
 
 // ---------------------------------------------------------------------------
-// Per chunk: T = (I + A)^{-1}, then W_v, W_k (fp32, [B][H][T][d]).
-// Workgroup = (chunk, h, b), 4 waves.
+// Per chunk: T = (I + A)^{-1}, then W_v, W_k (fp32, [B][H][Tp][d], Tp the
+// piece's tokens rounded up to whole chunks), P = (Q K^T) .* D and the decay
+// tables for the serial kernels.  Workgroup = (chunk, h, b), 4 waves.
 // ---------------------------------------------------------------------------
 template <typename T, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_prep_kernel(Act<const T> Q, Act<const T> K, Act<const T> V,
@@ -290,8 +292,8 @@ __device__ __forceinline__ ColHead xcd_col_head(int H, int B)
 // Serial walk over a piece's chunks for one (b, h) and state columns
 // [16 cb, 16 cb + 16).  4 waves; wave w carries state row blocks
 // FPW w .. FPW w + FPW - 1 (fp32 result tiles) and computes the chunk's rows
-// [16 w, 16 w + 16) of U and O.  Per chunk:
-//   P = (Q K^T) .* D                      (fp32 tiles in LDS)
+// [16 w, 16 w + 16) of U and O.  Per chunk, with P = (Q K^T) .* D from the
+// prep kernel:
 //   U = W_v - W_k S_0                      (rows of this wave)
 //   O^T = gamma .* (S_0^T Q^T) + U^T P^T   (stored transposed: 4 features a lane)
 //   S <- gamma_C S + (K .* gamma_C/gamma)^T U
@@ -859,7 +861,7 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
 }
 
 // Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), 4 waves;
-// output tiles are spread over the waves.
+// wave w owns the feature blocks w, w + 4, ... of both, every row block.
 template <typename T, typename OT, int DK, int DV, bool RAGGED>
 __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
                                                            Act<const float> beta,

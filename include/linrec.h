@@ -101,6 +101,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility: the functions declared here
+ * are its only exports. */
+#pragma GCC visibility push(default)
+
 typedef enum {
     LINREC_OK = 0,
     LINREC_E_NULL = 1,      /* a required pointer is NULL                     */
@@ -429,6 +433,8 @@ int linrec_last_hip_error(void);
 
 /* Library version, as major*10000 + minor*100 + patch. */
 int linrec_version(void);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,8 @@ HIPCC_FLAGS = [
     # never emit packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # only the C ABI of include/linrec.h is exported
+    "-fvisibility=hidden",
 ]
 
 

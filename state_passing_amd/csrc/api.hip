@@ -555,7 +555,7 @@ size_t linrec_bwd_recompute_workspace_bytes(const linrec_desc* d)
 }
 
 // Per-segment totals of the decay gradient, after the gradient records.
-size_t da_tot_bytes(const linrec_desc* d)
+static size_t da_tot_bytes(const linrec_desc* d)
 {
     const size_t raw = (size_t)d->B * d->H * (size_t)nseg_of(d->T) * sizeof(float);
     return (raw + 255) / 256 * 256;
@@ -577,7 +577,7 @@ size_t linrec_seq_states_bytes(const linrec_desc* d, int32_t npieces, const int3
 
 // Two slots of gradient records, each sized for the longest piece: piece
 // i - 1's are summed and folded while piece i's are read.
-size_t bwd_seq_slot_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
+static size_t bwd_seq_slot_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
 {
     return (size_t)d->B * (size_t)d->H * (size_t)max_nseg(npieces, lengths) * per_seg_bytes(d);
 }
@@ -839,7 +839,7 @@ namespace {
 
 // Tokens of a delta-rule piece rounded up to whole chunks: the rows its
 // workspace and saved buffers hold.
-size_t delta_tokens(const linrec_desc* d) { return (size_t)chunks_of(d->T) * kChunk; }
+static size_t delta_tokens(const linrec_desc* d) { return (size_t)chunks_of(d->T) * kChunk; }
 
 }  // namespace
 
@@ -871,7 +871,7 @@ size_t linrec_delta_bwd_workspace_bytes(const linrec_desc* d)
 
 namespace {
 
-linrec_status check_beta(const linrec_tensor& beta)
+static linrec_status check_beta(const linrec_tensor& beta)
 {
     if (!beta.ptr)
         return LINREC_E_NULL;

@@ -15,14 +15,17 @@ Outputs are checked twice: fp32 outputs against the plain 2e-2 bar, and the
 bf16 outputs the benchmark produces beyond their half-ulp representation
 limit, with the plain error and the error of a perfectly rounded bf16 result
 printed beside it (see parity_util); the bf16 outputs must also equal the
-fp32 outputs of the same kernels rounded to nearest even, on every head."""
+fp32 outputs of the same kernels rounded to nearest even, on every head.
+The three large workloads are also checked on every head at both ends of
+the sequence, where a window of the inputs fixes the outputs exactly."""
 import os
 
 import numpy as np
 import pytest
 import torch
 
-from parity_util import TOL, compare, oracle_run, rne_mismatch
+import oracle
+from parity_util import TOL, compare, np64, oracle_run, rel_err, rne_mismatch
 from state_passing_amd import linrec
 from state_passing_amd.workloads import WORKLOADS, make_inputs
 
@@ -82,4 +85,62 @@ def test_fullsize_sequence_accumulation(idx):
                   f"max {ulps} ulp", flush=True)
             assert frac <= 1e-4 and ulps <= 1, (name, frac, ulps)
     del kept
+    torch.cuda.empty_cache()
+
+
+EDGE = 320   # the first segment and a chunk of the second (last: the same from the end)
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_fullsize_every_head_at_both_ends(idx):
+    """Every (b, h) of the full-size run, at both ends of the sequence.
+
+    The recurrence is causal: o and dq of the first EDGE tokens depend only
+    on S_in and the inputs up to them, and with no dS_out, dk and dv of the
+    last EDGE tokens depend only on the inputs from them on.  The oracle run
+    on those two windows alone therefore gives them exactly, for every head,
+    which checks the addressing of the heads the sampled comparison skips."""
+    wl = WORKLOADS[idx]
+    lengths = wl.pieces()
+    print(f"workload {wl.name}: {len(lengths)} pieces, all {wl.B * wl.H} heads, "
+          f"{EDGE} tokens at each end", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    got = run_sa(inp, lengths, torch.float32)
+    per_token = inp.decay is not None and inp.decay.dim() == 3
+
+    def window(sl):
+        cut = lambda x: np.ascontiguousarray(np64(x[:, :, sl]))  # noqa: E731
+        a = None
+        if inp.decay is not None:
+            a = cut(inp.decay) if per_token else np.ascontiguousarray(np64(inp.decay))
+        return cut(inp.q), cut(inp.k), cut(inp.v), cut(inp.dO), a
+
+    nthreads = len(os.sched_getaffinity(0))
+    first, last = slice(0, EDGE), slice(wl.T - EDGE, wl.T)
+    S_in = None if inp.S_in is None else np.ascontiguousarray(np64(inp.S_in))
+    q, k, v, dO, a = window(first)
+    ro, _ = oracle.fwd(q, k, v, a, S_in, nthreads=nthreads)
+    rdq, _, _, _ = oracle.bwd(q, k, v, a, S_in, dO, None, nthreads=nthreads)
+    q, k, v, dO, a = window(last)
+    _, rdk, rdv, _ = oracle.bwd(q, k, v, a, None, dO, None, nthreads=nthreads)
+
+    tol = TOL[torch.float32]
+    errs = {"o[first]": rel_err(got["o"][:, :, first], ro),
+            "dq[first]": rel_err(got["dq"][:, :, first], rdq),
+            "dk[last]": rel_err(got["dk"][:, :, last], rdk),
+            "dv[last]": rel_err(got["dv"][:, :, last], rdv)}
+    # the worst head on its own scale, so a wrong head cannot hide in the others' RMS
+    worst = 0.0
+    for name, g, r in (("o", got["o"][:, :, first], ro), ("dq", got["dq"][:, :, first], rdq),
+                       ("dk", got["dk"][:, :, last], rdk), ("dv", got["dv"][:, :, last], rdv)):
+        g = np64(g)
+        for b in range(wl.B):
+            for h in range(wl.H):
+                rms = float(np.sqrt(np.mean(r[b, h] ** 2)))
+                worst = max(worst, float(np.max(np.abs(g[b, h] - r[b, h]))) / rms)
+    errs["worst head"] = worst
+    print("  " + "  ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{wl.name}: over {tol}: {bad}"
+    del got
     torch.cuda.empty_cache()

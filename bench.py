@@ -187,7 +187,9 @@ def cpu_baseline(inp, wl, sample_tokens: int):
 def delta_bench(linrec, dev, args):
     """Gated delta rule on its 16-head, 16K-token workload (4 pieces of 4096,
     per-token gate, d = 128, bf16): forward over the pieces (keeping what the
-    backward needs), then the backward in reverse, carrying dS."""
+    backward needs), then the backward in reverse, carrying dS, through the
+    sequence drivers (the backward runs a piece's per-chunk gradient kernels
+    beside the next piece's serial walk); the per-piece calls beside them."""
     import torch
     from state_passing_amd.workloads import DELTA_WORKLOADS, make_inputs
     wl = DELTA_WORKLOADS[6]
@@ -223,6 +225,18 @@ def delta_bench(linrec, dev, args):
                              dk=dk[:, :, sl], dv=dv[:, :, sl], dbeta=db[:, :, sl], dS_in=dS,
                              workspace=wsb)
 
+    seq_saved = torch.empty(linrec.delta_seq_saved_bytes(
+        linrec.desc(B, H, T, D, D, linrec.BF16, linrec.DECAY_TOKEN), lengths), dtype=torch.uint8,
+        device=dev)
+
+    def fwd_seq():
+        linrec.delta_fwd_seq(inp.q, inp.k, inp.v, inp.beta, inp.decay, lengths, None, o=o, S_out=S,
+                             saved=seq_saved)
+
+    def bwd_seq():
+        linrec.delta_bwd_seq(inp.q, inp.k, inp.v, inp.beta, inp.decay, lengths, seq_saved, inp.dO,
+                             None, dq=dq, dk=dk, dv=dv, dbeta=db, dS_in=dS)
+
     def timed(fn, steps):
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -236,14 +250,19 @@ def delta_bench(linrec, dev, args):
     for _ in range(max(args.warmup, 1)):
         fwd()
         bwd()
+        fwd_seq()
+        bwd_seq()
     steps = max(1, min(args.steps, 5))
-    ms_fwd = timed(fwd, steps)
-    ms_bwd = timed(bwd, steps)
+    ms_fwd = timed(fwd_seq, steps)
+    ms_bwd = timed(bwd_seq, steps)
+    ms_fwd_pp = timed(fwd, steps)
+    ms_bwd_pp = timed(bwd, steps)
     tokens = B * T
     return {"workload": wl.name, "B": B, "H": H, "T": T, "d": D,
             "pieces": f"{len(lengths)} x {lengths[0]}", "decay": "per-token gate",
             "fwd_ms": ms_fwd, "bwd_ms": ms_bwd, "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
-            "fwd_plus_bwd_tokens_per_s": tokens / ((ms_fwd + ms_bwd) * 1e-3)}
+            "fwd_plus_bwd_tokens_per_s": tokens / ((ms_fwd + ms_bwd) * 1e-3),
+            "per_piece_calls": {"fwd_ms": ms_fwd_pp, "bwd_ms": ms_bwd_pp}}
 
 
 def main():

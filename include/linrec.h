@@ -401,6 +401,51 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d,
                                linrec_tensor dk, linrec_tensor dv, linrec_tensor dbeta,
                                float* dS_in, void* workspace, void* stream);
 
+/* Delta rule over a sequence of pieces (lengths[0..npieces), each >= 1,
+ * summing to d->T), the state carried from piece to piece as through
+ * linrec_delta_fwd / linrec_delta_bwd called once per piece in order (the
+ * StateFlow pages train Gated DeltaNet with the state passed between the
+ * sub-sequences of a long context: gptget summary, "Experimental design";
+ * overlapping the state transitions with other work: Abstract).  The
+ * results equal those of the per-piece calls bit for bit.  In the backward
+ * the per-chunk gradient kernels of a piece, which need its serial walk but
+ * nothing carried, run on the context's aux stream beside the next piece's
+ * prep kernel and walk on the caller's stream.  Inputs and outputs span the
+ * whole sequence, laid out as for the per-piece calls.
+ *
+ * saved: the per-piece saved buffers one after another, piece i's at the
+ * sum of linrec_delta_saved_bytes over the pieces before it (a desc with
+ * T = that piece's length); linrec_delta_seq_saved_bytes bytes in all,
+ * 16-byte aligned.  Forward workspace: the per-piece workspace of the
+ * longest piece; backward workspace: two such slots (one for a single
+ * piece).  The size queries return 0 if `d`, `npieces` or `lengths` is
+ * invalid or d_k != d_v. */
+size_t linrec_delta_seq_saved_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths);
+size_t linrec_delta_fwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
+                                            const int32_t* lengths);
+size_t linrec_delta_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
+                                            const int32_t* lengths);
+
+/* Forward over the pieces: arguments as linrec_delta_fwd for the whole
+ * sequence; S_in enters the first piece, S_out leaves the last.  saved may
+ * be NULL (nothing kept for a backward). */
+linrec_status linrec_delta_fwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npieces,
+                                   const int32_t* lengths, linrec_tensor q, linrec_tensor k,
+                                   linrec_tensor v, linrec_tensor beta, linrec_tensor decay,
+                                   const float* S_in, linrec_tensor o, float* S_out, void* saved,
+                                   void* workspace, void* stream);
+
+/* Backward over the pieces in reverse: arguments as linrec_delta_bwd for the
+ * whole sequence; saved as written by linrec_delta_fwd_seq with the same
+ * lengths; dS_out enters the last piece, dS_in leaves the first. */
+linrec_status linrec_delta_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npieces,
+                                   const int32_t* lengths, linrec_tensor q, linrec_tensor k,
+                                   linrec_tensor v, linrec_tensor beta, linrec_tensor decay,
+                                   const void* saved, linrec_tensor dO, const float* dS_out,
+                                   linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                   linrec_tensor dbeta, float* dS_in, void* workspace,
+                                   void* stream);
+
 /* Kernel kinds for linrec_ctx_kernel_times(). */
 enum {
     LINREC_KERNEL_FWD_SUM = 0,    /* forward segment sums (parallel)           */
@@ -410,8 +455,8 @@ enum {
     LINREC_KERNEL_BWD_FOLD = 4,   /* reverse fold across segments (dS carried) */
     LINREC_KERNEL_BWD_SEG = 5,    /* backward segment kernel: dQ, dK, dV       */
     LINREC_KERNEL_DA_FINISH = 6,  /* decay gradient, last step                 */
-    LINREC_KERNEL_DELTA_FWD = 7,  /* delta rule forward (both of its kernels)  */
-    LINREC_KERNEL_DELTA_BWD = 8,  /* delta rule backward (its four kernels)    */
+    LINREC_KERNEL_DELTA_FWD = 7,  /* delta rule forward (each launch of a piece's kernels) */
+    LINREC_KERNEL_DELTA_BWD = 8,  /* delta rule backward (each launch of a piece's kernels) */
     LINREC_KERNEL_KINDS = 9
 };
 

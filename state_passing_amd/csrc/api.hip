@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -32,6 +33,7 @@ struct linrec_ctx {
     hipStream_t aux;        // state transitions
     hipEvent_t ev_start;    // inputs ready on the caller's stream
     hipEvent_t ev_scan;     // a piece's scan finished (aux)
+    hipEvent_t ev_slot[2];  // a workspace slot's last reader finished (aux)
     // opt-in per-kernel timing (linrec_ctx_set_timing)
     int timing;
     std::vector<TimedLaunch> pending;
@@ -459,6 +461,8 @@ linrec_status linrec_ctx_create(linrec_ctx** out, int device)
         e = hipEventCreateWithFlags(&c->ev_start, hipEventDisableTiming);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&c->ev_scan, hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&c->ev_slot[i], hipEventDisableTiming);
     // the no-allocation scratch's address on this device (the device is
     // current); a failure here only disables linrec_bwd_noalloc
     if (e == hipSuccess) {
@@ -485,6 +489,9 @@ linrec_status linrec_ctx_destroy(linrec_ctx* ctx)
         (void)hipEventDestroy(ctx->ev_start);
     if (ctx->ev_scan)
         (void)hipEventDestroy(ctx->ev_scan);
+    for (hipEvent_t ev : ctx->ev_slot)
+        if (ev)
+            (void)hipEventDestroy(ev);
     for (const TimedLaunch& t : ctx->pending) {
         (void)hipEventDestroy(t.begin);
         (void)hipEventDestroy(t.end);
@@ -884,6 +891,101 @@ static linrec_status check_beta(const linrec_tensor& beta)
 
 }  // namespace
 
+namespace {
+
+// Bytes of the delta rule's per-piece buffers for a piece of `len` tokens
+// of the sequence d describes (rows rounded up to whole chunks).
+static size_t delta_piece_saved_bytes(const linrec_desc* d, int32_t len)
+{
+    linrec_desc p = *d;
+    p.T = len;
+    return linrec_delta_saved_bytes(&p);
+}
+
+// Launch description of the delta-rule forward over tokens [tok0, tok0 + len)
+// of the tensors, with that piece's workspace at `ws` and saved values at
+// `saved` (may be NULL).
+static linrec::DeltaFwdLaunch delta_fwd_of(const linrec_desc* d, int64_t tok0, int32_t len,
+                                           const linrec_tensor& q, const linrec_tensor& k,
+                                           const linrec_tensor& v, const linrec_tensor& beta,
+                                           const linrec_tensor& decay, const float* S_in,
+                                           const linrec_tensor& o, float* S_out, void* saved,
+                                           void* ws)
+{
+    const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
+    linrec_desc p = *d;
+    p.T = len;
+    linrec::DeltaFwdLaunch s{};
+    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
+    s.B = d->B; s.H = d->H; s.T = len;
+    s.q = advance(q, tok0, esz); s.k = advance(k, tok0, esz); s.v = advance(v, tok0, esz);
+    s.beta = advance(beta, tok0, 4); s.o = advance(o, tok0, osz);
+    s.decay = advance_decay(d, decay, tok0);
+    s.decay_kind = d->decay;
+    s.S_in = S_in;
+    s.S_out = S_out;
+    const size_t bh = (size_t)d->B * d->H, Tp = delta_tokens(&p);
+    s.wk = (float*)ws;
+    s.wv = s.wk + bh * Tp * d->dk;
+    s.pm = s.wv + bh * Tp * d->dv;
+    s.tabs = s.pm + bh * Tp * kChunk;
+    if (saved) {
+        s.s0 = (float*)saved;
+        s.u = (float*)saved + bh * (Tp / kChunk) * d->dk * d->dv;
+    }
+    return s;
+}
+
+// Launch description of the delta-rule backward over tokens [tok0, tok0 + len).
+static linrec::DeltaBwdLaunch delta_bwd_of(const linrec_desc* d, int64_t tok0, int32_t len,
+                                           const linrec_tensor& q, const linrec_tensor& k,
+                                           const linrec_tensor& v, const linrec_tensor& beta,
+                                           const linrec_tensor& decay, const void* saved,
+                                           const linrec_tensor& dO, const float* dS_out,
+                                           const linrec_tensor& dq, const linrec_tensor& dk,
+                                           const linrec_tensor& dv, const linrec_tensor& dbeta,
+                                           float* dS_in, void* ws)
+{
+    const int esz = elem_size(d->dtype), osz = elem_size(d->out_dtype);
+    linrec_desc p = *d;
+    p.T = len;
+    // workspace and saved rows cover whole chunks; the last may be partial
+    const size_t bh = (size_t)d->B * d->H, T = delta_tokens(&p), N = T / kChunk;
+    linrec::DeltaBwdLaunch s{};
+    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
+    s.B = d->B; s.H = d->H; s.T = len;
+    s.q = advance(q, tok0, esz); s.k = advance(k, tok0, esz); s.v = advance(v, tok0, esz);
+    s.beta = advance(beta, tok0, 4); s.decay = advance_decay(d, decay, tok0);
+    s.dO = advance(dO, tok0, esz);
+    s.dq = advance(dq, tok0, osz); s.dk_ = advance(dk, tok0, osz); s.dv_ = advance(dv, tok0, osz);
+    s.dbeta = advance(dbeta, tok0, 4);
+    s.decay_kind = d->decay;
+    s.s0 = (const float*)saved;
+    s.u = (const float*)saved + bh * N * d->dk * d->dv;
+    s.dS_out = dS_out;
+    s.dS_in = dS_in;
+    float* w = (float*)ws;
+    s.wk = w;
+    s.wv = s.wk + bh * T * d->dk;
+    s.tm = s.wv + bh * T * d->dv;
+    s.duy = s.tm + bh * N * kChunk * kChunk;
+    s.dsc = s.duy + bh * T * d->dv;
+    s.pm = s.dsc + bh * N * d->dk * d->dv;
+    s.tabs = s.pm + bh * T * kChunk;
+    return s;
+}
+
+// Largest piece of a sequence.
+static int32_t longest_piece(int32_t npieces, const int32_t* lengths)
+{
+    int32_t m = 0;
+    for (int32_t i = 0; i < npieces; ++i)
+        m = std::max(m, lengths[i]);
+    return m;
+}
+
+}  // namespace
+
 linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_tensor q,
                                linrec_tensor k, linrec_tensor v, linrec_tensor beta,
                                linrec_tensor decay, const float* S_in, linrec_tensor o,
@@ -902,23 +1004,8 @@ linrec_status linrec_delta_fwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
         return st;
     if (d->T == 0)
         return pass_carry(d, S_in, S_out, (int64_t)d->dk * d->dv, (hipStream_t)stream);
-    linrec::DeltaFwdLaunch s{};
-    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
-    s.B = d->B; s.H = d->H; s.T = d->T;
-    s.q = targ(q); s.k = targ(k); s.v = targ(v); s.beta = targ(beta); s.o = targ(o);
-    s.decay = targ(decay);
-    s.decay_kind = d->decay;
-    s.S_in = S_in;
-    s.S_out = S_out;
-    const size_t bh = (size_t)d->B * d->H, Tp = delta_tokens(d);
-    s.wk = (float*)workspace;
-    s.wv = s.wk + bh * Tp * d->dk;
-    s.pm = s.wv + bh * Tp * d->dv;
-    s.tabs = s.pm + bh * Tp * kChunk;
-    if (saved) {
-        s.s0 = (float*)saved;
-        s.u = (float*)saved + bh * (Tp / kChunk) * d->dk * d->dv;
-    }
+    const linrec::DeltaFwdLaunch s =
+        delta_fwd_of(d, 0, d->T, q, k, v, beta, decay, S_in, o, S_out, saved, workspace);
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_FWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_fwd(s, (hipStream_t)stream); }));
     return LINREC_OK;
@@ -943,28 +1030,131 @@ linrec_status linrec_delta_bwd(linrec_ctx* ctx, const linrec_desc* d, linrec_ten
         return st;
     if (d->T == 0)
         return pass_carry(d, dS_out, dS_in, (int64_t)d->dk * d->dv, (hipStream_t)stream);
-    // workspace and saved rows cover whole chunks; the last may be partial
-    const size_t bh = (size_t)d->B * d->H, T = delta_tokens(d), N = T / kChunk;
-    linrec::DeltaBwdLaunch s{};
-    s.dtype = d->dtype; s.out_dtype = d->out_dtype; s.dk = d->dk; s.dv = d->dv;
-    s.B = d->B; s.H = d->H; s.T = d->T;
-    s.q = targ(q); s.k = targ(k); s.v = targ(v); s.beta = targ(beta); s.decay = targ(decay);
-    s.dO = targ(dO); s.dq = targ(dq); s.dk_ = targ(dk); s.dv_ = targ(dv); s.dbeta = targ(dbeta);
-    s.decay_kind = d->decay;
-    s.s0 = (const float*)saved;
-    s.u = (const float*)saved + bh * N * d->dk * d->dv;
-    s.dS_out = dS_out;
-    s.dS_in = dS_in;
-    float* ws = (float*)workspace;
-    s.wk = ws;
-    s.wv = s.wk + bh * T * d->dk;
-    s.tm = s.wv + bh * T * d->dv;
-    s.duy = s.tm + bh * N * kChunk * kChunk;
-    s.dsc = s.duy + bh * T * d->dv;
-    s.pm = s.dsc + bh * N * d->dk * d->dv;
-    s.tabs = s.pm + bh * T * kChunk;
+    const linrec::DeltaBwdLaunch s = delta_bwd_of(d, 0, d->T, q, k, v, beta, decay, saved, dO,
+                                                  dS_out, dq, dk, dv, dbeta, dS_in, workspace);
     LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, (hipStream_t)stream,
                         [&] { return linrec::launch_delta_bwd(s, (hipStream_t)stream); }));
+    return LINREC_OK;
+}
+
+size_t linrec_delta_seq_saved_bytes(const linrec_desc* d, int32_t npieces, const int32_t* lengths)
+{
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || check_pieces(d, npieces, lengths) != LINREC_OK)
+        return 0;
+    size_t n = 0;
+    for (int32_t i = 0; i < npieces; ++i)
+        n += delta_piece_saved_bytes(d, lengths[i]);
+    return n;
+}
+
+size_t linrec_delta_fwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
+                                            const int32_t* lengths)
+{
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || check_pieces(d, npieces, lengths) != LINREC_OK)
+        return 0;
+    linrec_desc p = *d;
+    p.T = longest_piece(npieces, lengths);
+    return linrec_delta_workspace_bytes(&p);
+}
+
+size_t linrec_delta_bwd_seq_workspace_bytes(const linrec_desc* d, int32_t npieces,
+                                            const int32_t* lengths)
+{
+    if (check_desc(d) != LINREC_OK || d->dk != d->dv || check_pieces(d, npieces, lengths) != LINREC_OK)
+        return 0;
+    linrec_desc p = *d;
+    p.T = longest_piece(npieces, lengths);
+    return (size_t)std::min<int32_t>(npieces, 2) * linrec_delta_bwd_workspace_bytes(&p);
+}
+
+linrec_status linrec_delta_fwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npieces,
+                                   const int32_t* lengths, linrec_tensor q, linrec_tensor k,
+                                   linrec_tensor v, linrec_tensor beta, linrec_tensor decay,
+                                   const float* S_in, linrec_tensor o, float* S_out, void* saved,
+                                   void* workspace, void* stream)
+{
+    linrec_status st = check_fwd_args(d, q, k, v, decay, S_in, o, S_out, workspace);
+    if (st != LINREC_OK || (st = check_pieces(d, npieces, lengths)) != LINREC_OK)
+        return st;
+    if (d->dk != d->dv)
+        return LINREC_E_SHAPE;
+    if ((st = check_beta(beta)) != LINREC_OK)
+        return st;
+    if (saved && !aligned(saved, 16))
+        return LINREC_E_WORKSPACE;
+    if ((st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    // Each piece's prep kernel, then its serial walk, on the caller's stream.
+    // (The prep kernel of the next piece beside the walk, on a second stream,
+    // slowed the walk, the critical path, by more than it saved.)
+    int64_t tok0 = 0;
+    size_t saved_off = 0;
+    for (int32_t i = 0; i < npieces; ++i) {
+        const linrec::DeltaFwdLaunch cur =
+            delta_fwd_of(d, tok0, lengths[i], q, k, v, beta, decay, i == 0 ? S_in : S_out, o, S_out,
+                         saved ? (char*)saved + saved_off : nullptr, workspace);
+        LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_FWD, s,
+                            [&] { return linrec::launch_delta_fwd(cur, s); }));
+        tok0 += lengths[i];
+        saved_off += delta_piece_saved_bytes(d, lengths[i]);
+    }
+    return LINREC_OK;
+}
+
+linrec_status linrec_delta_bwd_seq(linrec_ctx* ctx, const linrec_desc* d, int32_t npieces,
+                                   const int32_t* lengths, linrec_tensor q, linrec_tensor k,
+                                   linrec_tensor v, linrec_tensor beta, linrec_tensor decay,
+                                   const void* saved, linrec_tensor dO, const float* dS_out,
+                                   linrec_tensor dq, linrec_tensor dk, linrec_tensor dv,
+                                   linrec_tensor dbeta, float* dS_in, void* workspace,
+                                   void* stream)
+{
+    linrec_status st = check_bwd_args(d, q, k, v, decay, saved, dO, dS_out, dq, dk, dv, dS_in,
+                                      workspace);
+    if (st != LINREC_OK || (st = check_pieces(d, npieces, lengths)) != LINREC_OK)
+        return st;
+    if (d->dk != d->dv)
+        return LINREC_E_SHAPE;
+    if ((st = check_beta(beta)) != LINREC_OK || (st = check_beta(dbeta)) != LINREC_OK)
+        return st;
+    if ((st = check_ctx(ctx)) != LINREC_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    // Pieces in reverse.  Each piece's prep kernel and serial walk run on the
+    // caller's stream, the walks one after another (dS carried in dS_in).
+    // The per-chunk gradient kernels of piece i, which need its walk but
+    // nothing carried, run on the aux stream beside the prep and walk of
+    // piece i - 1.  Piece i's buffers live in workspace slot i % 2; the prep
+    // of piece i waits for the gradient kernels of piece i + 2, that slot's
+    // last reader (one event per slot).
+    linrec_desc p = *d;
+    p.T = longest_piece(npieces, lengths);
+    const size_t slot_bytes = linrec_delta_bwd_workspace_bytes(&p);
+    int64_t tok0 = d->T;
+    size_t off = linrec_delta_seq_saved_bytes(d, npieces, lengths);
+    for (int32_t i = npieces - 1; i >= 0; --i) {
+        tok0 -= lengths[i];
+        off -= delta_piece_saved_bytes(d, lengths[i]);
+        linrec::DeltaBwdLaunch cur = delta_bwd_of(
+            d, tok0, lengths[i], q, k, v, beta, decay, (const char*)saved + off, dO,
+            i == npieces - 1 ? dS_out : dS_in, dq, dk, dv, dbeta, dS_in,
+            (char*)workspace + (i % 2) * slot_bytes);
+        if (i + 2 < npieces)
+            HIPCHECK(hipStreamWaitEvent(s, ctx->ev_slot[i % 2], 0));
+        cur.parts = linrec::DELTA_PREP | linrec::DELTA_SERIAL;
+        LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, s,
+                            [&] { return linrec::launch_delta_bwd(cur, s); }));
+        HIPCHECK(hipEventRecord(ctx->ev_start, s));
+        HIPCHECK(hipStreamWaitEvent(ctx->aux, ctx->ev_start, 0));
+        cur.parts = linrec::DELTA_GRAD;
+        LAUNCH(timed_launch(ctx, LINREC_KERNEL_DELTA_BWD, ctx->aux,
+                            [&] { return linrec::launch_delta_bwd(cur, ctx->aux); }));
+        HIPCHECK(hipEventRecord(ctx->ev_slot[i % 2], ctx->aux));
+    }
+    // the caller's stream waits for the last gradient kernels
+    HIPCHECK(hipEventRecord(ctx->ev_scan, ctx->aux));
+    HIPCHECK(hipStreamWaitEvent(s, ctx->ev_scan, 0));
     return LINREC_OK;
 }
 

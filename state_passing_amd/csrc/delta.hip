@@ -1059,14 +1059,17 @@ hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
     const int64_t Tp = (int64_t)N * CHUNK;
     const Act<float> wk{s.wk, (int64_t)s.H * Tp * DK, Tp * DK, DK};
     const Act<float> wv{s.wv, (int64_t)s.H * Tp * DV, Tp * DV, DV};
+    const unsigned parts = s.parts ? s.parts : DELTA_PREP | DELTA_SERIAL;
     return with_ragged(tail < CHUNK, [&](auto rg) {
         constexpr bool RG = decltype(rg)::value;
-        launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
-                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                      nullptr, s.tabs, s.H, tail);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+        if (parts & DELTA_PREP) {
+            launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                          dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                          nullptr, s.tabs, s.H, tail);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || !(parts & DELTA_SERIAL))
+                return e;
+        }
         launch_kernel((delta_scan_kernel<T, OT, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256),
                       stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
                       Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, (const float*)s.tabs,
@@ -1083,19 +1086,26 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
     const int64_t Tp = (int64_t)N * CHUNK;
     const Act<float> wk{s.wk, (int64_t)s.H * Tp * DK, Tp * DK, DK};
     const Act<float> wv{s.wv, (int64_t)s.H * Tp * DV, Tp * DV, DV};
+    const unsigned parts = s.parts ? s.parts : DELTA_PREP | DELTA_SERIAL | DELTA_GRAD;
     return with_ragged(tail < CHUNK, [&](auto rg) {
         constexpr bool RG = decltype(rg)::value;
-        launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
-                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
-                      s.tm, s.tabs, s.H, tail);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        launch_kernel((delta_bscan_kernel<T, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
-                      dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
-                      Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm, (const float*)s.tabs,
-                      s.dS_out, s.dS_in, s.duy, s.dsc, s.H, N, tail);
-        if ((e = hipGetLastError()) != hipSuccess)
+        hipError_t e = hipSuccess;
+        if (parts & DELTA_PREP) {
+            launch_kernel((delta_prep_kernel<T, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+                          dact<T>(s.q), dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), dec, wk, wv, s.pm,
+                          s.tm, s.tabs, s.H, tail);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
+        if (parts & DELTA_SERIAL) {
+            launch_kernel((delta_bscan_kernel<T, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
+                          dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
+                          Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm,
+                          (const float*)s.tabs, s.dS_out, s.dS_in, s.duy, s.dsc, s.H, N, tail);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
+        if (!(parts & DELTA_GRAD))
             return e;
         launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
                       dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), (const float*)s.tabs, (const float*)s.s0,

@@ -143,6 +143,10 @@ struct DaFinishLaunch {
 
 // Gated delta rule, forward over one piece: per-chunk W_k, W_v into the
 // workspace (fp32 [B][H][T][d_k], then [B][H][T][d_v]), then the serial walk.
+// The launches of a delta-rule piece, which a sequence driver may issue on
+// different streams: the per-chunk prep kernel, the serial walk, and (in the
+// backward) the per-chunk gradient kernels behind it.
+enum : unsigned { DELTA_PREP = 1, DELTA_SERIAL = 2, DELTA_GRAD = 4 };
 struct DeltaFwdLaunch {
     int dtype, out_dtype, dk, dv, B, H, T;
     TensorArg q, k, v, beta, decay, o;
@@ -155,6 +159,7 @@ struct DeltaFwdLaunch {
     float* u;                // optional: U of every token, [B][H][T][d_v]
     float* pm;               // P = (Q K^T) .* D per chunk, [B][H][N][64][64] (workspace)
     float* tabs;             // the decay tables of every chunk, [B][H][N][256] (workspace)
+    unsigned parts;          // DELTA_PREP | DELTA_SERIAL; 0: both
 };
 
 // Gated delta rule, backward over one piece, from the forward's saved s0 and
@@ -176,6 +181,7 @@ struct DeltaBwdLaunch {
     float* dsc;
     float* pm;
     float* tabs;
+    unsigned parts;          // DELTA_PREP | DELTA_SERIAL | DELTA_GRAD; 0: all
 };
 
 // The state transition is two launches: the parallel segment sum, then the

@@ -46,7 +46,9 @@ EXPORTS = (
     "linrec_ctx_kernel_times", "linrec_bwd_recompute_workspace_bytes", "linrec_bwd_recompute",
     "linrec_bwd_da_workspace_bytes", "linrec_bwd_da", "linrec_bwd_noalloc",
     "linrec_delta_workspace_bytes", "linrec_delta_fwd", "linrec_delta_saved_bytes",
-    "linrec_delta_bwd_workspace_bytes", "linrec_delta_bwd",
+    "linrec_delta_bwd_workspace_bytes", "linrec_delta_bwd", "linrec_delta_seq_saved_bytes",
+    "linrec_delta_fwd_seq_workspace_bytes", "linrec_delta_bwd_seq_workspace_bytes",
+    "linrec_delta_fwd_seq", "linrec_delta_bwd_seq",
 )
 
 KERNEL_KINDS = {0: "fwd_sum", 1: "fwd_fold", 2: "fwd_seg", 3: "bwd_sum", 4: "bwd_fold",
@@ -104,6 +106,12 @@ def _lib():
         "linrec_delta_saved_bytes": ([D], ctypes.c_size_t),
         "linrec_delta_bwd_workspace_bytes": ([D], ctypes.c_size_t),
         "linrec_delta_bwd": ([P, D, T, T, T, T, T, P, T, P, T, T, T, T, P, P, P], ctypes.c_int),
+        "linrec_delta_seq_saved_bytes": ([D, I32, P], ctypes.c_size_t),
+        "linrec_delta_fwd_seq_workspace_bytes": ([D, I32, P], ctypes.c_size_t),
+        "linrec_delta_bwd_seq_workspace_bytes": ([D, I32, P], ctypes.c_size_t),
+        "linrec_delta_fwd_seq": ([P, D, I32, P, T, T, T, T, T, P, T, P, P, P, P], ctypes.c_int),
+        "linrec_delta_bwd_seq": ([P, D, I32, P, T, T, T, T, T, P, T, P, T, T, T, T, P, P, P],
+                                 ctypes.c_int),
         "linrec_bwd_da": ([P, D, T, T, T, T, P, T, P, T, T, T, P, T, P, P, P, P], ctypes.c_int),
         "linrec_fwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, P, P], ctypes.c_int),
         "linrec_bwd_seq": ([P, D, I32, P, T, T, T, T, P, T, P, T, T, T, P, P, P], ctypes.c_int),
@@ -687,6 +695,99 @@ def delta_bwd(q, k, v, beta, decay, saved, dO, dS_out=None, *, dq=None, dk=None,
                                  _act(dv), _beta_arg("dbeta", dbeta, B, H, T), _ptr(dS_in),
                                  _ptr(workspace), _stream(q.device))
     _check(rc, "linrec_delta_bwd")
+    return dq, dk, dv, dbeta, dS_in
+
+
+def _lengths_arg(lengths):
+    return (ctypes.c_int32 * len(lengths))(*lengths)
+
+
+def delta_seq_saved_bytes(d: Desc, lengths: Sequence[int]) -> int:
+    return int(_lib().linrec_delta_seq_saved_bytes(ctypes.byref(d), len(lengths),
+                                                   _lengths_arg(lengths)))
+
+
+def delta_fwd_seq_workspace_bytes(d: Desc, lengths: Sequence[int]) -> int:
+    return int(_lib().linrec_delta_fwd_seq_workspace_bytes(ctypes.byref(d), len(lengths),
+                                                           _lengths_arg(lengths)))
+
+
+def delta_bwd_seq_workspace_bytes(d: Desc, lengths: Sequence[int]) -> int:
+    return int(_lib().linrec_delta_bwd_seq_workspace_bytes(ctypes.byref(d), len(lengths),
+                                                           _lengths_arg(lengths)))
+
+
+def delta_fwd_seq(q, k, v, beta, decay, lengths: Sequence[int], S_in=None, *, o=None,
+                  S_out=None, saved=None, save=False, workspace=None, out_dtype=None):
+    """Gated delta rule forward over consecutive pieces, S carried (native
+    driver, linrec_delta_fwd_seq).  Returns (o, S_out, saved or None)."""
+    odt = _out_dtype(q, out_dtype, o)
+    devs = _validate(q, k, v, decay, outs=_outs(q, v, odt, o=o), states_in=(("S_in", S_in),),
+                     states_out=(("S_out", S_out),),
+                     extra=(("beta", beta), ("workspace", workspace), ("saved", saved)))
+    lengths = _piece_lengths(lengths, q.shape[2])
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    barg = _beta_arg("beta", beta, B, H, T)
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, delta_fwd_seq_workspace_bytes(d, lengths))
+    if saved is not None:
+        _check_buffer("saved", saved, delta_seq_saved_bytes(d, lengths))
+    _check_device(q, *devs)
+    o = _new_act(q, DV, odt, o)
+    S_out = _state_out(q, B, H, DK, DV, S_out)
+    if workspace is None:
+        workspace = torch.empty(max(delta_fwd_seq_workspace_bytes(d, lengths), 16),
+                                dtype=torch.uint8, device=q.device)
+    if saved is None and save:
+        saved = torch.empty(max(delta_seq_saved_bytes(d, lengths), 16), dtype=torch.uint8,
+                            device=q.device)
+    rc = _lib().linrec_delta_fwd_seq(context(q.device.index), ctypes.byref(d), len(lengths),
+                                     _lengths_arg(lengths), _act(q), _act(k), _act(v), barg, dec,
+                                     _ptr(S_in), _act(o), _ptr(S_out), _ptr(saved),
+                                     _ptr(workspace), _stream(q.device))
+    _check(rc, "linrec_delta_fwd_seq")
+    return o, S_out, saved
+
+
+def delta_bwd_seq(q, k, v, beta, decay, lengths: Sequence[int], saved, dO, dS_out=None, *,
+                  dq=None, dk=None, dv=None, dbeta=None, dS_in=None, workspace=None,
+                  out_dtype=None):
+    """Gated delta rule backward over consecutive pieces in reverse, dS
+    carried (linrec_delta_bwd_seq), from delta_fwd_seq's `saved`.  Returns
+    (dq, dk, dv, dbeta, dS_in)."""
+    odt = _out_dtype(q, out_dtype, dq)
+    devs = _validate(q, k, v, decay, dO=dO, outs=_outs(q, v, odt, dq=dq, dk=dk, dv=dv),
+                     states_in=(("dS_out", dS_out),), states_out=(("dS_in", dS_in),),
+                     extra=(("beta", beta), ("saved", saved), ("workspace", workspace),
+                            ("dbeta", dbeta)))
+    lengths = _piece_lengths(lengths, q.shape[2])
+    B, H, T, DK = q.shape
+    DV = v.shape[3]
+    barg = _beta_arg("beta", beta, B, H, T)
+    kind, dec = _decay(decay)
+    d = _desc_of(q, v, kind, odt)
+    _check_buffer("saved", saved, delta_seq_saved_bytes(d, lengths))
+    if workspace is not None:
+        _check_buffer("workspace", workspace, delta_bwd_seq_workspace_bytes(d, lengths))
+    if dbeta is not None:
+        _beta_arg("dbeta", dbeta, B, H, T)
+    _check_device(q, *devs)
+    dq, dk, dv = _new_act(q, DK, odt, dq), _new_act(q, DK, odt, dk), _new_act(q, DV, odt, dv)
+    dS_in = _state_out(q, B, H, DK, DV, dS_in)
+    if dbeta is None:
+        dbeta = torch.empty(B, H, T, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(delta_bwd_seq_workspace_bytes(d, lengths), 16),
+                                dtype=torch.uint8, device=q.device)
+    rc = _lib().linrec_delta_bwd_seq(context(q.device.index), ctypes.byref(d), len(lengths),
+                                     _lengths_arg(lengths), _act(q), _act(k), _act(v), barg, dec,
+                                     _ptr(saved), _act(dO), _ptr(dS_out), _act(dq), _act(dk),
+                                     _act(dv), _beta_arg("dbeta", dbeta, B, H, T), _ptr(dS_in),
+                                     _ptr(workspace), _stream(q.device))
+    _check(rc, "linrec_delta_bwd_seq")
     return dq, dk, dv, dbeta, dS_in
 
 

@@ -293,6 +293,53 @@ def test_delta_arguments():
     assert bcall(d(dk=64)) == E["LINREC_E_SHAPE"]
 
 
+def test_delta_sequence_arguments():
+    """The delta-rule sequence drivers: saved buffers of the pieces one after
+    another, the workspace of the longest piece (the backward: two slots, one
+    for a single piece), the piece list checked as for the linear sequence
+    drivers."""
+    lib = linrec._lib()
+    seq = d(T=8192)
+    lens = [4096, 4000, 96]
+    per = [linrec.delta_saved_bytes(d(T=n)) for n in lens]
+    assert linrec.delta_seq_saved_bytes(seq, lens) == sum(per)
+    assert linrec.delta_fwd_seq_workspace_bytes(seq, lens) == linrec.delta_workspace_bytes(d())
+    assert linrec.delta_bwd_seq_workspace_bytes(seq, lens) == \
+        2 * linrec.delta_bwd_workspace_bytes(d())
+    assert linrec.delta_fwd_seq_workspace_bytes(seq, [8192]) == \
+        linrec.delta_workspace_bytes(d(T=8192))
+    assert linrec.delta_seq_saved_bytes(seq, [8192]) == linrec.delta_saved_bytes(d(T=8192))
+    assert linrec.delta_seq_saved_bytes(seq, [4096, 4000]) == 0      # does not sum to T
+    assert linrec.delta_seq_saved_bytes(d(T=8192, dk=64), [8192]) == 0
+    assert linrec.delta_bwd_seq_workspace_bytes(seq, [8192, 0]) == 0
+
+    beta = linrec.Tensor(FAKE, 16 * 8192, 8192, 1)
+
+    def fcall(lengths, desc=seq, beta=beta, ws=FAKE, saved=None):
+        arr = (ctypes.c_int32 * max(len(lengths), 1))(*lengths)
+        return lib.linrec_delta_fwd_seq(None, ctypes.byref(desc), len(lengths), arr, act(), act(),
+                                        act(), beta, linrec.Tensor(FAKE, 0, 1, 0), None, act(), FAKE,
+                                        saved, ws, None)
+
+    def bcall(lengths, desc=seq, dbeta=beta, saved=FAKE):
+        arr = (ctypes.c_int32 * max(len(lengths), 1))(*lengths)
+        return lib.linrec_delta_bwd_seq(None, ctypes.byref(desc), len(lengths), arr, act(), act(),
+                                        act(), beta, linrec.Tensor(FAKE, 0, 1, 0), saved, act(), None,
+                                        act(), act(), act(), dbeta, FAKE, FAKE, None)
+    for call in (fcall, bcall):
+        assert call(lens) == E["LINREC_E_NULL"]                  # checks pass, no context
+        assert call([8192]) == E["LINREC_E_NULL"]
+        assert call([4096, 4000]) == E["LINREC_E_SHAPE"]
+        assert call([8192, 0]) == E["LINREC_E_SHAPE"]
+        assert call([]) == E["LINREC_E_SHAPE"]
+        assert call(lens, desc=d(T=8192, dk=64)) == E["LINREC_E_SHAPE"]
+    assert fcall(lens, beta=linrec.Tensor(None, 0, 0, 1)) == E["LINREC_E_NULL"]
+    assert fcall(lens, ws=None) == E["LINREC_E_WORKSPACE"]
+    assert fcall(lens, saved=FAKE + 8) == E["LINREC_E_WORKSPACE"]
+    assert bcall(lens, dbeta=linrec.Tensor(FAKE + 2, 0, 0, 1)) == E["LINREC_E_ALIGN"]
+    assert bcall(lens, saved=None) == E["LINREC_E_WORKSPACE"]
+
+
 def test_empty_piece_arguments():
     """T = 0: only the carried state and gradient pointers are checked;
     activations, decay, beta, states, saved and workspace may all be NULL.

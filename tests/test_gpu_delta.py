@@ -210,3 +210,60 @@ def test_delta_ragged(wl):
     torch.cuda.synchronize()
     assert bool((o[:, :, T:] == fill).all()) and bool((dq[:, :, T:] == fill).all())
     assert bool((db[:, :, T:] == fill).all())
+
+
+def run_seq(inp, lengths):
+    """The native sequence drivers (linrec_delta_fwd_seq / linrec_delta_bwd_seq),
+    fp32 outputs."""
+    o, S, saved = linrec.delta_fwd_seq(inp.q, inp.k, inp.v, inp.beta, inp.decay, lengths, inp.S_in,
+                                       save=True, out_dtype=torch.float32)
+    dq, dk, dv, db, dS = linrec.delta_bwd_seq(inp.q, inp.k, inp.v, inp.beta, inp.decay, lengths, saved,
+                                              inp.dO, inp.dS_out, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return {"o": o, "S_out": S, "dq": dq, "dk": dk, "dv": dv, "dbeta": db, "dS_in": dS}
+
+
+SEQ = [
+    (SMALL[0], [64, 64, 128]),
+    (SMALL[3], [128, 64, 128]),
+    (SMALL[4], [256]),
+    (RAGGED[2], [37, 246, 50]),
+    (RAGGED[1], [1, 63, 36]),
+    (small("delta-seq-many", 1, 2, 640, 128, "bf16", "head", s_in=0.1), [64] * 7 + [100, 92]),
+]
+
+
+@pytest.mark.parametrize("wl,lens", SEQ, ids=[f"{w.name}-{len(l)}" for w, l in SEQ])
+def test_delta_sequence_drivers(wl, lens):
+    """The sequence drivers overlap the next piece's per-chunk kernels with
+    the current piece's serial walk on a second stream; their results equal
+    those of the per-piece calls bit for bit, and the oracle's."""
+    print(f"case {wl.name} pieces {lens}", flush=True)
+    inp = to_dev(make_inputs(wl, device="cpu", seed=13, with_dS_out=True))
+    got = run_seq(inp, lens)
+    ref = run_pieces(inp, lens, backward=True)
+    same = {k: torch.equal(got[k], ref[k]) for k in ref}
+    assert all(same.values()), same
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    errs = errors(got, oracle_delta(inp, backward=True), heads)
+    print("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[wl.dtype] for v in errs.values()), errs
+
+
+def test_delta_sequence_drivers_gated_16k():
+    """The 16-head, 16K-token gated workload through the sequence drivers, as
+    timed: bitwise equal to the per-piece calls, twice in a row (the
+    workspace slots reused), and against the oracle on sampled heads."""
+    wl = DELTA_WORKLOADS[6]
+    lens = wl.pieces()
+    inp = make_inputs(wl, device=DEV, with_dS_out=True)
+    ref = run_pieces(inp, lens, backward=True)
+    for rep in range(2):
+        got = run_seq(inp, lens)
+        same = {k: torch.equal(got[k], ref[k]) for k in ref}
+        print(f"[{wl.name} run {rep}] bitwise equal: {same}", flush=True)
+        assert all(same.values()), same
+    heads = [(0, 2), (0, 13)]
+    errs = errors(got, oracle_delta(inp, heads, backward=True), heads)
+    print("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= TOL[wl.dtype] for v in errs.values()), errs

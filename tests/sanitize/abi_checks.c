@@ -137,6 +137,23 @@ int main(void)
                                 act(v, B, H, 128, 128), tbeta, tdec, states, act(dO, B, H, 128, 128), NULL,
                                 act(dq, B, H, 128, 128), act(dk, B, H, 128, 128), act(dv, B, H, 128, 128),
                                 tdbeta, S_out, ws, NULL) == LINREC_E_NULL, "delta_bwd");
+        const int32_t dl[3] = {64, 37, 27};
+        EXPECT(linrec_delta_seq_saved_bytes(&e, 3, dl) > 0, "delta seq saved bytes");
+        EXPECT(linrec_delta_fwd_seq_workspace_bytes(&e, 3, dl) <= linrec_delta_workspace_bytes(&e),
+               "delta fwd seq workspace bytes");
+        EXPECT(linrec_delta_bwd_seq_workspace_bytes(&e, 3, dl) > 0, "delta bwd seq workspace bytes");
+        EXPECT(linrec_delta_fwd_seq(NULL, &e, 3, dl, act(q, B, H, 128, 128), act(k, B, H, 128, 128),
+                                    act(v, B, H, 128, 128), tbeta, tdec, S_in, act(o, B, H, 128, 128),
+                                    S_out, states, ws, NULL) == LINREC_E_NULL, "delta_fwd_seq");
+        EXPECT(linrec_delta_bwd_seq(NULL, &e, 3, dl, act(q, B, H, 128, 128), act(k, B, H, 128, 128),
+                                    act(v, B, H, 128, 128), tbeta, tdec, states, act(dO, B, H, 128, 128),
+                                    NULL, act(dq, B, H, 128, 128), act(dk, B, H, 128, 128),
+                                    act(dv, B, H, 128, 128), tdbeta, S_out, ws, NULL) == LINREC_E_NULL,
+               "delta_bwd_seq");
+        const int32_t bad_dl[2] = {64, 0};
+        EXPECT(linrec_delta_fwd_seq(NULL, &e, 2, bad_dl, act(q, B, H, 128, 128), act(k, B, H, 128, 128),
+                                    act(v, B, H, 128, 128), tbeta, tdec, S_in, act(o, B, H, 128, 128),
+                                    S_out, states, ws, NULL) == LINREC_E_SHAPE, "delta_fwd_seq bad lengths");
     }
 
     /* bad arguments: rejected before the context is looked at */

@@ -290,16 +290,22 @@ __device__ __forceinline__ ColHead xcd_col_head(int H, int B)
 
 // ---------------------------------------------------------------------------
 // Serial walk over a piece's chunks for one (b, h) and state columns
-// [16 cb, 16 cb + 16).  4 waves; wave w carries state row blocks
-// FPW w .. FPW w + FPW - 1 (fp32 result tiles) and computes the chunk's rows
-// [16 w, 16 w + 16) of U and O.  Per chunk, with P = (Q K^T) .* D from the
+// [16 cb, 16 cb + 16).  8 waves.  Per chunk n, with P = (Q K^T) .* D from the
 // prep kernel:
-//   U = W_v - W_k S_0                      (rows of this wave)
-//   O^T = gamma .* (S_0^T Q^T) + U^T P^T   (stored transposed: 4 features a lane)
-//   S <- gamma_C S + (K .* gamma_C/gamma)^T U
+//   U = W_v - W_k S_0                      (waves 0-3: rows [16 w, 16 w + 16))
+//   S <- gamma_C S + (K .* gamma_C/gamma)^T U   (waves 0-3: state row blocks
+//                                                FPW w .. FPW w + FPW - 1)
+//   O^T = gamma .* (S_0^T Q^T) + U^T P^T   (waves 4-7, one chunk behind)
+// The state's chain per chunk is U, then the update; the output is not on
+// it, so waves 4-7 form chunk n - 1's output while waves 0-3 form chunk n's
+// U, and waves 0-3 issue first on the SIMD each shares with one of waves
+// 4-7.  K, the decay tables and the split S_0 and U planes are
+// double-buffered in LDS (chunk n in buffer n % 2), which leaves two
+// barriers per chunk: a buffer is written again two chunks later, after
+// every wave has passed the barrier that follows its last reader.
 // ---------------------------------------------------------------------------
 template <typename T, typename OT, int DK, int DV, bool RAGGED>
-__global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
+__global__ __launch_bounds__(512) void delta_scan_kernel(Act<const T> Q, Act<const T> K,
                                                          Act<const float> Wk, Act<const float> Wv,
                                                          const float* __restrict__ Pm,
                                                          const float* __restrict__ tabs,
@@ -308,48 +314,57 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
                                                          float* __restrict__ s0_out,
                                                          float* __restrict__ u_out, int H, int N, int tail)
 {
-    constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
-    static_assert(FPW >= 1 && FPW * NW == NFB, "d_k must be 64 or 128");
+    constexpr int NT = 512, NFB = DK / 16;
+    static_assert(NFB == 4 || NFB == 8, "d_k must be 64 or 128");
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD;
-    __shared__ __align__(16) T Ks[CHUNK * QP];
+    __shared__ __align__(16) T Ks[2][CHUNK * QP];
     // the state and U as bf16 hi/lo planes, transposed ([column][f] and
     // [column][token]), so that every product reads them with 16-byte reads
     constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
-    __shared__ __align__(16) T Ssp[2][16 * SPP];
-    __shared__ __align__(16) T Usp[2][16 * UPP];
-    __shared__ __align__(16) float tab[TAB_SIZE];
+    __shared__ __align__(16) T Ssp[2][2][16 * SPP];
+    __shared__ __align__(16) T Usp[2][2][16 * UPP];
+    __shared__ __align__(16) float tab[2][TAB_SIZE];
 
     const ColHead wg = xcd_col_head(H, gridDim.z);
     const int cb = wg.cb, h = wg.h, b = wg.b;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * cb;
+    // roles: waves 0-3 form U (row block w) and carry the state; waves 4-7
+    // form the output (row block w - 4)
+    constexpr int FPW = NFB / 4;
+    const bool urole = w < 4;
+    const int rb = w & 3;
+    if (urole)
+        __builtin_amdgcn_s_setprio(1);
 
-    floatx4 S[FPW];   // S[16 fb + 4g + r][cbase + t], fb = FPW w + q
+    floatx4 S[FPW];   // S[16 (FPW w + q) + 4g + r][cbase + t]
 #pragma unroll
-    for (int q = 0; q < FPW; ++q)
+    for (int q = 0; q < FPW; ++q) {
+        S[q] = zero4();
+        if (urole && S_in)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[q][r] = S_in ? S_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t]
-                           : 0.f;
+            for (int r = 0; r < 4; ++r)
+                S[q][r] = S_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t];
+    }
 
     const T* kh = K.head(b, h);
-    // Row operands of this wave's 16 tokens go from global memory straight
-    // into the registers of the products that take them: W_k (rows of U's
-    // A operand), W_v (U's result-tile entries), Q and P (the output's B
-    // operands), lane (g, t) holding row 16 w + t, columns 8g .. 8g + 7 of
-    // each k32 step.  Each is reloaded for the next chunk as soon as the
-    // current chunk's products have taken it.  K, which every wave reads
-    // transposed, and the decay tables are staged through LDS, loaded a
-    // chunk ahead.
+    // Row operands of a wave's 16 tokens go from global memory straight into
+    // the registers of the products that take them: W_k (rows of U's A
+    // operand) and W_v (U's result-tile entries) in waves 0-3, Q and P (the
+    // output's B operands) in waves 4-7, lane (g, t) holding row 16 rb + t,
+    // columns 8g .. 8g + 7 of each k32 step.  Each is reloaded for the next
+    // chunk as soon as the current chunk's products have taken it.  K, which
+    // every wave reads transposed, and the decay tables are staged through
+    // LDS, loaded a chunk ahead.
     // the last chunk may be partial (tail tokens): its row reads are clamped
     // to the last token; K's padded rows are zeroed in LDS, the prep
     // kernel's operands are zero there, and no output is stored for them
     auto rows_of = [&](int64_t tk) { return RAGGED && tk / CHUNK == N - 1 ? tail : CHUNK; };
     const T* qh = Q.head(b, h);
-    const float* wkrow = Wk.head(b, h) + (int64_t)(16 * w + t) * Wk.st + 8 * g;
-    const float* prow = Pm + bh * (int64_t)N * CHUNK * CHUNK + (16 * w + t) * CHUNK + 8 * g;
+    const float* wkrow = Wk.head(b, h) + (int64_t)(16 * rb + t) * Wk.st + 8 * g;
+    const float* prow = Pm + bh * (int64_t)N * CHUNK * CHUNK + (16 * rb + t) * CHUNK + 8 * g;
     const float* wvh = Wv.head(b, h) + cbase + t;
     const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
     constexpr int NKS = DK / 32;
@@ -365,10 +380,10 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            wv[r] = wvh[(tk + 16 * w + 4 * g + r) * Wv.st];
+            wv[r] = wvh[(tk + 16 * rb + 4 * g + r) * Wv.st];
     };
     auto load_q_p = [&](int64_t tk) {
-        const T* qrow = qh + (tk + (RAGGED ? min(16 * w + t, rows_of(tk) - 1) : 16 * w + t)) * Q.st + 8 * g;
+        const T* qrow = qh + (tk + (RAGGED ? min(16 * rb + t, rows_of(tk) - 1) : 16 * rb + t)) * Q.st + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             qv[ks].load(qrow + 32 * ks);
@@ -386,36 +401,85 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
         chunk_load(rk, kh + tk * K.st, K.st, rows_of(tk));
     };
     load_k_tab(0);
-    load_wk_wv(0);
-    load_q_p(0);
-    for (int n = 0; n < N; ++n) {
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        const int rows_n = rows_of(tok0);
-        chunk_store(rk, Ks, QP, rows_n);
-        if (threadIdx.x < TAB_SIZE / 4)
-            *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
+    if (urole)
+        load_wk_wv(0);
+    else
+        load_q_p(0);
+    // O^T[c][i] of chunk nn, tokens [16 rb, 16 rb + 16) (waves 4-7), from
+    // its buffers (nn % 2) and the registers holding its Q and P rows
+    auto out_tile = [&](int nn) {
+        const int bf = nn & 1;
+        floatx4 acc = zero4();
 #pragma unroll
-        for (int q = 0; q < FPW; ++q) {
-            put_split4(Ssp[0], Ssp[1], t * SPP + 16 * (FPW * w + q), S[q]);
-            if (s0_out)   // the state entering chunk n, for the backward
+        for (int ks = 0; ks < NKS; ++ks)
+            acc = mma(frag_rows_split(Ssp[bf][0], Ssp[bf][1], SPP, 0, 32 * ks), qv[ks].frag(), acc);
+        acc *= tab[bf][TAB_G + 16 * rb + t];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int f = 16 * (FPW * w + q) + 4 * g + r;
-                    s0_out[((bh * N + n) * DK + f) * DV + cbase + t] = S[q][r];
-                }
+        for (int js = 0; js < 2; ++js) {
+            if (js <= rb / 2) {
+                const float x[8] = {pv[js][0][0], pv[js][0][1], pv[js][0][2], pv[js][0][3],
+                                    pv[js][1][0], pv[js][1][1], pv[js][1][2], pv[js][1][3]};
+                acc = mma(frag_rows_split(Usp[bf][0], Usp[bf][1], UPP, 0, 32 * js), split8<T>(x), acc);
+            }
         }
-        __syncthreads();
-        if (n + 1 < N)
-            load_k_tab(tok0 + CHUNK);
-
-        // U rows [16 w, 16 w + 16) = W_v - W_k S_0
-        {
+        return acc;
+    };
+    // The top of chunk n: its K and decay tables into LDS, the state entering
+    // it as split planes (waves 0-3), and that state for the backward.
+    auto chunk_top = [&](int n) {
+        const int cur = n & 1;
+        chunk_store(rk, Ks[cur], QP, rows_of((int64_t)n * CHUNK));
+        if (threadIdx.x < TAB_SIZE / 4)
+            *reinterpret_cast<floatx4*>(tab[cur] + 4 * threadIdx.x) = rtab;
+        if (urole)
+#pragma unroll
+            for (int q = 0; q < FPW; ++q) {
+                const int fb = FPW * w + q;
+                put_split4(Ssp[cur][0], Ssp[cur][1], t * SPP + 16 * fb, S[q]);
+                if (s0_out)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s0_out[((bh * N + n) * DK + 16 * fb + 4 * g + r) * DV + cbase + t] = S[q][r];
+            }
+    };
+    // S <- gamma_C S + K~^T U of chunk n for this wave's row blocks
+    auto update = [&](int n) {
+        const int cur = n & 1;
+        if (urole) {
+            const float gC = tab[cur][TAB_G + CHUNK - 1];
+            float kf[2][8];
+            slot_factors(tab[cur] + TAB_F, kf);
+#pragma unroll
+            for (int q = 0; q < FPW; ++q) {
+                const int fb = FPW * w + q;
+                S[q] *= gC;
+#pragma unroll
+                for (int ks = 0; ks < CHUNK / 32; ++ks)
+                    S[q] = mma(split_scaled<T>(frag_cols(Ks[cur], QP, 16 * fb, 32 * ks), kf[ks]),
+                               frag_rows_split(Usp[cur][0], Usp[cur][1], UPP, 0, 32 * ks), S[q]);
+            }
+        }
+    };
+    // Chunk n: U and the update (waves 0-3), the output of chunk n - 1
+    // (waves 4-7); the last chunk's output follows the loop.  The
+    // two roles run separate loops with the same two barriers per chunk, so
+    // that each loop carries only its own operands from one chunk to the
+    // next and waits for them only where they are used.
+    if (urole) {
+        for (int n = 0; n < N; ++n) {
+            const int cur = n & 1;
+            const int64_t tok0 = (int64_t)n * CHUNK;
+            chunk_top(n);
+            __syncthreads();
+            if (n + 1 < N)
+                load_k_tab(tok0 + CHUNK);
+            // U rows [16 w, 16 w + 16) = W_v - W_k S_0
             floatx4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const float x[8] = {wk[ks][0][0], wk[ks][0][1], wk[ks][0][2], wk[ks][0][3],
                                     wk[ks][1][0], wk[ks][1][1], wk[ks][1][2], wk[ks][1][3]};
-                acc = mma(split8<T>(x), frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), acc);
+                acc = mma(split8<T>(x), frag_rows_split(Ssp[cur][0], Ssp[cur][1], SPP, 0, 32 * ks), acc);
             }
             floatx4 u4;
 #pragma unroll
@@ -426,52 +490,38 @@ __global__ __launch_bounds__(256) void delta_scan_kernel(Act<const T> Q, Act<con
             if (u_out)    // U for the backward, [B][H][T][DV]
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    u_out[(bh * (int64_t)N * CHUNK + tok0 + 16 * w + 4 * g + r) * DV + cbase + t] = u4[r];
-            put_split4(Usp[0], Usp[1], t * UPP + 16 * w, u4);
+                    u_out[(bh * (int64_t)N * CHUNK + tok0 + 16 * rb + 4 * g + r) * DV + cbase + t] = u4[r];
+            put_split4(Usp[cur][0], Usp[cur][1], t * UPP + 16 * rb, u4);
+            __syncthreads();
+            update(n);
         }
-        __syncthreads();
-
-        // O^T[c][i] for tokens [16 w, 16 w + 16)
-        {
-            floatx4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                acc = mma(frag_rows_split(Ssp[0], Ssp[1], SPP, 0, 32 * ks), qv[ks].frag(), acc);
-            acc *= tab[TAB_G + 16 * w + t];
-#pragma unroll
-            for (int js = 0; js < 2; ++js) {
-                if (js <= w / 2) {
-                    const float x[8] = {pv[js][0][0], pv[js][0][1], pv[js][0][2], pv[js][0][3],
-                                        pv[js][1][0], pv[js][1][1], pv[js][1][2], pv[js][1][3]};
-                    acc = mma(frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * js), split8<T>(x), acc);
-                }
-            }
+    } else {
+        for (int n = 0; n < N; ++n) {
+            const int64_t tok0 = (int64_t)n * CHUNK;
+            chunk_top(n);
+            __syncthreads();
             if (n + 1 < N)
-                load_q_p(tok0 + CHUNK);
-            store_tile_t<OT>(O.head(b, h) + tok0 * O.st, O.st, 16 * w, cbase, acc, rows_n);
-        }
-        // S <- gamma_C S + K~^T U for this wave's row blocks
-        {
-            const float gC = tab[TAB_G + CHUNK - 1];
-            float kf[2][8];
-            slot_factors(tab + TAB_F, kf);
-#pragma unroll
-            for (int q = 0; q < FPW; ++q) {
-                const int fb = FPW * w + q;
-                S[q] *= gC;
-#pragma unroll
-                for (int ks = 0; ks < CHUNK / 32; ++ks)
-                    S[q] = mma(split_scaled<T>(frag_cols(Ks, QP, 16 * fb, 32 * ks), kf[ks]),
-                               frag_rows_split(Usp[0], Usp[1], UPP, 0, 32 * ks), S[q]);
+                load_k_tab(tok0 + CHUNK);
+            if (n >= 1) {
+                const floatx4 acc = out_tile(n - 1);
+                load_q_p(tok0);
+                const int64_t tp = tok0 - CHUNK;
+                store_tile_t<OT>(O.head(b, h) + tp * O.st, O.st, 16 * rb, cbase, acc, rows_of(tp));
             }
+            __syncthreads();
+            update(n);
         }
-        __syncthreads();
+        // the last chunk's output: its U was written before the loop's last
+        // barrier, and no buffer is written after it
+        const int64_t tp = (int64_t)(N - 1) * CHUNK;
+        store_tile_t<OT>(O.head(b, h) + tp * O.st, O.st, 16 * rb, cbase, out_tile(N - 1), rows_of(tp));
     }
+    if (urole)
 #pragma unroll
-    for (int q = 0; q < FPW; ++q)
+        for (int q = 0; q < FPW; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S_out[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t] = S[q][r];
+            for (int r = 0; r < 4; ++r)
+                S_out[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t] = S[q][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -1070,7 +1120,7 @@ hipError_t delta_fwd_impl(const DeltaFwdLaunch& s, hipStream_t stream)
             if (e != hipSuccess || !(parts & DELTA_SERIAL))
                 return e;
         }
-        launch_kernel((delta_scan_kernel<T, OT, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256),
+        launch_kernel((delta_scan_kernel<T, OT, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(512),
                       stream, dact<T>(s.q), dact<T>(s.k), Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st},
                       Act<const float>{wv.ptr, wv.sb, wv.sh, wv.st}, (const float*)s.pm, (const float*)s.tabs,
                       s.S_in, s.S_out, Act<OT>{(OT*)s.o.ptr, s.o.sb, s.o.sh, s.o.st}, s.s0, s.u, s.H, N, tail);

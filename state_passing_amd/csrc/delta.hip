@@ -542,11 +542,19 @@ __global__ __launch_bounds__(512) void delta_scan_kernel(Act<const T> Q, Act<con
 // ---------------------------------------------------------------------------
 
 // Serial reverse walk over a piece's chunks for one (b, h) and gradient
-// columns [16 cb, 16 cb + 16), 4 waves as in delta_scan_kernel.  Writes dU
-// ([B][H][T][DV] fp32), the gradient leaving every chunk (dS_C, per chunk
-// [B][H][N][DK][DV]) and dS_in.
+// columns [16 cb, 16 cb + 16), 8 waves.  Writes dU ([B][H][T][DV] fp32), the
+// gradient leaving every chunk (dS_C, per chunk [B][H][N][DK][DV]) and dS_in.
+// Per chunk the gradient's chain is
+//   dU   = P^T dO + (K .* gamma_C/gamma) dS_C        (waves 0-3: rows 16 w ..)
+//   dS_0 = gamma_C dS_C + (Q .* gamma)^T dO - W_k^T dU  (waves 0-3: row blocks
+//                                                   FPW w .. FPW w + FPW - 1)
+// whose terms P^T dO and (Q .* gamma)^T dO do not depend on dS: waves 4-7
+// form them for the next (earlier) chunk while waves 0-3 walk the current
+// one, and pass them through LDS in the result-tile layout of the waves that
+// add them.  Q, dO, the decay tables and those terms are double-buffered
+// (chunk n in buffer n % 2); two barriers per chunk.
 template <typename T, int DK, int DV, bool RAGGED>
-__global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
+__global__ __launch_bounds__(512) void delta_bscan_kernel(Act<const T> Q, Act<const T> K,
                                                           Act<const T> dO, Act<const float> Wk,
                                                           const float* __restrict__ Pm,
                                                           const float* __restrict__ tabs,
@@ -554,56 +562,69 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
                                                           float* dS_in, float* __restrict__ dU_out,
                                                           float* __restrict__ dsc_out, int H, int N, int tail)
 {
-    constexpr int NT = 256, NW = 4, NFB = DK / 16, FPW = NFB / NW;
+    constexpr int NT = 512, NFB = DK / 16, FPW = NFB / 4;
+    static_assert(NFB == 4 || NFB == 8, "d_k must be 64 or 128");
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, OP = 16 + PAD;
-    __shared__ __align__(16) T Qs[CHUNK * QP];
-    __shared__ __align__(16) T dOs[CHUNK * OP];
+    __shared__ __align__(16) T Qs[2][CHUNK * QP];
+    __shared__ __align__(16) T dOs[2][CHUNK * OP];
     // the carried gradient and dU as bf16 hi/lo planes, transposed
     constexpr int SPP = DK + PAD, UPP = CHUNK + PAD;
     __shared__ __align__(16) T Gsp[2][16 * SPP];
     __shared__ __align__(16) T dUsp[2][16 * UPP];
-    __shared__ __align__(16) float tab[TAB_SIZE];
+    __shared__ __align__(16) float tab[2][TAB_SIZE];
+    // the terms that do not depend on dS, per chunk: (Q .* gamma)^T dO as
+    // NFB result tiles, then P^T dO as 4 (64 lanes x 4 values each)
+    __shared__ __align__(16) float XY[2][(NFB + 4) * 256];
 
     const ColHead wg = xcd_col_head(H, gridDim.z);
     const int cb = wg.cb, h = wg.h, b = wg.b;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
     const int64_t bh = (int64_t)b * H + h;
     const int cbase = 16 * cb;
+    // roles: waves 0-3 walk the gradient (row block w of dU, feature blocks
+    // FPW w .. of dS); waves 4-7 form the next chunk's dS-free terms (row
+    // block w - 4 of P^T dO, feature blocks FPW (w - 4) .. of (Q .* gamma)^T dO)
+    const bool chain = w < 4;
+    const int rb = w & 3;
+    if (chain)
+        __builtin_amdgcn_s_setprio(1);
 
     floatx4 G[FPW];   // dS[16 fb + 4g + r][cbase + t], fb = FPW w + q
 #pragma unroll
     for (int q = 0; q < FPW; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            G[q][r] = dS_out ? dS_out[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t]
-                             : 0.f;
+            G[q][r] = chain && dS_out
+                          ? dS_out[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t]
+                          : 0.f;
 
     const T* qh = Q.head(b, h);
     const T* doh = dO.head(b, h);
     const float* th = tabs + bh * (int64_t)N * TAB_SIZE;
-    // Operands only this wave reads go from global memory straight into the
-    // registers of its products, in fragment layout, and are reloaded for
-    // the next (earlier) chunk as soon as the current chunk's products have
-    // taken them: K rows 16 w .. (dU's A operand), P columns 16 w .. (dU's
-    // P^T), and the W_k columns of this wave's feature blocks (the gradient
-    // update's W_k^T).  Q and dO, which every wave reads transposed, and the
-    // decay tables are staged through LDS, a chunk ahead.
+    // Operands only one wave reads go from global memory straight into the
+    // registers of its products, in fragment layout, a chunk ahead: K rows
+    // 16 w .. (dU's A operand) and the W_k columns of the wave's feature
+    // blocks (the gradient update's W_k^T) in waves 0-3, P columns
+    // 16 (w - 4) .. (P^T dO) in waves 4-7.  Q and dO, which waves 4-7 read
+    // transposed, and the decay tables are staged through LDS by every wave.
     constexpr int NKS = DK / 32;
     // the last chunk may be partial (tail tokens): row reads are clamped to
     // its last token, Q and dO are zeroed past it in LDS, and dU is zero
     // there (the prep kernel's W_k and P are zero for those tokens)
     auto rows_of = [&](int64_t tk) { return RAGGED && tk / CHUNK == N - 1 ? tail : CHUNK; };
     const T* kh = K.head(b, h);
-    const float* pcol = Pm + bh * (int64_t)N * CHUNK * CHUNK + 8 * g * CHUNK + 16 * w + t;
-    const float* wkcol = Wk.head(b, h) + (int64_t)(8 * g) * Wk.st + 16 * FPW * w + t;
+    const float* pcol = Pm + bh * (int64_t)N * CHUNK * CHUNK + 8 * g * CHUNK + 16 * rb + t;
+    const float* wkcol = Wk.head(b, h) + (int64_t)(8 * g) * Wk.st + 16 * FPW * rb + t;
     RowFrag<T> kv[NKS];
     float pc[2][8], wkc[FPW][2][8];
-    auto load_k_p = [&](int64_t tk) {
-        const T* krow = kh + (tk + (RAGGED ? min(16 * w + t, rows_of(tk) - 1) : 16 * w + t)) * K.st + 8 * g;
+    auto load_k = [&](int64_t tk) {
+        const T* krow = kh + (tk + (RAGGED ? min(16 * rb + t, rows_of(tk) - 1) : 16 * rb + t)) * K.st + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
             kv[ks].load(krow + 32 * ks);
+    };
+    auto load_p = [&](int64_t tk) {
 #pragma unroll
         for (int js = 0; js < 2; ++js)
 #pragma unroll
@@ -634,82 +655,140 @@ __global__ __launch_bounds__(256) void delta_bscan_kernel(Act<const T> Q, Act<co
             rdo = *reinterpret_cast<const u32x4*>(doh + (tk + row) * dO.st + cbase + col);
         }
     };
-    load_q_do_tab((int64_t)(N - 1) * CHUNK);
-    load_k_p((int64_t)(N - 1) * CHUNK);
-    load_wk((int64_t)(N - 1) * CHUNK);
-    for (int n = N - 1; n >= 0; --n) {
-        const int64_t tok0 = (int64_t)n * CHUNK;
-        const int rows_n = rows_of(tok0);
-        chunk_store(rq, Qs, QP, rows_n);
+    auto store_q_do_tab = [&](int m) {
+        const int bf = m & 1, rows_m = rows_of((int64_t)m * CHUNK);
+        chunk_store(rq, Qs[bf], QP, rows_m);
         if (threadIdx.x < CHUNK * PER) {
             const int row = threadIdx.x / PER, col = VEC * (threadIdx.x % PER);
-            *reinterpret_cast<u32x4*>(dOs + row * OP + col) = !RAGGED || row < rows_n ? rdo : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(dOs[bf] + row * OP + col) =
+                !RAGGED || row < rows_m ? rdo : u32x4{0u, 0u, 0u, 0u};
         }
         if (threadIdx.x < TAB_SIZE / 4)
-            *reinterpret_cast<floatx4*>(tab + 4 * threadIdx.x) = rtab;
+            *reinterpret_cast<floatx4*>(tab[bf] + 4 * threadIdx.x) = rtab;
+    };
+    // waves 4-7: chunk m's (Q .* gamma)^T dO tiles of feature blocks
+    // FPW rb .. and P^T dO tile of row block rb, into XY[m % 2]
+    auto free_terms = [&](int m) {
+        const int bf = m & 1;
+        float qf[2][8];
+        slot_factors(tab[bf] + TAB_G, qf);
 #pragma unroll
         for (int q = 0; q < FPW; ++q) {
-            put_split4(Gsp[0], Gsp[1], t * SPP + 16 * (FPW * w + q), G[q]);
+            const int fb = FPW * rb + q;
+            floatx4 acc = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int f = 16 * (FPW * w + q) + 4 * g + r;
-                dsc_out[((bh * N + n) * DK + f) * DV + cbase + t] = G[q][r];
-            }
+            for (int ks = 0; ks < CHUNK / 32; ++ks)
+                acc = mma(split_scaled<T>(frag_cols(Qs[bf], QP, 16 * fb, 32 * ks), qf[ks]),
+                          frag_cols(dOs[bf], OP, 0, 32 * ks), acc);
+            *reinterpret_cast<floatx4*>(XY[bf] + (fb * 64 + l) * 4) = acc;
         }
-        __syncthreads();
-        if (n > 0)
-            load_q_do_tab(tok0 - CHUNK);
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+            if (js >= rb / 2)
+                acc = mma(split8<T>(pc[js]), frag_cols(dOs[bf], OP, 0, 32 * js), acc);
+        *reinterpret_cast<floatx4*>(XY[bf] + ((NFB + rb) * 64 + l) * 4) = acc;
+    };
 
-        // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
-        {
-            floatx4 acc = zero4(), acc2 = zero4();
+    // prologue: the last chunk's staged operands and dS-free terms
+    const int64_t last = (int64_t)(N - 1) * CHUNK;
+    load_q_do_tab(last);
+    if (chain) {
+        load_k(last);
+        load_wk(last);
+    } else {
+        load_p(last);
+    }
+    store_q_do_tab(N - 1);
+    if (N > 1)
+        load_q_do_tab(last - CHUNK);
+    __syncthreads();
+    if (!chain) {
+        free_terms(N - 1);
+        if (N > 1)
+            load_p(last - CHUNK);
+    }
+
+    // Chunk n (in reverse): the gradient's chain in waves 0-3, chunk n - 1's
+    // dS-free terms in waves 4-7.  The two roles run separate loops with the
+    // same two barriers per chunk, so that each loop carries only its own
+    // operands from one chunk to the next.
+    if (chain) {
+        for (int n = N - 1; n >= 0; --n) {
+            const int cur = n & 1;
+            const int64_t tok0 = (int64_t)n * CHUNK;
+            const int rows_n = rows_of(tok0);
 #pragma unroll
-            for (int js = 0; js < 2; ++js)
-                if (js >= w / 2)
-                    acc = mma(split8<T>(pc[js]), frag_cols(dOs, OP, 0, 32 * js), acc);
+            for (int q = 0; q < FPW; ++q) {
+                put_split4(Gsp[0], Gsp[1], t * SPP + 16 * (FPW * w + q), G[q]);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                acc2 = mma(kv[ks].frag(), frag_rows_split(Gsp[0], Gsp[1], SPP, 0, 32 * ks), acc2);
+                for (int r = 0; r < 4; ++r) {
+                    const int f = 16 * (FPW * w + q) + 4 * g + r;
+                    dsc_out[((bh * N + n) * DK + f) * DV + cbase + t] = G[q][r];
+                }
+            }
             if (n > 0)
-                load_k_p(tok0 - CHUNK);
-            floatx4 u4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * g + r;
-                u4[r] = !RAGGED || i < rows_n ? acc[r] + tab[TAB_F + i] * acc2[r] : 0.f;
-                dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
-            }
-            put_split4(dUsp[0], dUsp[1], t * UPP + 16 * w, u4);
-        }
-        __syncthreads();
+                store_q_do_tab(n - 1);
+            __syncthreads();
+            if (n > 1)
+                load_q_do_tab(tok0 - 2 * CHUNK);
+            const float gC = tab[cur][TAB_G + CHUNK - 1];
 
-        // dS <- gamma_C dS + (Q .* gamma)^T dO - W_k^T dU, this wave's row blocks
-        {
-            const float gC = tab[TAB_G + CHUNK - 1];
-            float qf[2][8];
-            slot_factors(tab + TAB_G, qf);
+            // dU rows [16 w, 16 w + 16): P^T dO (j >= i) + (gamma_C/gamma_i) K dS_C
+            {
+                const floatx4 acc = *reinterpret_cast<const floatx4*>(XY[cur] + ((NFB + w) * 64 + l) * 4);
+                floatx4 acc2 = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc2 = mma(kv[ks].frag(), frag_rows_split(Gsp[0], Gsp[1], SPP, 0, 32 * ks), acc2);
+                if (n > 0)
+                    load_k(tok0 - CHUNK);
+                floatx4 u4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * w + 4 * g + r;
+                    u4[r] = !RAGGED || i < rows_n ? acc[r] + tab[cur][TAB_F + i] * acc2[r] : 0.f;
+                    dU_out[(bh * (int64_t)N * CHUNK + tok0 + i) * DV + cbase + t] = u4[r];
+                }
+                put_split4(dUsp[0], dUsp[1], t * UPP + 16 * w, u4);
+            }
+            __syncthreads();
+
+            // dS <- gamma_C dS + (Q .* gamma)^T dO - W_k^T dU, this wave's row blocks
 #pragma unroll
             for (int q = 0; q < FPW; ++q) {
                 const int fb = FPW * w + q;
-                floatx4 acc = zero4(), acc2 = zero4();
+                const floatx4 acc = *reinterpret_cast<const floatx4*>(XY[cur] + (fb * 64 + l) * 4);
+                floatx4 acc2 = zero4();
 #pragma unroll
-                for (int ks = 0; ks < CHUNK / 32; ++ks) {
-                    acc = mma(split_scaled<T>(frag_cols(Qs, QP, 16 * fb, 32 * ks), qf[ks]),
-                              frag_cols(dOs, OP, 0, 32 * ks), acc);
+                for (int ks = 0; ks < CHUNK / 32; ++ks)
                     acc2 = mma(split8<T>(wkc[q][ks]), frag_rows_split(dUsp[0], dUsp[1], UPP, 0, 32 * ks), acc2);
-                }
                 G[q] = gC * G[q] + acc - acc2;
             }
             if (n > 0)
                 load_wk(tok0 - CHUNK);
         }
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < FPW; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dS_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t] = G[q][r];
+    } else {
+        for (int n = N - 1; n >= 0; --n) {
+            const int64_t tok0 = (int64_t)n * CHUNK;
+            if (n > 0)
+                store_q_do_tab(n - 1);
+            __syncthreads();
+            if (n > 1)
+                load_q_do_tab(tok0 - 2 * CHUNK);
+            if (n > 0) {
+                free_terms(n - 1);
+                if (n > 1)
+                    load_p(tok0 - 2 * CHUNK);
+            }
+            __syncthreads();
+        }
     }
-#pragma unroll
-    for (int q = 0; q < FPW; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dS_in[bh * DK * DV + (int64_t)(16 * (FPW * w + q) + 4 * g + r) * DV + cbase + t] = G[q][r];
 }
 
 // Per chunk, first part: Y = T^T dU (written over dU), dV, M (written over
@@ -1148,7 +1227,7 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
                 return e;
         }
         if (parts & DELTA_SERIAL) {
-            launch_kernel((delta_bscan_kernel<T, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(256), stream,
+            launch_kernel((delta_bscan_kernel<T, DK, DV, RG>), dim3(DV / 16, s.H, s.B), dim3(512), stream,
                           dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO),
                           Act<const float>{wk.ptr, wk.sb, wk.sh, wk.st}, (const float*)s.pm,
                           (const float*)s.tabs, s.dS_out, s.dS_in, s.duy, s.dsc, s.H, N, tail);

@@ -989,10 +989,15 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     }
 }
 
-// Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), 4 waves;
-// wave w owns the feature blocks w, w + 4, ... of both, every row block.
+// Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), one wave
+// per feature block (d_k / 16, at least 4); wave w owns feature blocks
+// w, w + NW, ... of both, every row block.  The LDS holds one workgroup per
+// CU, so the waves of that one workgroup are all the CU's latency hiding.
+template <int DK>
+constexpr int bgrad2_waves() { return DK / 16 >= 8 ? 8 : 4; }
+
 template <typename T, typename OT, int DK, int DV, bool RAGGED>
-__global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
+__global__ __launch_bounds__(64 * bgrad2_waves<DK>()) void delta_bgrad2_kernel(Act<const T> Q, Act<const T> K, Act<const T> dO,
                                                            Act<const float> beta,
                                                            const float* __restrict__ tabs,
                                                            const float* __restrict__ s0,
@@ -1002,7 +1007,7 @@ __global__ __launch_bounds__(256) void delta_bgrad2_kernel(Act<const T> Q, Act<c
                                                            const float* __restrict__ Mg, Act<OT> dQo,
                                                            Act<OT> dKo, int H, int tail)
 {
-    constexpr int NT = 256, NW = 4;
+    constexpr int NW = bgrad2_waves<DK>(), NT = 64 * NW;
     constexpr int PAD = Pad<T>::value;
     constexpr int QP = DK + PAD, OP = DV + PAD;
     constexpr int UP = DV + 4, AP = CHUNK + 4;
@@ -1242,7 +1247,7 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
                       Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H, tail);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+        launch_kernel((delta_bgrad2_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(64 * bgrad2_waves<DK>()), stream,
                       dact<T>(s.q), dact<T>(s.k), dact<T>(s.dO), dact<float>(s.beta), (const float*)s.tabs,
                       (const float*)s.s0, (const float*)s.dsc, (const float*)s.u, (const float*)s.duy,
                       (const float*)s.tm, Act<OT>{(OT*)s.dq.ptr, s.dq.sb, s.dq.sh, s.dq.st},

@@ -792,10 +792,13 @@ __global__ __launch_bounds__(512) void delta_bscan_kernel(Act<const T> Q, Act<co
 }
 
 // Per chunk, first part: Y = T^T dU (written over dU), dV, M (written over
-// T) and dbeta.  Workgroup = (chunk, h, b), 4 waves; wave w owns token rows
-// [16 w, 16 w + 16) of Y, dV, M and dbeta (no reduction crosses waves).
+// T) and dbeta.  Workgroup = (chunk, h, b), 8 waves (its LDS holds one
+// workgroup per CU); wave w owns token rows [16 rb, 16 rb + 16), rb = w % 4,
+// and half of the column blocks of Y and dV (ch = w / 4) and of the row
+// block's M tiles; the two waves of a row block add their shares of dbeta
+// through LDS.
 template <typename T, typename OT, int DK, int DV, bool RAGGED>
-__global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<const T> V,
+__global__ __launch_bounds__(512) void delta_bgrad1_kernel(Act<const T> K, Act<const T> V,
                                                            Act<const float> beta,
                                                            const float* __restrict__ tabs,
                                                            const float* __restrict__ s0,
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
                                                            float* __restrict__ Tm, float* __restrict__ dUY,
                                                            Act<OT> dVo, Act<float> dbeta, int H, int tail)
 {
-    constexpr int NT = 256;
+    constexpr int NT = 512;
     constexpr int PAD = Pad<T>::value;
     constexpr int KP = DK + PAD, SPP = DK + PAD;
     constexpr int UP = DV + 4, AP = CHUNK + 4;
@@ -818,6 +821,7 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     __shared__ __align__(16) unsigned char region[RBYTES];
     __shared__ __align__(16) float tab[TAB_SIZE];
     __shared__ float bet[CHUNK];
+    __shared__ float dbp[2][CHUNK];   // each column half's share of dbeta
     float* const Ts = reinterpret_cast<float*>(region);
     float* const dUs = Ts + CHUNK * AP;
     T* const S0h = reinterpret_cast<T*>(region);
@@ -827,6 +831,8 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
 
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z, N = gridDim.x;
     const int w = wave_id(), l = lane_id(), t = l & 15, g = l >> 4;
+    constexpr int NCB = DV / 16, CPW = NCB / 2;   // column blocks, per wave
+    const int rb = w & 3, ch = w >> 2, cb0 = ch * CPW;
     const int64_t bh = (int64_t)b * H + h;
     const int64_t tok0 = (int64_t)n * CHUNK;
     float* Tc = Tm + (bh * N + n) * CHUNK * CHUNK;
@@ -858,12 +864,13 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
         rdu[i] = *reinterpret_cast<const floatx4*>(yc + 4 * (threadIdx.x + NT * i));
         ru[i] = *reinterpret_cast<const floatx4*>(uc + 4 * (threadIdx.x + NT * i));
     }
-    float vv[DV / 16][4];   // V[16 w + 4 g + r][16 cb + t]
+    float vv[CPW][4];   // V[16 rb + 4 g + r][16 (cb0 + c) + t]
 #pragma unroll
-    for (int cb = 0; cb < DV / 16; ++cb)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            vv[cb][r] = (float)vh[(RAGGED ? min(16 * w + 4 * g + r, rows - 1) : 16 * w + 4 * g + r) * V.st + 16 * cb + t];
+            vv[c][r] = (float)vh[(RAGGED ? min(16 * rb + 4 * g + r, rows - 1) : 16 * rb + 4 * g + r) * V.st +
+                                 16 * (cb0 + c) + t];
 
     if (threadIdx.x < CHUNK)
         bet[threadIdx.x] = !RAGGED || (int)threadIdx.x < rows ? bt : 0.f;
@@ -882,36 +889,37 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     }
     __syncthreads();
 
-    // Y rows [16 w, 16 w + 16): Y[i][c] = sum_{m >= i} T[m][i] dU[m][c]
-    floatx4 Y[DV / 16];
+    // Y rows [16 rb, 16 rb + 16), this wave's column blocks:
+    // Y[i][c] = sum_{m >= i} T[m][i] dU[m][c]
+    floatx4 Y[CPW];
 #pragma unroll
-    for (int cb = 0; cb < DV / 16; ++cb) {
-        Y[cb] = zero4();
-        for (int ms = w / 2; ms < 2; ++ms)
-            Y[cb] = mma(split_cols_f32<T>(Ts, AP, 16 * w, 32 * ms), split_cols_f32<T>(dUs, UP, 16 * cb, 32 * ms),
-                        Y[cb]);
+    for (int c = 0; c < CPW; ++c) {
+        Y[c] = zero4();
+        for (int ms = rb / 2; ms < 2; ++ms)
+            Y[c] = mma(split_cols_f32<T>(Ts, AP, 16 * rb, 32 * ms),
+                       split_cols_f32<T>(dUs, UP, 16 * (cb0 + c), 32 * ms), Y[c]);
     }
     {
         // Y to the workspace (over dU, which every thread read before the
         // barrier above) and dV
         OT* dvh = dVo.head(b, h) + tok0 * dVo.st;
 #pragma unroll
-        for (int cb = 0; cb < DV / 16; ++cb)
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * g + r, c = 16 * cb + t;
-                yc[i * DV + c] = Y[cb][r];
+                const int i = 16 * rb + 4 * g + r, col = 16 * (cb0 + c) + t;
+                yc[i * DV + col] = Y[c][r];
                 if (!RAGGED || i < rows)
-                    dvh[i * dVo.st + c] = (OT)(bet[i] * Y[cb][r]);
+                    dvh[i * dVo.st + col] = (OT)(bet[i] * Y[c][r]);
             }
     }
     // S_0 (fp32 [f][c]) in result-tile order: lane (g, t) of wave w takes
-    // the tiles (fb, cb) with fb = w, w + 4, ...
-    constexpr int NFB = DK / 16, NCB = DV / 16, SPW = NFB * NCB / 4;
+    // the tiles w, w + 8, ... of the NFB x NCB tiles (tile = fb NCB + cb)
+    constexpr int NFB = DK / 16, SPW = NFB * NCB / 8;
     float sv[SPW][4];
 #pragma unroll
     for (int k = 0; k < SPW; ++k) {
-        const int fb = w + 4 * (k / NCB), cb = k % NCB;
+        const int fb = (w + 8 * k) / NCB, cb = (w + 8 * k) % NCB;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             sv[k][r] = S0[(16 * fb + 4 * g + r) * DV + 16 * cb + t];
@@ -919,23 +927,24 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     __syncthreads();   // every wave has read T and dU
 #pragma unroll
     for (int k = 0; k < SPW; ++k) {
-        const int fb = w + 4 * (k / NCB), cb = k % NCB;
+        const int fb = (w + 8 * k) / NCB, cb = (w + 8 * k) % NCB;
         put_split4(S0h, S0l, (16 * cb + t) * SPP + 16 * fb, floatx4{sv[k][0], sv[k][1], sv[k][2], sv[k][3]});
     }
     __syncthreads();
 
-    // (K S_0) of rows 16 w; z = V - gamma (K S_0); dbeta gets < z_i, Y_i >
-    float db[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta of rows 16 w + 4g + r, this lane's columns
+    // (K S_0) of rows 16 rb; z = V - gamma (K S_0); dbeta gets < z_i, Y_i >
+    float db[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta of rows 16 rb + 4g + r, this lane's columns
 #pragma unroll
-    for (int cb = 0; cb < DV / 16; ++cb) {
+    for (int c = 0; c < CPW; ++c) {
         floatx4 ks0 = zero4();
 #pragma unroll
         for (int fs = 0; fs < DK / 32; ++fs)
-            ks0 = mma(frag_rows(Ks, KP, 16 * w, 32 * fs), frag_rows_split(S0h, S0l, SPP, 16 * cb, 32 * fs), ks0);
+            ks0 = mma(frag_rows(Ks, KP, 16 * rb, 32 * fs),
+                      frag_rows_split(S0h, S0l, SPP, 16 * (cb0 + c), 32 * fs), ks0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * g + r;
-            db[r] += (vv[cb][r] - tab[TAB_G + i] * ks0[r]) * Y[cb][r];
+            const int i = 16 * rb + 4 * g + r;
+            db[r] += (vv[c][r] - tab[TAB_G + i] * ks0[r]) * Y[c][r];
         }
     }
     __syncthreads();   // every wave has read S_0
@@ -943,10 +952,10 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
     {
         auto* ysv = (volatile __attribute__((address_space(3))) float*)Ys;
 #pragma unroll
-        for (int cb = 0; cb < DV / 16; ++cb)
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                ysv[(16 * w + 4 * g + r) * UP + 16 * cb + t] = Y[cb][r];
+                ysv[(16 * rb + 4 * g + r) * UP + 16 * (cb0 + c) + t] = Y[c][r];
     }
 #pragma unroll
     for (int i = 0; i < NUV; ++i) {
@@ -954,29 +963,32 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
         *reinterpret_cast<floatx4*>(Us + (e / DV) * UP + e % DV) = ru[i];
     }
     __syncthreads();
-    // dA = -Y U^T (j < i), M = dA .* gamma_i / gamma_j; sum_j M_ij k_i . k_j into dbeta
-    for (int jb = 0; jb <= w; ++jb) {
+    // dA = -Y U^T (j < i), M = dA .* gamma_i / gamma_j, this wave's column
+    // blocks jb = ch, ch + 2, ... of the row block; sum_j M_ij k_i . k_j
+    // into dbeta
+    for (int jb = ch; jb <= rb; jb += 2) {
         floatx4 dA = zero4(), gk = zero4();
 #pragma unroll
         for (int cs = 0; cs < DV / 32; ++cs)
-            dA = mma(split_rows_f32<T>(Ys, UP, 16 * w, 32 * cs), split_rows_f32<T>(Us, UP, 16 * jb, 32 * cs), dA);
+            dA = mma(split_rows_f32<T>(Ys, UP, 16 * rb, 32 * cs), split_rows_f32<T>(Us, UP, 16 * jb, 32 * cs), dA);
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks)
-            gk = mma(frag_rows(Ks, KP, 16 * w, 32 * ks), frag_rows(Ks, KP, 16 * jb, 32 * ks), gk);
+            gk = mma(frag_rows(Ks, KP, 16 * rb, 32 * ks), frag_rows(Ks, KP, 16 * jb, 32 * ks), gk);
         const int j = 16 * jb + t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * g + r;
+            const int i = 16 * rb + 4 * g + r;
             const float m = j < i ? -dA[r] * __expf(tab[TAB_LAM + i] - tab[TAB_LAM + j]) : 0.f;
             Tc[i * CHUNK + j] = m;
             db[r] += m * gk[r];
         }
     }
-    for (int jb = w + 1; jb < 4; ++jb)
+    for (int jb = rb + 1 + ch; jb < 4; jb += 2)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            Tc[(16 * w + 4 * g + r) * CHUNK + 16 * jb + t] = 0.f;
-    // row sums over the 16 lanes of a group
+            Tc[(16 * rb + 4 * g + r) * CHUNK + 16 * jb + t] = 0.f;
+    // row sums over the 16 lanes of a group, then over the row block's two
+    // waves
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float x = db[r];
@@ -984,9 +996,13 @@ __global__ __launch_bounds__(256) void delta_bgrad1_kernel(Act<const T> K, Act<c
         x += __shfl_xor(x, 2, 64);
         x += __shfl_xor(x, 4, 64);
         x += __shfl_xor(x, 8, 64);
-        if (t == 0 && (!RAGGED || 16 * w + 4 * g + r < rows))
-            dbeta.ptr[b * dbeta.sb + h * dbeta.sh + (tok0 + 16 * w + 4 * g + r) * dbeta.st] = x;
+        if (t == 0)
+            dbp[ch][16 * rb + 4 * g + r] = x;
     }
+    __syncthreads();
+    if (threadIdx.x < CHUNK && (!RAGGED || (int)threadIdx.x < rows))
+        dbeta.ptr[b * dbeta.sb + h * dbeta.sh + (tok0 + threadIdx.x) * dbeta.st] =
+            dbp[0][threadIdx.x] + dbp[1][threadIdx.x];
 }
 
 // Per chunk, second part: dQ and dK.  Workgroup = (chunk, h, b), one wave
@@ -1241,7 +1257,7 @@ hipError_t delta_bwd_impl(const DeltaBwdLaunch& s, hipStream_t stream)
         }
         if (!(parts & DELTA_GRAD))
             return e;
-        launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(256), stream,
+        launch_kernel((delta_bgrad1_kernel<T, OT, DK, DV, RG>), dim3(N, s.H, s.B), dim3(512), stream,
                       dact<T>(s.k), dact<T>(s.v), dact<float>(s.beta), (const float*)s.tabs, (const float*)s.s0,
                       (const float*)s.u, s.tm, s.duy, Act<OT>{(OT*)s.dv_.ptr, s.dv_.sb, s.dv_.sh, s.dv_.st},
                       Act<float>{(float*)s.dbeta.ptr, s.dbeta.sb, s.dbeta.sh, s.dbeta.st}, s.H, tail);

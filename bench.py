@@ -85,6 +85,9 @@ KERNEL_SYMBOL = {
     "bwd_fold": "seg_fold_kernel<128,128,true>",
     "bwd_seg": "bwd_seg_kernel<bf16,bf16,128,128,false,false>",
 }
+# gated delta rule, per head-token at d = 128, bf16 activations, fp32 beta and gate
+DELTA_BYTES = {"fwd": 4 * 256 + 2 * 4,          # q, k, v, o; beta, gate
+               "bwd": 7 * 256 + 2 * 4 + 4}      # q, k, v, dO, dq, dk, dv; beta, gate; dbeta
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_seg_sa256k_traffic.txt")
 SQ_FILE = os.path.join(ROOT, "profiles", "linrec_kernels_sa256k_sq_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "state_passing_amd", "csrc", f)
@@ -99,6 +102,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0)
     p.add_argument("--profile", action="store_true")
+    p.add_argument("--profile-delta", action="store_true",
+                   help="run one forward and one backward of the delta-rule workload's sequence drivers only")
     return p.parse_args()
 
 
@@ -247,6 +252,12 @@ def delta_bench(linrec, dev, args):
         torch.cuda.synchronize()
         return a.elapsed_time(b_) / steps
 
+    if args.profile_delta:
+        # only the sequence drivers' dispatches, for a profiler
+        fwd_seq()
+        bwd_seq()
+        torch.cuda.synchronize()
+        return {"profile": "delta-rule sequence drivers", "steps": 1}
     for _ in range(max(args.warmup, 1)):
         fwd()
         bwd()
@@ -258,10 +269,20 @@ def delta_bench(linrec, dev, args):
     ms_fwd_pp = timed(fwd, steps)
     ms_bwd_pp = timed(bwd, steps)
     tokens = B * T
+    # algorithmic bytes per head-token (bf16, d = 128): forward reads q, k, v,
+    # beta, gate and writes o; backward reads q, k, v, dO, beta, gate and
+    # writes dq, dk, dv, dbeta
+    fwd_b, bwd_b = DELTA_BYTES["fwd"] * B * H * T, DELTA_BYTES["bwd"] * B * H * T
+    fwd_gbs, bwd_gbs = fwd_b / (ms_fwd * 1e-3) / 1e9, bwd_b / (ms_bwd * 1e-3) / 1e9
     return {"workload": wl.name, "B": B, "H": H, "T": T, "d": D,
             "pieces": f"{len(lengths)} x {lengths[0]}", "decay": "per-token gate",
             "fwd_ms": ms_fwd, "bwd_ms": ms_bwd, "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
             "fwd_plus_bwd_tokens_per_s": tokens / ((ms_fwd + ms_bwd) * 1e-3),
+            "roofline": {"bound": "latency (serial chunk walks on half the CUs)",
+                         "algorithmic_bytes_per_head_token": DELTA_BYTES,
+                         "fwd_GBs": fwd_gbs, "bwd_GBs": bwd_gbs, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "fwd_frac": fwd_gbs / PEAK_HBM_GBS,
+                         "bwd_frac": bwd_gbs / PEAK_HBM_GBS},
             "per_piece_calls": {"fwd_ms": ms_fwd_pp, "bwd_ms": ms_bwd_pp}}
 
 
@@ -275,6 +296,12 @@ def main():
     if args.copy_probe:
         print(json.dumps({"copy_probe_bytes": args.copy_probe,
                           "read_plus_write_GBs": copy_probe(args.copy_probe)}))
+        return
+    if args.profile_delta:
+        from state_passing_amd import linrec
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps(delta_bench(linrec, dev, args)))
         return
 
     from state_passing_amd import linrec
